@@ -1,0 +1,295 @@
+"""Benchmark: one step = the whole compressed-KV decode path on one layer.
+
+Default workload: the Llama-3-8B-shaped layer (1 sequence, 32 query heads,
+8 KV heads, head_dim 128, 32768-token context, K 8-bit / V 3-bit). A step
+encodes the 64-token pending batch (K and V) into the cache and then runs the
+fused decode attention over all 32768 tokens (query rotation, split attend,
+combine + inverse rotation). Inputs are synthetic and seeded (workloads/).
+
+Cold cache: the packed cache (48 MB) fits in MI355X's 256 MB Infinity Cache,
+so the timed steps cycle through enough independent copies (>= 512 MB) that
+each step's reads come from HBM.
+
+Prints ONE JSON line. `value` is algorithmic attend bytes / step time (GB/s);
+`roofline` is the split-attend kernel alone, timed with HIP events on its own
+stream; `cpu_baseline` times the CPU oracle on a bounded sample of the step.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused compressed-KV decode-attend HBM GB/s (% of peak); ctx-tokens/s per layer"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--workload", default="llama8b_32k_k8v3")
+    p.add_argument("--cold-bytes", type=float, default=512e6,
+                   help="total bytes of cache copies cycled through (0: one warm copy)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    return p.parse_args()
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime (events on an explicit stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The oracle as it stands, single-threaded, on KV heads of the same step
+    until about budget_s seconds of timed work: pending-batch encode of K and V
+    for that head plus attention of its query heads over the whole context."""
+    import oracle
+    ok = oracle.Codec(wl.dim, wl.k_bits, wl.codec_seed)
+    ov = oracle.Codec(wl.dim, wl.v_bits, wl.codec_seed)
+    G = wl.group
+    T = int(inp.lengths[0])
+    P = wl.pending
+    done_bytes = 0
+    done_tokens = 0
+    timed = 0.0
+    heads = 0
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            L = int(inp.lengths[b])
+            # setup (untimed, as the GPU's cache is resident before its clock starts)
+            kc, kn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L - P])
+            vc, vn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L - P])
+            t0 = time.perf_counter()
+            if P:
+                pkc, pkn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, L - P:L])
+                pvc, pvn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, L - P:L])
+                kc = np.concatenate([kc, pkc], axis=2)
+                kn = np.concatenate([kn, pkn], axis=2)
+                vc = np.concatenate([vc, pvc], axis=2)
+                vn = np.concatenate([vn, pvn], axis=2)
+            oracle.attend(ok, ov, inp.q[b:b + 1, g * G:(g + 1) * G], kc, kn, vc, vn,
+                          np.array([L], np.int32))
+            timed += time.perf_counter() - t0
+            heads += 1
+            done_tokens += L
+            done_bytes += L * ((wl.dim * wl.k_bits // 8 + 4) + (wl.dim * wl.v_bits // 8 + 4))
+            if timed >= budget_s:
+                break
+        if timed >= budget_s:
+            break
+    return {
+        "value": done_bytes / timed / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{heads} of {wl.batch * wl.n_kv_heads} (sequence, KV head) units of the step "
+                  f"({heads * G} query heads, {done_tokens} cached tokens, "
+                  f"{P}-token pending encode each); {timed:.2f} s timed, fp64 C oracle, 1 thread",
+        "ctx_tokens_per_s": done_tokens / timed,
+        "seconds": timed,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    import compressed_domain_decode_amd as tq
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.WORKLOADS[args.workload]
+    inp = workloads.generate(wl)
+    B, Hq, Hkv, d = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.dim
+    lengths_np = inp.lengths
+    T = inp.k.shape[2]
+    P = wl.pending
+    kc = tq.tq_codec_init(d, wl.k_bits, wl.codec_seed)
+    vc = tq.tq_codec_init(d, wl.v_bits, wl.codec_seed)
+    kr, vr = kc.row_bytes, vc.row_bytes
+
+    k_dev = torch.from_numpy(inp.k).to(dev)
+    v_dev = torch.from_numpy(inp.v).to(dev)
+    q_dev = torch.from_numpy(inp.q).to(dev)
+    lengths = torch.from_numpy(lengths_np).to(dev)
+    max_len = int(lengths_np.max())
+
+    footprint = B * Hkv * T * (kr + vr + 8)
+    ncopies = 1 if args.cold_bytes <= 0 else max(2, math.ceil(args.cold_bytes / footprint))
+
+    def encode_into(codec, x, codes, norms, t0, t1):
+        xv = x.view(B * Hkv, T, d).permute(1, 0, 2)[t0:t1]
+        cv = codes.view(B * Hkv, T, codec.row_bytes).permute(1, 0, 2)[t0:t1]
+        nv = norms.view(B * Hkv, T).permute(1, 0)[t0:t1]
+        tq.tq_encode(codec, xv, cv, nv)
+
+    copies = []
+    for i in range(ncopies):
+        kcd = torch.empty((B, Hkv, T, kr), dtype=torch.uint8, device=dev)
+        vcd = torch.empty((B, Hkv, T, vr), dtype=torch.uint8, device=dev)
+        knd = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+        vnd = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+        # setup: everything before the pending batch is already in the cache
+        encode_into(kc, k_dev, kcd, knd, 0, T - P)
+        encode_into(vc, v_dev, vcd, vnd, 0, T - P)
+        copies.append((kcd, knd, vcd, vnd))
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, max_len), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+
+    def step(i):
+        kcd, knd, vcd, vnd = copies[i % ncopies]
+        if P:
+            encode_into(kc, k_dev, kcd, knd, T - P, T)
+            encode_into(vc, v_dev, vcd, vnd, T - P, T)
+        tq.tq_decode_attend(kc, vc, q_dev, kcd, knd, vcd, vnd, lengths, max_len, scale, out, ws)
+
+    stream = torch.cuda.current_stream()
+    # ---- split-kernel timing (eager, HIP events recorded by the library around the kernel)
+    hip = Hip()
+    n_ev = max(args.steps, 20)
+    evs = [(hip.event(), hip.event()) for _ in range(n_ev)]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        tq.tq_set_split_events(evs[i][0], evs[i][1])
+        step(i)
+    tq.tq_set_split_events(None, None)
+    torch.cuda.synchronize()
+    split_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    split_avg_ms = float(np.mean(split_ms))
+
+    # ---- whole-step timing: K steps captured in a graph (one launch per step set)
+    graph = None
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(ncopies):
+                    step(i)
+            graph = g
+        except Exception as e:  # capture unsupported: fall back to eager launches
+            print(f"graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+            torch.cuda.synchronize()
+    reps = max(1, args.steps // ncopies) if graph is not None else 0
+    n_steps = reps * ncopies if graph is not None else args.steps
+    if graph is not None:
+        for _ in range(max(1, args.warmup // ncopies)):
+            graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_host0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for i in range(n_steps):
+            step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / n_steps
+
+    alg_bytes = workloads.algorithmic_bytes(lengths_np, Hkv, d, wl.k_bits, wl.v_bits)
+    ctx_tokens = int(lengths_np.sum())
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
+            "context": int(max_len), "k_bits": wl.k_bits, "v_bits": wl.v_bits,
+            "pending_encode_tokens": P, "cold_copies": ncopies,
+            "splits": tq.tq_attend_num_splits(B, Hq, Hkv, d, max_len),
+            "timing": "graph replay" if graph is not None else "eager",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "ctx_tokens_per_s": round(ctx_tokens / (ms_per_step * 1e-3), 1),
+        "host_wall_s": round(t_host, 4),
+        "roofline": {
+            "kernel": "attend_split_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_us": round(split_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

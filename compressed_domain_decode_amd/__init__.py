@@ -1,0 +1,237 @@
+"""compressed_domain_decode_amd -- TurboQuant-style KV-cache compression and
+compressed-domain decode attention for MI355X (gfx950).
+
+A thin ctypes binding over libtq.so, whose C ABI is declared in include/tq.h.
+Every function here has the name of the C entry point it wraps and does only
+argument marshalling: torch tensors supply device pointers and strides, and
+torch's current HIP stream is passed through. All computation happens in the
+library's HIP kernels. If libtq.so is missing this package raises on import;
+there is no fallback path.
+
+Build the library first:  python compressed_domain_decode_amd/build.py
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK = 0
+TQ_ERR_INVALID_ARG = -1
+TQ_ERR_UNSUPPORTED = -2
+TQ_ERR_WORKSPACE = -3
+TQ_ERR_HIP = -4
+TQ_ERR_NOMEM = -5
+
+# C symbols the header declares; the ABI test checks the library exports each.
+EXPORTED = (
+    "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
+    "tq_encode", "tq_attend_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
+    "tq_status_string", "tq_last_error", "tq_set_split_events",
+)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python compressed_domain_decode_amd/build.py` "
+        "(the HIP library is required, there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_lib.tq_codec_init.argtypes = [_I, _I, ctypes.c_uint64, ctypes.POINTER(_P)]
+_lib.tq_codec_init.restype = _I
+_lib.tq_codec_destroy.argtypes = [_P]
+_lib.tq_codec_destroy.restype = None
+_lib.tq_codec_tables.argtypes = [_P, _P, _P, _P]
+_lib.tq_codec_tables.restype = _I
+_lib.tq_codec_info.argtypes = [_P, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_uint64)]
+_lib.tq_codec_info.restype = _I
+_lib.tq_row_bytes.argtypes = [_I, _I]
+_lib.tq_row_bytes.restype = _I
+_lib.tq_encode.argtypes = [_P, _P, _I, _I, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]
+_lib.tq_encode.restype = _I
+_lib.tq_attend_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.tq_attend_workspace_bytes.restype = ctypes.c_size_t
+_lib.tq_attend_num_splits.argtypes = [_I, _I, _I, _I, _I]
+_lib.tq_attend_num_splits.restype = _I
+_lib.tq_decode_attend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
+                                  ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_decode_attend.restype = _I
+_lib.tq_set_split_events.argtypes = [_P, _P]
+_lib.tq_set_split_events.restype = _I
+_lib.tq_status_string.argtypes = [_I]
+_lib.tq_status_string.restype = ctypes.c_char_p
+_lib.tq_last_error.argtypes = []
+_lib.tq_last_error.restype = ctypes.c_char_p
+
+
+def _status_name(s: int) -> str:
+    return _lib.tq_status_string(s).decode()
+
+
+def tq_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def tq_last_error() -> str:
+    return _lib.tq_last_error().decode()
+
+
+def _check(status: int):
+    if status != TQ_OK:
+        raise TQError(status, tq_last_error())
+
+
+def _stream_ptr(stream):
+    """A hipStream_t as an int: explicit value, a torch stream, or torch's current one."""
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+# ------------------------------------------------------------------ codec
+
+class Codec:
+    """Owns one tq_codec handle (host memory only)."""
+
+    def __init__(self, handle: int, dim: int, bits: int, seed: int):
+        self._h = ctypes.c_void_p(handle)
+        self.dim, self.bits, self.seed = dim, bits, seed
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def row_bytes(self) -> int:
+        return self.dim * self.bits // 8
+
+    def close(self):
+        if self._h:
+            _lib.tq_codec_destroy(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __repr__(self):
+        return f"Codec(dim={self.dim}, bits={self.bits}, seed={self.seed})"
+
+
+def tq_codec_init(dim: int, bits: int, seed: int) -> Codec:
+    h = ctypes.c_void_p()
+    _check(_lib.tq_codec_init(dim, bits, ctypes.c_uint64(seed), ctypes.byref(h)))
+    return Codec(h.value, dim, bits, seed)
+
+
+def tq_codec_destroy(codec: Codec) -> None:
+    codec.close()
+
+
+def tq_codec_tables(codec: Codec):
+    """(signs int8[dim], centroids float32[2^bits], boundaries float32[2^bits-1]) host copies."""
+    s = np.zeros(codec.dim, np.int8)
+    c = np.zeros(1 << codec.bits, np.float32)
+    b = np.zeros((1 << codec.bits) - 1, np.float32)
+    _check(_lib.tq_codec_tables(codec.handle, s.ctypes.data, c.ctypes.data, b.ctypes.data))
+    return s, c, b
+
+
+def tq_codec_info(codec: Codec):
+    d, b, s = _I(), _I(), ctypes.c_uint64()
+    _check(_lib.tq_codec_info(codec.handle, ctypes.byref(d), ctypes.byref(b), ctypes.byref(s)))
+    return d.value, b.value, s.value
+
+
+def tq_row_bytes(dim: int, bits: int) -> int:
+    return _lib.tq_row_bytes(dim, bits)
+
+
+# ------------------------------------------------------------------ encode
+
+def tq_encode(codec: Codec, x, codes, norms, stream=None) -> None:
+    """Encode x[n_tok][n_head][dim] (fp16, any strides, last dim contiguous) into
+    codes[n_tok][n_head][row_bytes] (uint8) and norms[n_tok][n_head] (fp32).
+    Strides are read from the tensors, so views into a [B][H][T][...] cache
+    (e.g. cache[b].transpose(0, 1)[t0:t1]) encode in place."""
+    n_tok, n_head, d = x.shape
+    if d != codec.dim or x.stride(2) != 1:
+        raise TQError(TQ_ERR_INVALID_ARG, "x must be [n_tok][n_head][dim] with contiguous dim")
+    if tuple(codes.shape) != (n_tok, n_head, codec.row_bytes) or codes.stride(2) != 1:
+        raise TQError(TQ_ERR_INVALID_ARG, "codes must be [n_tok][n_head][row_bytes], row contiguous")
+    if tuple(norms.shape) != (n_tok, n_head):
+        raise TQError(TQ_ERR_INVALID_ARG, "norms must be [n_tok][n_head]")
+    _check(_lib.tq_encode(codec.handle, _ptr(x), n_tok, n_head, x.stride(0), x.stride(1),
+                          _ptr(codes), codes.stride(0), codes.stride(1), _ptr(norms),
+                          norms.stride(0), norms.stride(1), _stream_ptr(stream)))
+
+
+# ------------------------------------------------------------------ attend
+
+def tq_attend_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, dim: int,
+                              max_len: int) -> int:
+    return int(_lib.tq_attend_workspace_bytes(batch, n_q_heads, n_kv_heads, dim, max_len))
+
+
+def tq_attend_num_splits(batch: int, n_q_heads: int, n_kv_heads: int, dim: int,
+                         max_len: int) -> int:
+    return int(_lib.tq_attend_num_splits(batch, n_q_heads, n_kv_heads, dim, max_len))
+
+
+def tq_decode_attend(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms, lengths,
+                     max_len: int, scale: float, out, workspace, stream=None) -> None:
+    """q [B][Hq][d] fp16; codes [B][Hkv][max_ctx][row] uint8; norms [B][Hkv][max_ctx] fp32;
+    lengths int32[B] (device); out [B][Hq][d] fp32; workspace uint8 tensor of at least
+    tq_attend_workspace_bytes(...) bytes. All contiguous."""
+    B, Hq, d = q.shape
+    Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
+    for name, t in (("q", q), ("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
+                    ("v_norms", v_norms), ("lengths", lengths), ("out", out),
+                    ("workspace", workspace)):
+        if not t.is_contiguous():
+            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
+       tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
+       tuple(v_norms.shape) != (B, Hkv, max_ctx) or tuple(out.shape) != (B, Hq, d) or \
+       tuple(lengths.shape) != (B,):
+        raise TQError(TQ_ERR_INVALID_ARG, "cache / output shapes disagree")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tq_decode_attend(kc.handle, vc.handle, _ptr(q), B, Hq, Hkv, _ptr(k_codes),
+                                 _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), max_ctx,
+                                 _ptr(lengths), int(max_len), float(scale), _ptr(out),
+                                 _ptr(workspace), nbytes, _stream_ptr(stream)))
+
+
+def tq_set_split_events(before, after) -> None:
+    """Record caller-owned hipEvent_t handles (ints) around the split-attend
+    kernel of subsequent tq_decode_attend calls on this thread; None, None stops."""
+    _check(_lib.tq_set_split_events(before, after))
+
+
+def library_path() -> str:
+    return LIB_PATH

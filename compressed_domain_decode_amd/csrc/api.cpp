@@ -1,0 +1,223 @@
+// api.cpp -- the C ABI declared in include/tq.h: argument validation, launch
+// planning and error reporting. Every check runs on the host before anything
+// is enqueued, so a failing call leaves the stream untouched.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/tq.h"
+#include "codec.hpp"
+#include "kernels.hpp"
+
+struct tq_codec {
+  tq::CodecTables tabs;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_split_before = nullptr;
+thread_local hipEvent_t g_split_after = nullptr;
+
+tq_status fail(tq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tq_status ok() {
+  g_last_error.clear();
+  return TQ_OK;
+}
+
+bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+tq::SignArg sign_arg(const tq_codec* c) {
+  tq::SignArg s;
+  std::memcpy(s.bits, c->tabs.sign_bits, sizeof(s.bits));
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    case TQ_ERR_NOMEM: return "TQ_ERR_NOMEM";
+  }
+  return "TQ_ERR_UNKNOWN";
+}
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+int tq_row_bytes(int dim, int bits) {
+  if (dim <= 0 || bits < 1 || bits > 8) return 0;
+  return dim * bits / 8;
+}
+
+tq_status tq_codec_init(int dim, int bits, uint64_t seed, tq_codec** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codec_init: out is NULL");
+  *out = nullptr;
+  if (!dim_ok(dim))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_init: dim %d not in {64, 128, 256}", dim);
+  if (bits < 1 || bits > 8)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_init: bits %d not in [1, 8]", bits);
+  tq_codec* c = new (std::nothrow) tq_codec;
+  if (!c) return fail(TQ_ERR_NOMEM, "tq_codec_init: out of host memory");
+  if (!tq::build_codec(dim, bits, seed, &c->tabs)) {
+    delete c;
+    return fail(TQ_ERR_INVALID_ARG, "tq_codec_init: Lloyd-Max solve did not converge");
+  }
+  *out = c;
+  return ok();
+}
+
+void tq_codec_destroy(tq_codec* c) { delete c; }
+
+tq_status tq_codec_tables(const tq_codec* c, int8_t* signs, float* centroids,
+                          float* boundaries) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_codec_tables: codec is NULL");
+  const int n = 1 << c->tabs.bits;
+  if (signs)
+    for (int j = 0; j < c->tabs.dim; ++j)
+      signs[j] = ((c->tabs.sign_bits[j >> 5] >> (j & 31)) & 1u) ? -1 : 1;
+  if (centroids) std::memcpy(centroids, c->tabs.centroids, sizeof(float) * n);
+  if (boundaries) std::memcpy(boundaries, c->tabs.boundaries, sizeof(float) * (n - 1));
+  return ok();
+}
+
+tq_status tq_codec_info(const tq_codec* c, int* dim, int* bits, uint64_t* seed) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_codec_info: codec is NULL");
+  if (dim) *dim = c->tabs.dim;
+  if (bits) *bits = c->tabs.bits;
+  if (seed) *seed = c->tabs.seed;
+  return ok();
+}
+
+tq_status tq_encode(const tq_codec* c, const void* x_fp16, int n_tok, int n_head,
+                    int64_t x_stride_tok, int64_t x_stride_head, uint8_t* codes,
+                    int64_t c_stride_tok, int64_t c_stride_head, float* norms,
+                    int64_t n_stride_tok, int64_t n_stride_head, void* stream) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_encode: codec is NULL");
+  if (n_tok < 0 || n_head < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_encode: negative count (n_tok %d, n_head %d)", n_tok,
+                n_head);
+  if (n_tok == 0 || n_head == 0) return ok();
+  if (!x_fp16 || !codes || !norms) return fail(TQ_ERR_INVALID_ARG, "tq_encode: NULL pointer");
+  if (((uintptr_t)codes & 3) || (c_stride_tok & 3) || (c_stride_head & 3))
+    return fail(TQ_ERR_INVALID_ARG,
+                "tq_encode: codes pointer and strides must be multiples of 4 bytes");
+  if (((uintptr_t)x_fp16 & 1) || ((uintptr_t)norms & 3))
+    return fail(TQ_ERR_INVALID_ARG, "tq_encode: misaligned x or norms pointer");
+  const long long nvec = (long long)n_tok * n_head;
+  if ((nvec + 3) / 4 > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "tq_encode: too many vectors");
+  tq::EncodeTables tabs;
+  tabs.sign = sign_arg(c);
+  std::memcpy(tabs.boundaries, c->tabs.boundaries, sizeof(tabs.boundaries));
+  hipError_t err = tq::launch_encode(c->tabs.dim, c->tabs.bits, x_fp16, n_tok, n_head,
+                                     x_stride_tok, x_stride_head, codes, c_stride_tok,
+                                     c_stride_head, norms, n_stride_tok, n_stride_head, tabs,
+                                     (hipStream_t)stream);
+  if (err != hipSuccess)
+    return fail(TQ_ERR_HIP, "tq_encode: launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
+tq_status tq_set_split_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(TQ_ERR_INVALID_ARG, "tq_set_split_events: give both events or neither");
+  g_split_before = (hipEvent_t)before;
+  g_split_after = (hipEvent_t)after;
+  return ok();
+}
+
+static bool attend_shape_ok(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
+  return batch > 0 && n_kv_heads > 0 && n_q_heads > 0 && n_q_heads % n_kv_heads == 0 &&
+         n_q_heads / n_kv_heads <= 16 && dim_ok(dim) && max_len > 0 && batch <= 65535 &&
+         n_kv_heads <= 65535;
+}
+
+size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int dim,
+                                 int max_len) {
+  if (!attend_shape_ok(batch, n_q_heads, n_kv_heads, dim, max_len)) return 0;
+  return tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len).total_bytes;
+}
+
+int tq_attend_num_splits(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
+  if (!attend_shape_ok(batch, n_q_heads, n_kv_heads, dim, max_len)) return 0;
+  return tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len).splits;
+}
+
+tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                           int batch, int n_q_heads, int n_kv_heads,
+                           const uint8_t* k_codes, const float* k_norms,
+                           const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                           const int32_t* lengths, int max_len, float scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: codec is NULL");
+  if (kc->tabs.dim != vc->tabs.dim)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: K dim %d != V dim %d", kc->tabs.dim,
+                vc->tabs.dim);
+  const int dim = kc->tabs.dim;
+  if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: batch %d, heads %d/%d must be positive",
+                batch, n_q_heads, n_kv_heads);
+  if (n_q_heads % n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: %d query heads not a multiple of %d",
+                n_q_heads, n_kv_heads);
+  if (n_q_heads / n_kv_heads > 16)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attend: group size %d > 16",
+                n_q_heads / n_kv_heads);
+  if (batch > 65535 || n_kv_heads > 65535)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attend: batch or kv heads above 65535");
+  if (max_len <= 0 || max_len > max_ctx)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: need 1 <= max_len (%d) <= max_ctx (%d)",
+                max_len, max_ctx);
+  if (!q_fp16 || !k_codes || !k_norms || !v_codes || !v_norms || !lengths || !out)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: NULL pointer");
+  if (((uintptr_t)k_codes & 3) || ((uintptr_t)v_codes & 3) || ((uintptr_t)k_norms & 3) ||
+      ((uintptr_t)v_norms & 3) || ((uintptr_t)out & 3) || ((uintptr_t)lengths & 3) ||
+      ((uintptr_t)q_fp16 & 1))
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: misaligned pointer");
+  if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: scale is NaN");
+  const int group = n_q_heads / n_kv_heads;
+  if (!tq::attend_supported(dim, kc->tabs.bits, vc->tabs.bits, group))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "tq_decode_attend: no kernel for dim %d, K %d-bit, V %d-bit, group %d", dim,
+                kc->tabs.bits, vc->tabs.bits, group);
+  const tq::AttendPlan plan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
+  if ((long long)plan.splits > 0x7fffffffLL)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attend: context too long");
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(TQ_ERR_WORKSPACE, "tq_decode_attend: workspace %zu bytes, need %zu",
+                workspace ? workspace_bytes : (size_t)0, plan.total_bytes);
+  if ((uintptr_t)workspace & 255)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: workspace must be 256-byte aligned");
+  tq::AttendTables tabs;
+  std::memcpy(tabs.k_centroids, kc->tabs.centroids, sizeof(tabs.k_centroids));
+  std::memcpy(tabs.v_centroids, vc->tabs.centroids, sizeof(tabs.v_centroids));
+  hipError_t err = tq::launch_attend(dim, kc->tabs.bits, vc->tabs.bits, batch, n_q_heads,
+                                     n_kv_heads, q_fp16, sign_arg(kc), sign_arg(vc), tabs,
+                                     k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
+                                     max_len, scale, out, workspace, plan, g_split_before,
+                                     g_split_after, (hipStream_t)stream);
+  if (err != hipSuccess)
+    return fail(TQ_ERR_HIP, "tq_decode_attend: launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+/*
+ * tq.h -- C ABI of the compressed-domain KV decode library (MI355X, gfx950).
+ *
+ * The method (TurboQuant-style KV-cache compression, as described in the
+ * mlx-swift-lm pull request "add TurboQuant KV cache compression", the
+ * VeloxQuant "How I built" post and the turboquant-mlx KV-cache guide):
+ *
+ *   encode   x (fp16, d values)  ->  norm N = |x|_2 (fp32)
+ *                                    codes idx_j = #{k : beta_k < z_j}, packed LSB-first
+ *            where w = H (sigma (.) x), z = w / N, H the d x d Sylvester-Hadamard
+ *            matrix, sigma a seeded +/-1 vector and beta the midpoints of the
+ *            2^bits-level Lloyd-Max codebook c for N(0,1).
+ *   attend   out = sum_t softmax_t(scale * <q, k_hat_t>) v_hat_t over the
+ *            compressed cache, where x_hat = (N/d) sigma (.) (H c[idx]); computed
+ *            in the rotated basis: K is scored against H (sigma_K (.) q), V is
+ *            accumulated as N c[idx] and one inverse transform per head ends it.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device memory (or host memory the device can read)
+ *     owned by the caller; the library never allocates, frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue work on it and return without waiting.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failing call enqueues nothing. tq_last_error() then holds a message.
+ *   - Supported: dim in {64, 128, 256}; bits in [1, 8]; n_q_heads a multiple
+ *     of n_kv_heads with n_q_heads / n_kv_heads <= 16.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, stride or alignment    */
+  TQ_ERR_UNSUPPORTED = -2, /* valid request the kernels do not cover; a      */
+                           /* caller may fall back to another path           */
+  TQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  TQ_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed     */
+  TQ_ERR_NOMEM = -5        /* host allocation failed                          */
+} tq_status;
+
+/* Opaque codec: sign vector and fp32 Lloyd-Max tables for one (dim, bits, seed).
+ * Immutable after init, host memory only, shareable across threads, streams,
+ * devices and layers (all layers with the same triple share one codec, as in
+ * the PR's "shared codecs" design note). The tables travel to the GPU inside
+ * each launch's kernel arguments, so a codec holds no device memory. */
+typedef struct tq_codec tq_codec;
+
+/* Build a codec. dim: head dimension (64, 128 or 256; the Hadamard rotation
+ * needs a power of two). bits: code width (1..8), 2^bits centroids.
+ * seed: sign-vector seed; sign j is -1 iff the top bit of the j-th SplitMix64
+ * output for that seed is set. The codebook is the Lloyd-Max fixed point for
+ * N(0,1) (boundaries are centroid midpoints, centroids are cell conditional
+ * means), solved on the host in quad precision and rounded once to fp32.
+ * Errors: TQ_ERR_UNSUPPORTED for other dims/bits, TQ_ERR_INVALID_ARG for NULL out. */
+tq_status tq_codec_init(int dim, int bits, uint64_t seed, tq_codec** out);
+
+/* Free a codec (NULL is a no-op). Work already enqueued keeps its own copy of
+ * the tables in its kernel arguments, so a codec may be destroyed at any time. */
+void tq_codec_destroy(tq_codec* c);
+
+/* Host copies of the codec's tables: signs[dim] (+1/-1), centroids[2^bits],
+ * boundaries[2^bits - 1] (each may be NULL to skip). */
+tq_status tq_codec_tables(const tq_codec* c, int8_t* signs, float* centroids,
+                          float* boundaries);
+
+/* dim, bits and seed of a codec (each pointer may be NULL). */
+tq_status tq_codec_info(const tq_codec* c, int* dim, int* bits, uint64_t* seed);
+
+/* Bytes of one packed code row: dim * bits / 8. */
+int tq_row_bytes(int dim, int bits);
+
+/*
+ * Encode n_tok x n_head vectors (the PR's batch recompression of pending
+ * tokens; a cache append is this call with the destination offset to the
+ * append position).
+ *   x_fp16: vector (t, h) starts at element t*x_stride_tok + h*x_stride_head
+ *           (in fp16 elements); its dim values are contiguous.
+ *   codes:  row (t, h) starts at byte t*c_stride_tok + h*c_stride_head and
+ *           receives dim*bits/8 bytes; pointer and strides must be multiples of 4.
+ *   norms:  norm (t, h) is written at element t*n_stride_tok + h*n_stride_head.
+ * Results are bit-exact with the definition above: the rotation and norm are
+ * computed in fp64 (the rotation of fp16 input is exact; the squared norm is
+ * summed over the canonical pairwise tree), z = w/N in IEEE fp64, a zero
+ * vector encodes to norm 0 and index 2^(bits-1)-1 everywhere.
+ * n_tok == 0 or n_head == 0 enqueues nothing and returns TQ_OK.
+ */
+tq_status tq_encode(const tq_codec* c, const void* x_fp16, int n_tok, int n_head,
+                    int64_t x_stride_tok, int64_t x_stride_head, uint8_t* codes,
+                    int64_t c_stride_tok, int64_t c_stride_head, float* norms,
+                    int64_t n_stride_tok, int64_t n_stride_head, void* stream);
+
+/* Workspace bytes tq_decode_attend needs for this shape (split partials and
+ * the rotated queries). A pure function of its arguments; 0 on invalid input. */
+size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int dim,
+                                 int max_len);
+
+/*
+ * Decode attention straight from the packed cache (the fused compressed-domain
+ * decode of the X post and the turboquant-mlx guide: score, softmax and inline
+ * dequantisation without expanding the cache).
+ *   kc, vc:     codecs of the K and V caches (same dim; bits may differ).
+ *   q_fp16:     [batch][n_q_heads][dim] fp16, contiguous.
+ *   k_codes:    [batch][n_kv_heads][max_ctx][dim*kc_bits/8] bytes, contiguous.
+ *   k_norms:    [batch][n_kv_heads][max_ctx] fp32.  v_codes / v_norms likewise.
+ *   lengths:    device int32[batch]; sequence b attends to rows [0, lengths[b]).
+ *               Values are clamped to max_len on the device, so the cache is
+ *               never read past max_len rows; a length <= 0 gives a zero row.
+ *   max_len:    host-side upper bound of lengths, 1 <= max_len <= max_ctx; it
+ *               sizes the launch.
+ *   scale:      softmax scale (1/sqrt(dim) for standard attention).
+ *   out:        [batch][n_q_heads][dim] fp32. Query head h reads KV head
+ *               h / (n_q_heads / n_kv_heads).
+ *   workspace:  device buffer of at least tq_attend_workspace_bytes(...) bytes,
+ *               256-byte aligned; its contents need not be initialised.
+ * Three kernels are enqueued (query rotation, split attend, combine + inverse
+ * rotation). Results agree with softmax attention over the dequantised cache
+ * (computed in fp64) to about 1e-5 absolute for unit-scale inputs; fp32 sums
+ * in a different order make the low bits differ from any serial evaluation.
+ */
+tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                           int batch, int n_q_heads, int n_kv_heads,
+                           const uint8_t* k_codes, const float* k_norms,
+                           const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                           const int32_t* lengths, int max_len, float scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement hook (per calling thread): while `before` and `after` are
+ * non-NULL, each tq_decode_attend records the hipEvent_t `before` on its stream
+ * immediately before the split-attend kernel and `after` immediately after it,
+ * so a caller can time that kernel alone with hipEventElapsedTime. The events
+ * are created and owned by the caller. Pass NULL, NULL to stop. */
+tq_status tq_set_split_events(void* before, void* after);
+
+/* Number of context splits tq_decode_attend launches for this shape (for
+ * measurement and tests); 0 on invalid input. */
+int tq_attend_num_splits(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len);
+
+/* Static text for a status code. */
+const char* tq_status_string(tq_status s);
+
+/* Detail text of the last failing call on this thread ("" if none). */
+const char* tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,150 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+symbol include/tq.h declares, builds codec tables identical to the oracle's,
+and rejects bad arguments before enqueueing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import compressed_domain_decode_amd as tq
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    declared = _declared_functions()
+    assert set(declared) == set(tq.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for f in declared:
+        assert hasattr(lib, f)
+
+
+def test_header_compiles_as_plain_c():
+    r = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Werror", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_library_has_no_oracle_dependency():
+    out = subprocess.run(["nm", "-D", tq.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "orc_" not in out
+    deps = subprocess.run(["ldd", tq.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+
+
+@pytest.mark.parametrize("dim", [64, 128, 256])
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_codec_tables_match_oracle_bitwise(dim, bits):
+    c = tq.tq_codec_init(dim, bits, 42)
+    s, cent, bnd = tq.tq_codec_tables(c)
+    o = oracle.Codec(dim, bits, 42)
+    np.testing.assert_array_equal(s, o.signs)
+    assert cent.tobytes() == o.centroids.tobytes()
+    assert bnd.tobytes() == o.boundaries.tobytes()
+    assert tq.tq_codec_info(c) == (dim, bits, 42)
+    assert tq.tq_row_bytes(dim, bits) == dim * bits // 8
+
+
+@pytest.mark.parametrize("seed", [0, 1, 7, 2**63 + 5])
+def test_codec_signs_match_oracle_for_seeds(seed):
+    c = tq.tq_codec_init(128, 3, seed)
+    np.testing.assert_array_equal(tq.tq_codec_tables(c)[0], oracle.signs(seed, 128))
+
+
+@pytest.mark.parametrize("dim,bits", [(32, 4), (96, 4), (512, 4), (0, 4), (128, 0), (128, 9), (128, -1)])
+def test_codec_init_rejects_unsupported(dim, bits):
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_codec_init(dim, bits, 1)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    assert "tq_codec_init" in tq.tq_last_error()
+
+
+def test_codec_init_null_out():
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    lib.tq_codec_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p]
+    assert lib.tq_codec_init(128, 4, 1, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s, name in [(0, "TQ_OK"), (-1, "TQ_ERR_INVALID_ARG"), (-2, "TQ_ERR_UNSUPPORTED"),
+                    (-3, "TQ_ERR_WORKSPACE"), (-4, "TQ_ERR_HIP"), (-5, "TQ_ERR_NOMEM")]:
+        assert tq.tq_status_string(s) == name
+
+
+# ---- argument validation: every call below fails before any HIP call is made
+
+_lib = ctypes.CDLL(tq.LIB_PATH)
+_lib.tq_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                           ctypes.c_void_p]
+_lib.tq_decode_attend.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + \
+    [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+def test_encode_validation():
+    c = tq.tq_codec_init(128, 4, 1)
+    h = c.handle
+    assert _lib.tq_encode(None, FAKE, 1, 1, 128, 128, FAKE, 64, 64, FAKE, 1, 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert _lib.tq_encode(h, None, 1, 1, 128, 128, FAKE, 64, 64, FAKE, 1, 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert _lib.tq_encode(h, FAKE, -1, 1, 128, 128, FAKE, 64, 64, FAKE, 1, 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert _lib.tq_encode(h, FAKE, 1, 1, 128, 128, FAKE + 2, 64, 64, FAKE, 1, 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert _lib.tq_encode(h, FAKE, 1, 1, 128, 128, FAKE, 66, 64, FAKE, 1, 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert _lib.tq_encode(h, FAKE + 1, 1, 1, 128, 128, FAKE, 64, 64, FAKE, 1, 1, None) == tq.TQ_ERR_INVALID_ARG
+    # nothing to do is fine and touches nothing
+    assert _lib.tq_encode(h, None, 0, 5, 0, 0, None, 0, 0, None, 0, 0, None) == tq.TQ_OK
+
+
+def _attend_call(kc, vc, B=1, Hq=4, Hkv=2, max_ctx=256, max_len=256, ws=FAKE, ws_bytes=1 << 30,
+                 q=FAKE, out=FAKE):
+    return _lib.tq_decode_attend(kc.handle, vc.handle, q, B, Hq, Hkv, FAKE, FAKE, FAKE, FAKE,
+                                 max_ctx, FAKE, max_len, 0.125, out, ws, ws_bytes, None)
+
+
+def test_decode_attend_validation():
+    kc, vc = tq.tq_codec_init(64, 4, 42), tq.tq_codec_init(64, 4, 42)
+    vc128 = tq.tq_codec_init(128, 4, 42)
+    assert _attend_call(kc, vc128) == tq.TQ_ERR_INVALID_ARG          # dim mismatch
+    assert _attend_call(kc, vc, Hq=5, Hkv=2) == tq.TQ_ERR_INVALID_ARG  # ratio
+    assert _attend_call(kc, vc, Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED  # group 17
+    assert _attend_call(kc, vc, B=0) == tq.TQ_ERR_INVALID_ARG
+    assert _attend_call(kc, vc, max_len=300, max_ctx=256) == tq.TQ_ERR_INVALID_ARG
+    assert _attend_call(kc, vc, max_len=0) == tq.TQ_ERR_INVALID_ARG
+    assert _attend_call(kc, vc, q=None) == tq.TQ_ERR_INVALID_ARG
+    assert _attend_call(kc, vc, out=FAKE + 2) == tq.TQ_ERR_INVALID_ARG
+    need = tq.tq_attend_workspace_bytes(1, 4, 2, 64, 256)
+    assert need > 0
+    assert _attend_call(kc, vc, ws_bytes=need - 1) == tq.TQ_ERR_WORKSPACE
+    assert _attend_call(kc, vc, ws=None) == tq.TQ_ERR_WORKSPACE
+    assert _attend_call(kc, vc, ws=FAKE + 64) == tq.TQ_ERR_INVALID_ARG  # not 256-aligned
+    assert "workspace" in tq.tq_last_error() or "aligned" in tq.tq_last_error()
+
+
+def test_workspace_and_split_plan():
+    assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
+    assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0
+    for (B, Hq, Hkv, d, L) in [(1, 4, 2, 64, 256), (1, 32, 8, 128, 32768), (16, 32, 8, 128, 8192),
+                               (1, 64, 8, 64, 131072), (1, 24, 8, 128, 4096)]:
+        S = tq.tq_attend_num_splits(B, Hq, Hkv, d, L)
+        ws = tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, L)
+        assert S >= 1
+        assert ws >= B * Hq * d * 4 + B * Hq * S * (d + 2) * 4
+        assert ws % 256 == 0

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: packed codes byte-identical and norms bit-identical (the contract is
+exact, stronger than the required 1e-5 relative); decode-attend outputs within
+2e-3 max-abs of the oracle's fp64 result. Oracle inputs never come from the
+HIP path: the oracle encodes its own copy of every cache it attends over.
+"""
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import compressed_domain_decode_amd as tq
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ATOL = 2e-3
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=None)
+def codecs(dim, bits, seed=42):
+    return tq.tq_codec_init(dim, bits, seed), oracle.Codec(dim, bits, seed)
+
+
+def gpu_encode_rows(codec, x_np):
+    """x_np (N, H, d) fp16 -> (codes (N, H, row), norms (N, H)) via one tq_encode."""
+    N, H, d = x_np.shape
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(DEV)
+    codes = torch.full((N, H, codec.row_bytes), 0xA5, dtype=torch.uint8, device=DEV)
+    norms = torch.full((N, H), -1.0, dtype=torch.float32, device=DEV)
+    tq.tq_encode(codec, x, codes, norms)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), norms.cpu().numpy()
+
+
+def gpu_encode_cache(codec, x_dev):
+    """x_dev (B, Hkv, T, d) fp16 on device -> device codes (B, Hkv, T, row), norms (B, Hkv, T).
+    One call: (B*Hkv) heads of T tokens, written straight into the cache layout."""
+    B, H, T, d = x_dev.shape
+    codes = torch.empty((B, H, T, codec.row_bytes), dtype=torch.uint8, device=DEV)
+    norms = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    xv = x_dev.view(B * H, T, d).permute(1, 0, 2)
+    cv = codes.view(B * H, T, codec.row_bytes).permute(1, 0, 2)
+    nv = norms.view(B * H, T).permute(1, 0)
+    tq.tq_encode(codec, xv, cv, nv)
+    return codes, norms
+
+
+def gpu_attend(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np, scale=None, max_len=None):
+    B, Hq, d = q_np.shape
+    Hkv, T = knorms.shape[1], knorms.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if max_len is None:
+        max_len = max(1, int(np.max(lengths_np)))
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).to(DEV)
+    lengths = torch.from_numpy(np.asarray(lengths_np, dtype=np.int32)).to(DEV)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, max_len), dtype=torch.uint8, device=DEV)
+    tq.tq_decode_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, max_len, scale, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+# ------------------------------------------------------------------ encode
+
+def _encode_inputs(d, seed):
+    rng = np.random.default_rng(seed)
+    n = 384
+    x = rng.standard_normal((n, 2, d)) * rng.uniform(1e-3, 50, size=(n, 1, 1))
+    x[0] = 0.0                                   # zero vector
+    x[1, 0] = 6e-8                               # fp16 subnormals only
+    x[2, 0, :] = 1.0                             # all equal
+    x[3, 0] = rng.choice([-65504.0, 65504.0], size=d)  # largest magnitude
+    x[4, 0] = 0.0
+    x[4, 0, d // 3] = 3.0                        # one-hot
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_encode_matches_oracle(d, bits):
+    announce(f"encode d={d} bits={bits}")
+    g, o = codecs(d, bits)
+    x = _encode_inputs(d, d * 10 + bits)
+    codes, norms = gpu_encode_rows(g, x)
+    oc, on, _ = oracle.encode(o, x)
+    assert codes.tobytes() == oc.tobytes()
+    assert norms.tobytes() == on.tobytes()
+
+
+def test_encode_strided_views_and_append():
+    announce("encode strided views / append")
+    d, bits = 128, 3
+    g, o = codecs(d, bits)
+    rng = np.random.default_rng(5)
+    B, H, T = 2, 3, 200
+    x = rng.standard_normal((B, H, T, d)).astype(np.float16)
+    codes, norms = gpu_encode_cache(g, to_dev(x))
+    torch.cuda.synchronize()
+    oc, on, _ = oracle.encode(o, x)
+    assert codes.cpu().numpy().tobytes() == oc.tobytes()
+    assert norms.cpu().numpy().tobytes() == on.tobytes()
+    # append: re-encode tokens 150..199 of sequence 1 into a cleared region
+    codes[1, :, 150:] = 0
+    norms[1, :, 150:] = 0
+    xv = to_dev(x[1]).permute(1, 0, 2)[150:]
+    tq.tq_encode(g, xv, codes[1].permute(1, 0, 2)[150:], norms[1].permute(1, 0)[150:])
+    torch.cuda.synchronize()
+    assert codes.cpu().numpy().tobytes() == oc.tobytes()
+    assert norms.cpu().numpy().tobytes() == on.tobytes()
+
+
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+def test_encode_workload_full_size_sampled(name):
+    wl = workloads.WORKLOADS[name]
+    announce(f"encode full cache {name}")
+    inp = workloads.generate(wl)
+    rng = np.random.default_rng(99)
+    for which, bits, x in (("K", wl.k_bits, inp.k), ("V", wl.v_bits, inp.v)):
+        g, o = codecs(wl.dim, bits, wl.codec_seed)
+        codes, norms = gpu_encode_cache(g, to_dev(x))
+        torch.cuda.synchronize()
+        B, H, T, _ = x.shape
+        pick = (rng.integers(0, B, 4096), rng.integers(0, H, 4096), rng.integers(0, T, 4096))
+        c_np = codes.cpu().numpy()[pick]
+        n_np = norms.cpu().numpy()[pick]
+        oc, on, _ = oracle.encode(o, x[pick])
+        assert c_np.tobytes() == oc.tobytes(), which
+        assert n_np.tobytes() == on.tobytes(), which
+
+
+# ------------------------------------------------------------------ attend
+
+def _oracle_cache(o, x):
+    c, n, _ = oracle.encode(o, x)
+    return c, n
+
+
+def _attend_case(d, kb, vb, G, lengths, Hkv=2, seed=0, T=None, kscale=1.0, vscale=1.0):
+    lengths = np.asarray(lengths, dtype=np.int32)
+    B = lengths.size
+    T = T or max(1, int(lengths.max()))
+    lens, k, v, q = workloads.small_case(seed, B, Hkv * G, Hkv, d, T, lengths, kscale, vscale)
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    kcodes, knorms = gpu_encode_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    got = gpu_attend(gk, gv, q, kcodes, knorms, vcodes, vnorms, lens)
+    okc, okn = _oracle_cache(ok, k)
+    ovc, ovn = _oracle_cache(ov, v)
+    # the GPU cache the kernel read is the oracle's cache byte for byte
+    assert kcodes.cpu().numpy().tobytes() == okc.tobytes()
+    assert vcodes.cpu().numpy().tobytes() == ovc.tobytes()
+    want = oracle.attend(ok, ov, q, okc, okn, ovc, ovn, lens)
+    return got, want
+
+
+SUPPORTED_SMALL = [
+    (64, 4, 4, 2), (64, 3, 3, 8), (64, 4, 4, 1), (64, 3, 3, 4), (64, 8, 3, 4), (64, 2, 2, 2),
+    (64, 1, 1, 2), (64, 5, 7, 2), (64, 6, 6, 16), (64, 8, 8, 1),
+    (128, 4, 2, 3), (128, 8, 3, 4), (128, 3, 3, 4), (128, 4, 4, 4), (128, 4, 3, 4), (128, 2, 2, 4),
+    (128, 8, 4, 4), (128, 4, 4, 8), (128, 8, 3, 8), (128, 4, 2, 1), (128, 3, 3, 2), (128, 8, 8, 2),
+    (128, 1, 1, 4), (128, 7, 5, 6),
+    (256, 4, 4, 4), (256, 8, 3, 4), (256, 3, 3, 2), (256, 8, 4, 1), (256, 2, 2, 8),
+]
+
+
+@pytest.mark.parametrize("d,kb,vb,G", SUPPORTED_SMALL)
+def test_attend_matches_oracle_small(d, kb, vb, G):
+    announce(f"attend d={d} K{kb} V{vb} G={G}")
+    got, want = _attend_case(d, kb, vb, G, lengths=[700, 37, 257], seed=d + kb * 10 + vb + G)
+    err = np.abs(got - want).max()
+    print(f"  max abs err {err:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+
+
+@pytest.mark.parametrize("d,kb,vb,G", [(128, 8, 3, 4), (64, 3, 3, 8), (128, 4, 2, 3)])
+def test_attend_ragged_edge_lengths(d, kb, vb, G):
+    lengths = [1, 2, 63, 64, 65, 255, 256, 257, 511, 513, 1024, 1025, 3000]
+    announce(f"attend ragged lengths d={d} K{kb} V{vb} G={G}")
+    got, want = _attend_case(d, kb, vb, G, lengths=lengths, seed=7)
+    assert np.abs(got - want).max() <= ATOL
+
+
+def test_attend_zero_length_and_single_token():
+    announce("attend zero length / single token")
+    d, kb, vb, G = 128, 8, 3, 4
+    got, want = _attend_case(d, kb, vb, G, lengths=[0, 1, 5, 0], T=300, seed=3)
+    assert np.all(got[0] == 0.0) and np.all(got[3] == 0.0)
+    assert np.abs(got - want).max() <= ATOL
+    # one token: the output is that token's dequantised V row
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    lens, k, v, q = workloads.small_case(3, 4, 8, 2, d, 300, [0, 1, 5, 0])
+    ovc, ovn = _oracle_cache(ov, v)
+    v_hat = oracle.dequant(ov, ovc, ovn)
+    for h in range(8):
+        np.testing.assert_allclose(got[1, h], v_hat[1, h // G, 0], atol=1e-5)
+
+
+def test_attend_rows_beyond_length_never_read():
+    announce("attend poisoned rows beyond length")
+    d, kb, vb, G = 128, 8, 3, 4
+    gk, _ = codecs(d, kb)
+    gv, _ = codecs(d, vb)
+    lens, k, v, q = workloads.small_case(11, 3, 8, 2, d, 1500, [1500, 700, 65])
+    kc, kn = gpu_encode_cache(gk, to_dev(k))
+    vc, vn = gpu_encode_cache(gv, to_dev(v))
+    clean = gpu_attend(gk, gv, q, kc, kn, vc, vn, lens)
+    for b, L in enumerate(lens):
+        kc[b, :, L:] = 0xFF
+        vc[b, :, L:] = 0xFF
+        kn[b, :, L:] = float("nan")
+        vn[b, :, L:] = float("nan")
+    dirty = gpu_attend(gk, gv, q, kc, kn, vc, vn, lens, max_len=1500)
+    assert clean.tobytes() == dirty.tobytes()
+
+
+def test_attend_deterministic():
+    announce("attend determinism")
+    d, kb, vb, G = 64, 3, 3, 8
+    gk, _ = codecs(d, kb)
+    gv, _ = codecs(d, vb)
+    lens, k, v, q = workloads.small_case(4, 2, 16, 2, d, 5000, [5000, 4097])
+    kc, kn = gpu_encode_cache(gk, to_dev(k))
+    vc, vn = gpu_encode_cache(gv, to_dev(v))
+    a = gpu_attend(gk, gv, q, kc, kn, vc, vn, lens)
+    b = gpu_attend(gk, gv, q, kc, kn, vc, vn, lens)
+    assert a.tobytes() == b.tobytes()
+
+
+def test_attend_distinct_heads_and_batches():
+    """Every (b, h) row differs and matches its own oracle row: a swapped
+    batch / head stride cannot hide behind identical data."""
+    announce("attend stride order")
+    d, kb, vb, G = 128, 4, 2, 3
+    got, want = _attend_case(d, kb, vb, G, lengths=[300, 290, 280], Hkv=3, seed=21)
+    flat = got.reshape(-1, d)
+    assert len({r.tobytes() for r in flat}) == flat.shape[0]
+    assert np.abs(got - want).max() <= ATOL
+
+
+def test_attend_large_scale_inputs():
+    announce("attend peaked softmax")
+    # scaled keys make the softmax concentrate on few tokens
+    got, want = _attend_case(128, 8, 3, 4, lengths=[2000, 999], seed=17, kscale=4.0, vscale=3.0)
+    assert np.abs(got - want).max() <= ATOL
+
+
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+def test_attend_workload_full_size_sampled(name):
+    """Full-size cache and launch configuration of each workload; sampled
+    (b, h) rows against the oracle, which encodes the sampled KV heads itself."""
+    wl = workloads.WORKLOADS[name]
+    announce(f"attend full size {name}")
+    inp = workloads.generate(wl)
+    gk, ok = codecs(wl.dim, wl.k_bits, wl.codec_seed)
+    gv, ov = codecs(wl.dim, wl.v_bits, wl.codec_seed)
+    kc, kn = gpu_encode_cache(gk, to_dev(inp.k))
+    vc, vn = gpu_encode_cache(gv, to_dev(inp.v))
+    got = gpu_attend(gk, gv, inp.q, kc, kn, vc, vn, inp.lengths)
+    B, Hq = wl.batch, wl.n_q_heads
+    G = wl.group
+    rng = np.random.default_rng(123)
+    if B * Hq <= 8:
+        pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    else:
+        pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(3)]
+        pairs.append((B - 1, Hq - 1))
+    worst = 0.0
+    for b, h in pairs:
+        g = h // G
+        L = int(inp.lengths[b])
+        okc, okn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L])
+        ovc, ovn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L])
+        assert kc[b, g, :L].cpu().numpy().tobytes() == okc.tobytes()
+        assert vc[b, g, :L].cpu().numpy().tobytes() == ovc.tobytes()
+        want = oracle.attend(ok, ov, inp.q[b:b + 1, g * G:(g + 1) * G], okc, okn, ovc, ovn,
+                             np.array([L], np.int32))
+        err = np.abs(got[b, g * G:(g + 1) * G] - want[0]).max()
+        worst = max(worst, err)
+    print(f"  {name}: worst max-abs err {worst:.3e} over {len(pairs)} sampled rows", flush=True)
+    assert np.isfinite(got).all()
+    assert worst <= ATOL
