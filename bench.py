@@ -53,7 +53,16 @@ class Hip:
     """hipEvent helpers through the HIP runtime (events on an explicit stream)."""
 
     def __init__(self):
-        self.lib = ctypes.CDLL("libamdhip64.so")
+        # the HIP runtime already mapped into this process (torch's copy), never a second one
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.lib = ctypes.CDLL(path)
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,

@@ -46,6 +46,11 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is not built; run `python compressed_domain_decode_amd/build.py` "
         "(the HIP library is required, there is no CPU fallback)")
 
+# The library links libamdhip64.so.7 by soname. torch ships its own copy of the
+# HIP runtime; importing torch first makes the loader reuse that copy, so the
+# process holds one HIP runtime and device pointers / streams are shared.
+import torch  # noqa: E402,F401  (loaded for its HIP runtime, before libtq.so)
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

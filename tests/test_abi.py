@@ -148,3 +148,11 @@ def test_workspace_and_split_plan():
         assert S >= 1
         assert ws >= B * Hq * d * 4 + B * Hq * S * (d + 2) * 4
         assert ws % 256 == 0
+
+
+def test_single_hip_runtime_in_process():
+    """The binding must not bring a second HIP runtime next to torch's."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip
