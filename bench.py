@@ -46,7 +46,34 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="time a plain device-to-device copy of --copy-mb MB (measured peak, and the "
+                        "reference dispatch for HBM byte counters) and exit")
+    p.add_argument("--copy-mb", type=float, default=256.0)
     return p.parse_args()
+
+
+def copy_calibration(mb, steps):
+    """Plain torch device copy of a known size: achievable streaming bandwidth and
+    the known-size dispatch the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    import torch
+    n = int(mb * 1e6) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda:0").uniform_()
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    moved = 2 * n * 4
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms_per_copy": ms,
+                      "read_plus_write_GBps": moved / (ms * 1e-3) / 1e9}), flush=True)
 
 
 class Hip:
@@ -141,6 +168,9 @@ def cpu_baseline(wl, inp, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_mb, max(10, min(args.steps, 200)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
               "multi-GPU mode", file=sys.stderr)
