@@ -189,7 +189,7 @@ tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q
                 max_len, max_ctx);
   if (!q_fp16 || !k_codes || !k_norms || !v_codes || !v_norms || !lengths || !out)
     return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: NULL pointer");
-  if (((uintptr_t)k_codes & 3) || ((uintptr_t)v_codes & 3) || ((uintptr_t)k_norms & 3) ||
+  if (((uintptr_t)k_codes & 15) || ((uintptr_t)v_codes & 15) || ((uintptr_t)k_norms & 3) ||
       ((uintptr_t)v_norms & 3) || ((uintptr_t)out & 3) || ((uintptr_t)lengths & 3) ||
       ((uintptr_t)q_fp16 & 1))
     return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: misaligned pointer");

@@ -11,28 +11,40 @@
 // accumulated in the rotated basis as nV_t cV[idxV_t] and one inverse
 // transform per head, out = (1/d) sigma_V (.) H a, finishes it.
 //
-// Three kernels (all on the caller's stream):
-//  1. rotate_q: q^ = (scale * log2 e / d) H (sigma_K (.) q) in fp64, stored fp32.
-//     Folding log2 e lets the softmax use exp2 directly.
-//  2. attend_split (the hot one): grid (splits, kv heads, batch), 4 wavefronts
-//     per workgroup, each wavefront streams 64-token tiles of the workgroup's
-//     context range with its own online-softmax state:
-//       K phase, one lane per token: the lane reads its token's packed K row,
-//       looks each code up in an LDS copy of the K codebook and accumulates G
-//       scores; q^ is wavefront-uniform and comes through scalar loads, so the
-//       inner step is one table lookup and G FMAs per coordinate.
-//       softmax: wavefront max per head (cross-lane butterfly), rescale, p.
-//       V phase, lanes over coordinates: per token, the G weights p * nV_t are
-//       broadcast from LDS and each lane decodes its E = d/64 codes of that
-//       token's V row (staged in LDS), accumulating G x E fp32 outputs.
-//     The four wavefronts merge (m, l, acc) through LDS and write one partial
-//     per (batch, query head, split).
-//  3. combine: log-sum-exp merge of the split partials, normalisation, inverse
-//     Walsh-Hadamard transform (cross-lane butterfly), sign flip, 1/d.
+// Two kernels on the caller's stream:
+//
+// 1. attend_split (the hot one). Grid (splits, kv heads, batch); each
+//    workgroup owns one context range of one (sequence, KV head) and all G
+//    query heads that read it; its wavefronts stream 64-token tiles.
+//    Per tile, both contractions run on the fp32 matrix cores with the
+//    v_mfma_f32_4x4x1 16-block instruction, while the VALU and LDS only
+//    unpack codes and look centroids up:
+//      scores  S[h][t] = sum_j q^[h][j] * cK[idxK[t][j]]
+//              lane t holds token t's packed K row; for each coordinate j the
+//              centroid it looks up is the B operand, and the A operand is
+//              q^[h][j] broadcast from one 4-lane block (CBSZ/ABID), so one
+//              VGPR carries q^ for 16 coordinates and lane t ends with the 4
+//              heads' scores of token t.
+//      softmax online softmax in base 2 (log2 e folded into q^), per head
+//              running max from a cross-lane reduction; weights p * nV_t.
+//      values  A[h][j] += sum_t w[h][t] * cV[idxV[t][j]]
+//              lanes own coordinates; per token the lane decodes its codes
+//              from the tile's V rows (staged in LDS) and the weights of the
+//              4 heads are broadcast the same way as q^.
+//    Centroid tables live in LDS replicated once per bank (16 copies of
+//    8-byte code-pair entries, or 32 copies of 4-byte entries), so a lookup
+//    is conflict-free whatever the codes; codes of <= 3 bits are looked up
+//    two coordinates at a time. The query rotation q^ = (scale log2 e / d)
+//    H (sigma_K (.) q) is done by every wavefront in its prologue.
+//    The wavefronts merge (max, sum, accumulator) through LDS and write one
+//    partial per (sequence, query head, split).
+// 2. combine: log-sum-exp merge of the split partials, normalisation, inverse
+//    Walsh-Hadamard transform (cross-lane butterfly), sign flip, 1/d.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <utility>
 
 #include "kernels.hpp"
 
@@ -40,377 +52,601 @@ namespace tq {
 
 namespace {
 
-constexpr int kTile = 64;            // tokens per wavefront tile
-constexpr int kWaves = 4;            // wavefronts per workgroup
+constexpr int kTile = 64;  // tokens per wavefront tile (one per lane)
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline float wave_max(float v) {
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+template <int... Is, class F>
+__device__ __forceinline__ void sfor_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+template <int N, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  sfor_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// D[v] += A[4*ABID + v] * B[lane] on a 4x4x1 block grid, the A operand of
+// block ABID broadcast to all 16 blocks: lane l accumulates column l % 4 of
+// its block, i.e. lane l gets A_bcast[v] * B[l] for v = 0..3.
+template <int ABID>
+__device__ __forceinline__ v4f mfma_bcast(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
 }
-__device__ inline float wave_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
   return v;
 }
 
-// Make this wavefront's LDS writes visible to its other lanes before reading.
-__device__ inline void wave_lds_sync() {
+// Order this wavefront's LDS writes before its following LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ---------------------------------------------------------------- 1. rotate q
-
-template <int D>
-__global__ __launch_bounds__(64) void rotate_q_kernel(const __half* __restrict__ q,
-                                                      float* __restrict__ qhat, float qscale,
-                                                      SignArg sign) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x;
-  const long long row = (long long)blockIdx.y * gridDim.x + blockIdx.x;  // b * Hq + h
-  const __half* qv = q + row * D + E * lane;
-  double u[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = E * lane + e;
-    const double x = (double)__half2float(qv[e]);
-    u[e] = ((sign.bits[j >> 5] >> (j & 31)) & 1u) ? -x : x;
+// Bits [o - 7, o + 25) of the register row w (o a compile-time bit offset),
+// so that the field starting at bit o lands at bit 7.
+template <int O, int NW>
+__device__ __forceinline__ uint32_t field_at7(const uint32_t (&w)[NW]) {
+  constexpr int wi = O >> 5, sh = O & 31;
+  if constexpr (sh >= 7) {
+    if constexpr (wi + 1 < NW && sh > 7)
+      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh - 7);
+    else
+      return w[wi] >> (sh - 7);
+  } else {
+    return w[wi] << (7 - sh);
   }
-#pragma unroll
-  for (int hs = 1; hs < E; hs <<= 1)
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((e & hs) == 0) {
-        const double a = u[e], b = u[e + hs];
-        u[e] = a + b;
-        u[e + hs] = a - b;
-      }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const double p = __shfl_xor(u[e], m);
-      u[e] = upper ? (p - u[e]) : (u[e] + p);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) qhat[row * D + E * lane + e] = (float)(u[e] * (double)qscale);
 }
 
-// ---------------------------------------------------------------- 2. split attend
+template <int D_, int BK_, int BV_, int NHG_, int WAVES_>
+struct Cfg {
+  static constexpr int D = D_, BK = BK_, BV = BV_, NHG = NHG_, WAVES = WAVES_;
+  static constexpr int E = D / 64;                     // coordinates per lane (rotation)
+  static constexpr bool KPAIR = BK <= 3;               // K looked up two coordinates at a time
+  static constexpr bool VPAIR = BV <= 3 && D >= 128;   // V likewise (pair tables <= 8 KB)
+  static constexpr int KF = KPAIR ? 2 * BK : BK;       // bits per K lookup
+  static constexpr int VF = VPAIR ? 2 * BV : BV;       // bits per V lookup
+  static constexpr int NKL = KPAIR ? D / 2 : D;        // K lookups per token
+  static constexpr int NVS = VPAIR ? D / 128 : D / 64; // V lookups per lane per token
+  static constexpr int RKW = D * BK / 32;              // dwords per K row
+  static constexpr int RVW = D * BV / 32;              // dwords per V row
+  static constexpr int VSTR = ((RVW + 2) & 1) ? RVW + 2 : RVW + 3;  // odd stride: lead pad, row, tail pad
+  static constexpr int KT_BYTES = (1 << KF) * 128;     // 16 x 8 B or 32 x 4 B per entry
+  static constexpr int VT_BYTES = (1 << VF) * 128;
+  static constexpr int STAGE_DW = kTile * VSTR;
+  static constexpr int STAGE_DW_Q = STAGE_DW > D ? STAGE_DW : D;   // also holds one rotated query
+  static constexpr int WBUF_F = kTile * 4 * NHG;
+  static constexpr int WAVE_BYTES = (STAGE_DW_Q + WBUF_F) * 4;
+  static constexpr int MAIN_BYTES = KT_BYTES + VT_BYTES + WAVES * WAVE_BYTES;
+  static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * D) * 4;
+  static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+  static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
+  static_assert(LDS_BYTES <= 65536, "LDS budget");
+};
 
-// Code j (0..31) of a 32-code group held in BITS consecutive dwords w[].
-template <int BITS>
-__device__ inline uint32_t code_at(const uint32_t* w, int j) {
-  const int bit = BITS * j;
-  const int lo = bit >> 5, sh = bit & 31;
-  if (sh + BITS <= 32) return (w[lo] >> sh) & ((1u << BITS) - 1u);
-  return __builtin_amdgcn_alignbit(w[lo + 1], w[lo], sh) & ((1u << BITS) - 1u);
-}
-
-template <int D, int BK, int BV, int G>
-__global__ __launch_bounds__(256, 2) void attend_split_kernel(
-    const float* __restrict__ qhat, const uint8_t* __restrict__ k_codes,
+template <class C>
+__global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
+    const __half* __restrict__ q, const uint8_t* __restrict__ k_codes,
     const float* __restrict__ k_norms, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ v_norms, const int32_t* __restrict__ lengths, int n_kv_heads,
-    int max_ctx, int max_len, int tokens_per_split, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, AttendTables tabs) {
-  constexpr int E = D / 64;                 // V coordinates per lane
-  constexpr int RKW = D * BK / 32;          // dwords per K row
-  constexpr int RVW = D * BV / 32;          // dwords per V row
-  constexpr int VSTR = RVW + 1;             // LDS stride of a staged V row
-  constexpr int NK = 1 << BK, NV = 1 << BV;
-  constexpr int VCH = E * BV;               // V bits per lane per token
-
-  __shared__ float s_ck[NK];
-  __shared__ float s_cv[NV];
-  __shared__ uint32_t s_vrow[kWaves][kTile * VSTR];
-  __shared__ float s_w[kWaves][kTile * G];
-  __shared__ float s_merge[kWaves * D];
-  __shared__ float s_ml[kWaves][2 * G];
+    int group, int max_ctx, int max_len, int tokens_per_split, float qscale,
+    float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign) {
+  constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
+  constexpr int RKW = C::RKW, RVW = C::RVW, VSTR = C::VSTR;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int len = min(lengths[b], max_len);   // never read past the host bound
+  const int len = min(lengths[b], max_len);  // never read past the host bound
   const int t_begin = split * tokens_per_split;
-  if (t_begin >= len) return;  // whole workgroup: this split is past the sequence end
+  if (t_begin >= len) return;  // whole workgroup: range past the sequence end
   const int t_end = min(len, t_begin + tokens_per_split);
-
-  for (int i = threadIdx.x; i < NK; i += blockDim.x) s_ck[i] = tabs.k_centroids[i];
-  for (int i = threadIdx.x; i < NV; i += blockDim.x) s_cv[i] = tabs.v_centroids[i];
-  __syncthreads();
-
+  const int G = group;
   const int n_q_heads = n_kv_heads * G;
-  const float* __restrict__ qh = qhat + ((long long)b * n_q_heads + (long long)g * G) * D;
+
+  unsigned char* kt = lds;
+  unsigned char* vt = lds + C::KT_BYTES;
+  uint32_t* stage = (uint32_t*)(lds + C::KT_BYTES + C::VT_BYTES + wave * C::WAVE_BYTES);
+  float* wbuf = (float*)(stage + C::STAGE_DW_Q);
+
   const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_ctx;
   const uint32_t* __restrict__ kbase = (const uint32_t*)k_codes + kvrow0 * RKW;
   const uint32_t* __restrict__ vbase = (const uint32_t*)v_codes + kvrow0 * RVW;
+  const float* __restrict__ knb = k_norms + kvrow0;
+  const float* __restrict__ vnb = v_norms + kvrow0;
 
-  float m_run[G], l_lane[G], acc[G][E];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_lane[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
-  }
-
-  // this lane's V bits within a row: [VCH*lane, VCH*lane + VCH)
-  const int vbit0 = VCH * lane;
-  const int vdw = vbit0 >> 5, vsh = vbit0 & 31;
-  uint32_t* my_vrow = s_vrow[wave];
-  float* my_w = s_w[wave];
-
-  for (int tile = t_begin + wave * kTile; tile < t_end; tile += kWaves * kTile) {
+  // ---- tile registers: this lane's token rows and norms
+  auto load_tile = [&](int tile, uint32_t (&kw)[RKW], uint32_t (&vw)[RVW], float& nk, float& nv) {
     const int t = tile + lane;
-    const bool valid = t < t_end;
-    const int ntok = min(kTile, t_end - tile);
-
-    // ---- K phase: one lane per token
-    float sc[G];
+    if (t < t_end) {
+      const uint32_t* kr = kbase + (long long)t * RKW;
+      const uint32_t* vr = vbase + (long long)t * RVW;
+      if constexpr (RKW % 4 == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.f;
-    float nv = 0.f;
-    if (valid) {
-      const uint32_t* krow = kbase + (long long)t * RKW;
+        for (int i = 0; i < RKW; i += 4) {
+          const uint4 x = *(const uint4*)(kr + i);
+          kw[i] = x.x; kw[i + 1] = x.y; kw[i + 2] = x.z; kw[i + 3] = x.w;
+        }
+      } else {
 #pragma unroll
-      for (int grp = 0; grp < D / 32; ++grp) {
-        uint32_t w[BK];
-#pragma unroll
-        for (int i = 0; i < BK; ++i) w[i] = krow[grp * BK + i];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const float c = s_ck[code_at<BK>(w, j)];
-#pragma unroll
-          for (int h = 0; h < G; ++h) sc[h] = fmaf(qh[h * D + grp * 32 + j], c, sc[h]);
+        for (int i = 0; i < RKW; i += 2) {
+          const uint2 x = *(const uint2*)(kr + i);
+          kw[i] = x.x; kw[i + 1] = x.y;
         }
       }
-      const float nk = k_norms[kvrow0 + t];
+      if constexpr (RVW % 4 == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] *= nk;
-      nv = v_norms[kvrow0 + t];
-      const uint32_t* vrow = vbase + (long long)t * RVW;
+        for (int i = 0; i < RVW; i += 4) {
+          const uint4 x = *(const uint4*)(vr + i);
+          vw[i] = x.x; vw[i + 1] = x.y; vw[i + 2] = x.z; vw[i + 3] = x.w;
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < RVW; ++i) my_vrow[lane * VSTR + i] = vrow[i];
+        for (int i = 0; i < RVW; i += 2) {
+          const uint2 x = *(const uint2*)(vr + i);
+          vw[i] = x.x; vw[i + 1] = x.y;
+        }
+      }
+      nk = knb[t];
+      nv = vnb[t];
     } else {
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = -INFINITY;
+      for (int i = 0; i < RKW; ++i) kw[i] = 0u;
+#pragma unroll
+      for (int i = 0; i < RVW; ++i) vw[i] = 0u;
+      nk = 0.f;
+      nv = 0.f;
     }
+  };
 
-    // ---- online softmax (base 2)
-    float alpha[G];
+  uint32_t kw[RKW], vw[RVW];
+  float nk, nv;
+  int tile = t_begin + wave * kTile;
+  if (tile < t_end) load_tile(tile, kw, vw, nk, nv);
+
+  // ---- centroid tables, one copy per LDS bank
+  {
+    const int nthr = 64 * WAVES;
+    if constexpr (C::KPAIR) {
+      constexpr int M = (1 << C::BK) - 1;
+      for (int i = threadIdx.x; i < (1 << C::KF) * 16; i += nthr) {
+        const int pr = i >> 4;
+        ((v2f*)kt)[i] = v2f{tabs.k_centroids[pr & M], tabs.k_centroids[pr >> C::BK]};
+      }
+    } else {
+      for (int i = threadIdx.x; i < (1 << C::KF) * 32; i += nthr)
+        ((float*)kt)[i] = tabs.k_centroids[i >> 5];
+    }
+    if constexpr (C::VPAIR) {
+      constexpr int M = (1 << C::BV) - 1;
+      for (int i = threadIdx.x; i < (1 << C::VF) * 16; i += nthr) {
+        const int pr = i >> 4;
+        ((v2f*)vt)[i] = v2f{tabs.v_centroids[pr & M], tabs.v_centroids[pr >> C::BV]};
+      }
+    } else {
+      for (int i = threadIdx.x; i < (1 << C::VF) * 32; i += nthr)
+        ((float*)vt)[i] = tabs.v_centroids[i >> 5];
+    }
+  }
+
+  // ---- rotated queries in the broadcast layout: lane 4c + v of VGPR Q[hg][m]
+  //      holds q^[4 hg + v][16 m + c]
+  float Q[NHG][D / 16];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mt = wave_max(sc[h]);
-      const float mn = fmaxf(m_run[h], mt);
-      alpha[h] = exp2f(m_run[h] - mn);      // m_run = -inf -> 0
-      const float p = valid ? exp2f(sc[h] - mn) : 0.f;
-      l_lane[h] = l_lane[h] * alpha[h] + p;
-      m_run[h] = mn;
-      my_w[lane * G + h] = p * nv;
+  for (int hg = 0; hg < NHG; ++hg)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] *= alpha[h];
+    for (int m = 0; m < D / 16; ++m) Q[hg][m] = 0.f;
+  {
+    float* qbuf = (float*)stage;
+    const __half* qb = q + ((long long)b * n_q_heads + (long long)g * G) * D;
+    sfor<4 * NHG>([&](auto HH) {
+      constexpr int h = HH;
+      if (h < G) {
+        float u[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = E * lane + e;
+          const float x = __half2float(qb[h * D + j]);
+          u[e] = ((ksign.bits[j >> 5] >> (j & 31)) & 1u) ? -x : x;
+        }
+#pragma unroll
+        for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if ((e & hs) == 0) {
+              const float a0 = u[e], a1 = u[e + hs];
+              u[e] = a0 + a1;
+              u[e + hs] = a0 - a1;
+            }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const bool upper = (lane & m) != 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float p = __shfl_xor(u[e], m);
+            u[e] = upper ? (p - u[e]) : (u[e] + p);
+          }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < E; ++e) qbuf[E * lane + e] = u[e] * qscale;
+        wave_lds_sync();
+        const bool mine = (lane & 3) == (h & 3);
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) {
+          const float x = qbuf[16 * m + (lane >> 2)];
+          Q[h / 4][m] = mine ? x : Q[h / 4][m];
+        }
+      }
+    });
+  }
+  __syncthreads();  // tables ready
+
+  // ---- per-wave online-softmax state
+  float m_run[NHG][4];
+  v4f l_run[NHG];
+  v4f acc[C::NACC][NHG];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    l_run[hg] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) m_run[hg][v] = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < C::NACC; ++a) acc[a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // V lookup positions of this lane: field index f_k = 64k + lane, bit o_k =
+  // VF * f_k of the row; the staged row starts one dword into its slot.
+  int vdw[C::NVS], vsh[C::NVS];
+#pragma unroll
+  for (int k = 0; k < C::NVS; ++k) {
+    const int o = C::VF * (64 * k + lane) + 32 - 7;
+    vdw[k] = o >> 5;
+    vsh[k] = o & 31;
+  }
+  const uint32_t koff = C::KPAIR ? (uint32_t)(lane & 15) << 3 : (uint32_t)(lane & 31) << 2;
+  const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 15) << 3 : (uint32_t)(lane & 31) << 2;
+  constexpr uint32_t KMASK = ((1u << C::KF) - 1u) << 7;
+  constexpr uint32_t VMASK = ((1u << C::VF) - 1u) << 7;
+
+  for (; tile < t_end; tile += WAVES * kTile) {
+    const int next = tile + WAVES * kTile;
+    const bool valid = tile + lane < t_end;
+
+    // stage this tile's V rows for the lanes-over-coordinates phase
+#pragma unroll
+    for (int i = 0; i < RVW; ++i) stage[lane * VSTR + 1 + i] = vw[i];
+
+    // ---- scores on the matrix cores
+    v4f s0[NHG], s1[NHG];
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+      s0[hg] = v4f{0.f, 0.f, 0.f, 0.f};
+      s1[hg] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    sfor<C::NKL>([&](auto FI) {
+      constexpr int f = FI;
+      const uint32_t x = field_at7<C::KF * f>(kw);
+      const uint32_t addr = (x & KMASK) | koff;
+      if constexpr (C::KPAIR) {
+        const v2f c = *(const v2f*)(kt + addr);
+        constexpr int j0 = 2 * f, j1 = 2 * f + 1;
+#pragma unroll
+        for (int hg = 0; hg < NHG; ++hg) {
+          s0[hg] = mfma_bcast<j0 % 16>(Q[hg][j0 / 16], c.x, s0[hg]);
+          s1[hg] = mfma_bcast<j1 % 16>(Q[hg][j1 / 16], c.y, s1[hg]);
+        }
+      } else {
+        const float c = *(const float*)(kt + addr);
+#pragma unroll
+        for (int hg = 0; hg < NHG; ++hg) {
+          if constexpr (f % 2 == 0)
+            s0[hg] = mfma_bcast<f % 16>(Q[hg][f / 16], c, s0[hg]);
+          else
+            s1[hg] = mfma_bcast<f % 16>(Q[hg][f / 16], c, s1[hg]);
+        }
+      }
+    });
+
+    const float nv_cur = nv;
+    const float nk_cur = nk;
+    // prefetch the next tile while this one is finished
+    if (next < t_end) load_tile(next, kw, vw, nk, nv);
+
+    // ---- online softmax (base 2) and value weights
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+      v4f s = (s0[hg] + s1[hg]) * nk_cur;
+      v4f w;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sv = valid ? s[v] : -INFINITY;
+        const float mn = fmaxf(m_run[hg][v], wave_max(sv));
+        const float alpha = exp2f(m_run[hg][v] - mn);
+        const float p = exp2f(sv - mn);
+        l_run[hg][v] = l_run[hg][v] * alpha + p;
+        m_run[hg][v] = mn;
+        w[v] = p * nv_cur;
+#pragma unroll
+        for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
+      }
+      *(v4f*)(wbuf + (lane * NHG + hg) * 4) = w;
     }
     wave_lds_sync();
 
-    // ---- V phase: lanes over coordinates
-    for (int tt = 0; tt < ntok; ++tt) {
-      const uint32_t* vr = my_vrow + tt * VSTR;
-      uint32_t bits;
-      if (vsh + VCH <= 32) {
-        bits = vr[vdw] >> vsh;
-      } else {
-        bits = __builtin_amdgcn_alignbit(vr[vdw + 1], vr[vdw], vsh);
+    // weights in the broadcast layout: lane 4c + v of Wr[hg][m] holds w[4 hg + v][16 m + c]
+    float Wr[NHG][4];
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        Wr[hg][m] = wbuf[((16 * m + (lane >> 2)) * NHG + hg) * 4 + (lane & 3)];
+
+    // ---- values on the matrix cores, lanes over coordinates
+    sfor<kTile>([&](auto TI) {
+      constexpr int t = TI;
+      const uint32_t* row = stage + t * VSTR;
+#pragma unroll
+      for (int k = 0; k < C::NVS; ++k) {
+        const uint32_t x = __builtin_amdgcn_alignbit(row[vdw[k] + 1], row[vdw[k]], vsh[k]);
+        const uint32_t addr = (x & VMASK) | voff;
+        if constexpr (C::VPAIR) {
+          const v2f c = *(const v2f*)(vt + addr);
+#pragma unroll
+          for (int hg = 0; hg < NHG; ++hg) {
+            acc[2 * k][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], c.x, acc[2 * k][hg]);
+            acc[2 * k + 1][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], c.y, acc[2 * k + 1][hg]);
+          }
+        } else {
+          const float c = *(const float*)(vt + addr);
+          constexpr int par = (C::NVS == 1) ? (t & 1) : 0;
+#pragma unroll
+          for (int hg = 0; hg < NHG; ++hg)
+            acc[k + par][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], c, acc[k + par][hg]);
+        }
       }
-      float wt[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) wt[h] = my_w[tt * G + h];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float c = s_cv[(bits >> (BV * e)) & (NV - 1)];
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wt[h], c, acc[h][e]);
-      }
-    }
+    });
     wave_lds_sync();
   }
 
-  // ---- merge the four wavefronts and write this split's partials
-  float l_w[G];
+  // ---- merge the wavefronts of this workgroup and write the split partial
+  float lsum[NHG][4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_lane[h]);
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) lsum[hg][v] = wave_sum(l_run[hg][v]);
+  if constexpr (C::NVS == 1 && !C::VPAIR) {
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) acc[0][hg] += acc[1][hg];
+  }
+  __syncthreads();  // all wavefronts are done with tables and staging
+  float* mbuf = (float*)lds;                    // [WAVES][4 NHG][2]
+  float* abuf = mbuf + WAVES * 4 * NHG * 2;     // [WAVES][4][D]
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_ml[wave][2 * h] = m_run[h];
-      s_ml[wave][2 * h + 1] = l_w[h];
-    }
+    for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        mbuf[(wave * 4 * NHG + 4 * hg + v) * 2] = m_run[hg][v];
+        mbuf[(wave * 4 * NHG + 4 * hg + v) * 2 + 1] = lsum[hg][v];
+      }
   }
   const int S = gridDim.x;
-  for (int h = 0; h < G; ++h) {
+  sfor<NHG>([&](auto HGI) {
+    constexpr int hg = HGI;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < E; ++e) s_merge[wave * D + E * lane + e] = acc[h][e];
+    for (int v = 0; v < 4; ++v) {
+      float* dst = abuf + (wave * 4 + v) * D;
+      if constexpr (C::VPAIR) {
+#pragma unroll
+        for (int k = 0; k < C::NVS; ++k) {
+          dst[2 * (64 * k + lane)] = acc[2 * k][hg][v];
+          dst[2 * (64 * k + lane) + 1] = acc[2 * k + 1][hg][v];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = acc[k][hg][v];
+      }
+    }
     __syncthreads();
-    float M = -INFINITY;
+    for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WAVES) {
+      const int v = idx / D, j = idx - v * D;
+      const int h = 4 * hg + v;
+      if (h >= G) continue;
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][2 * h]);
-    const long long prow = ((long long)b * n_q_heads + (long long)g * G + h) * S + split;
-    for (int j = threadIdx.x; j < D; j += blockDim.x) {
-      float a = 0.f;
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[(w * 4 * NHG + h) * 2]);
+      float a = 0.f, L = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_ml[w][2 * h];
+      for (int w = 0; w < WAVES; ++w) {
+        const float mw = mbuf[(w * 4 * NHG + h) * 2];
         const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        a = fmaf(f, s_merge[w * D + j], a);
+        a = fmaf(f, abuf[(w * 4 + v) * D + j], a);
+        L = fmaf(f, mbuf[(w * 4 * NHG + h) * 2 + 1], L);
       }
+      const long long prow = ((long long)b * n_q_heads + (long long)g * G + h) * S + split;
       part_acc[prow * D + j] = a;
-    }
-    if (threadIdx.x == 0) {
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_ml[w][2 * h];
-        if (mw != -INFINITY) L = fmaf(exp2f(mw - M), s_ml[w][2 * h + 1], L);
+      if (j == 0) {
+        part_ml[prow * 2] = M;
+        part_ml[prow * 2 + 1] = L;
       }
-      part_ml[prow * 2] = M;
-      part_ml[prow * 2 + 1] = L;
     }
-  }
+  });
 }
 
-// ---------------------------------------------------------------- 3. combine
+// ---------------------------------------------------------------- 2. combine
+
+constexpr int kCombineThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_acc,
-                                                     const float* __restrict__ part_ml,
-                                                     const int32_t* __restrict__ lengths,
-                                                     int max_len, int n_q_heads, int splits,
-                                                     int tokens_per_split, float* __restrict__ out,
-                                                     SignArg sign) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float* __restrict__ part_acc, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ lengths, int max_len, int n_q_heads, int splits,
+    int tokens_per_split, float* __restrict__ out, SignArg sign) {
   constexpr int E = D / 64;
-  const int lane = threadIdx.x;
+  constexpr int NG = kCombineThreads / D;  // split groups
+  __shared__ float s_red[kCombineThreads];
+  __shared__ float s_acc[NG][D];
+  __shared__ float s_l[NG];
+  const int tid = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
   const long long row = (long long)b * n_q_heads + h;
   const int len = min(lengths[b], max_len);
-  float a[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) a[e] = 0.f;
-  if (len > 0) {
-    const int ns = min(splits, (len + tokens_per_split - 1) / tokens_per_split);
-    const float* ml = part_ml + row * splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float f = exp2f(ml[2 * s] - M);
-      L = fmaf(f, ml[2 * s + 1], L);
-      const float* pa = part_acc + (row * splits + s) * D + E * lane;
-#pragma unroll
-      for (int e = 0; e < E; ++e) a[e] = fmaf(f, pa[e], a[e]);
-    }
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int e = 0; e < E; ++e) a[e] *= inv;
+  const int ns = len > 0 ? min(splits, (len + tokens_per_split - 1) / tokens_per_split) : 0;
+  const float* ml = part_ml + row * splits * 2;
+
+  // global max over the valid splits
+  float M = -INFINITY;
+  for (int s = tid; s < ns; s += kCombineThreads) M = fmaxf(M, ml[2 * s]);
+  s_red[tid] = M;
+  __syncthreads();
+  for (int w = kCombineThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+    __syncthreads();
   }
-  // inverse rotation: out = (1/d) sigma_V (.) H a
+  M = s_red[0];
+
+  // rescaled sums: thread (group grp, coordinate j) over splits s = grp mod NG
+  const int j = tid % D, grp = tid / D;
+  float a = 0.f, L = 0.f;
+  for (int s = grp; s < ns; s += NG) {
+    const float f = exp2f(ml[2 * s] - M);
+    a = fmaf(f, part_acc[(row * splits + s) * D + j], a);
+    L = fmaf(f, ml[2 * s + 1], L);
+  }
+  s_acc[grp][j] = a;
+  if (j == 0) s_l[grp] = L;
+  __syncthreads();
+
+  if (tid < 64) {
+    const int lane = tid;
+    float u[E];
+    float Lt = 0.f;
 #pragma unroll
-  for (int hs = 1; hs < E; hs <<= 1)
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((e & hs) == 0) {
-        const float x = a[e], y = a[e + hs];
-        a[e] = x + y;
-        a[e + hs] = x - y;
-      }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+    for (int g2 = 0; g2 < NG; ++g2) Lt += s_l[g2];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float p = __shfl_xor(a[e], m);
-      a[e] = upper ? (p - a[e]) : (a[e] + p);
-    }
-  }
-  const float invd = 1.f / (float)D;
+      float x = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = E * lane + e;
-    const float v = a[e] * invd;
-    out[row * D + j] = ((sign.bits[j >> 5] >> (j & 31)) & 1u) ? -v : v;
+      for (int g2 = 0; g2 < NG; ++g2) x += s_acc[g2][E * lane + e];
+      u[e] = ns > 0 ? x / Lt : 0.f;
+    }
+    // inverse rotation: out = (1/d) sigma_V (.) H a
+#pragma unroll
+    for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((e & hs) == 0) {
+          const float x0 = u[e], x1 = u[e + hs];
+          u[e] = x0 + x1;
+          u[e + hs] = x0 - x1;
+        }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float p = __shfl_xor(u[e], m);
+        u[e] = upper ? (p - u[e]) : (u[e] + p);
+      }
+    }
+    const float invd = 1.f / (float)D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int jj = E * lane + e;
+      const float v = u[e] * invd;
+      out[row * D + jj] = ((sign.bits[jj >> 5] >> (jj & 31)) & 1u) ? -v : v;
+    }
   }
 }
 
 // ---------------------------------------------------------------- dispatch
 
-template <int D, int BK, int BV, int G>
-hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, const float* qhat,
-                        const uint8_t* kc, const float* kn, const uint8_t* vc, const float* vn,
-                        const int32_t* lengths, int max_ctx, int max_len, float* pacc,
-                        float* pml, const AttendTables& tabs, hipStream_t stream) {
-  hipLaunchKernelGGL((attend_split_kernel<D, BK, BV, G>),
-                     dim3(plan.splits, n_kv_heads, batch), dim3(64 * kWaves), 0, stream, qhat,
-                     kc, kn, vc, vn, lengths, n_kv_heads, max_ctx, max_len,
-                     plan.tokens_per_split, pacc, pml, tabs);
+template <class C>
+hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, int group,
+                        const void* q, const uint8_t* kc, const float* kn, const uint8_t* vc,
+                        const float* vn, const int32_t* lengths, int max_ctx, int max_len,
+                        float qscale, float* pacc, float* pml, const AttendTables& tabs,
+                        const SignArg& ksign, hipStream_t stream) {
+  hipLaunchKernelGGL((attend_split_kernel<C>), dim3(plan.splits, n_kv_heads, batch),
+                     dim3(64 * C::WAVES), 0, stream, (const __half*)q, kc, kn, vc, vn, lengths,
+                     n_kv_heads, group, max_ctx, max_len, plan.tokens_per_split, qscale, pacc,
+                     pml, tabs, ksign);
   return hipGetLastError();
 }
 
-typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, const float*, const uint8_t*,
+typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, int, const void*, const uint8_t*,
                               const float*, const uint8_t*, const float*, const int32_t*, int,
-                              int, float*, float*, const AttendTables&, hipStream_t);
+                              int, float, float*, float*, const AttendTables&, const SignArg&,
+                              hipStream_t);
 
 struct SplitEntry {
-  int d, bk, bv, g;
+  int d, bk, bv, nhg;
   SplitFn fn;
 };
 
-#define TQ_SPLIT(D, BK, BV, G) {D, BK, BV, G, &launch_split<D, BK, BV, G>}
+// Instantiated (head_dim, K bits, V bits, groups of 4 query heads, wavefronts
+// per workgroup). A group size G is served by the entry with the smallest
+// nhg such that G <= 4 * nhg.
+#define TQ_SPLIT(D, BK, BV, NHG, W) {D, BK, BV, NHG, &launch_split<Cfg<D, BK, BV, NHG, W>>}
 const SplitEntry kSplitTable[] = {
     // head_dim 64
-    TQ_SPLIT(64, 4, 4, 2), TQ_SPLIT(64, 3, 3, 8), TQ_SPLIT(64, 4, 4, 1), TQ_SPLIT(64, 3, 3, 4),
-    TQ_SPLIT(64, 8, 3, 4), TQ_SPLIT(64, 2, 2, 2), TQ_SPLIT(64, 1, 1, 2), TQ_SPLIT(64, 5, 7, 2),
-    TQ_SPLIT(64, 6, 6, 16), TQ_SPLIT(64, 8, 8, 1),
+    TQ_SPLIT(64, 4, 4, 1, 4), TQ_SPLIT(64, 3, 3, 2, 4), TQ_SPLIT(64, 3, 3, 1, 4),
+    TQ_SPLIT(64, 8, 3, 1, 4), TQ_SPLIT(64, 2, 2, 1, 4), TQ_SPLIT(64, 1, 1, 1, 4),
+    TQ_SPLIT(64, 5, 7, 1, 4), TQ_SPLIT(64, 6, 6, 4, 4), TQ_SPLIT(64, 4, 4, 2, 4),
+    TQ_SPLIT(64, 8, 3, 2, 4),
     // head_dim 128
-    TQ_SPLIT(128, 4, 2, 3), TQ_SPLIT(128, 8, 3, 4), TQ_SPLIT(128, 3, 3, 4), TQ_SPLIT(128, 4, 4, 4),
-    TQ_SPLIT(128, 4, 3, 4), TQ_SPLIT(128, 2, 2, 4), TQ_SPLIT(128, 8, 4, 4), TQ_SPLIT(128, 4, 4, 8),
-    TQ_SPLIT(128, 8, 3, 8), TQ_SPLIT(128, 4, 2, 1), TQ_SPLIT(128, 3, 3, 2), TQ_SPLIT(128, 8, 8, 2),
-    TQ_SPLIT(128, 1, 1, 4), TQ_SPLIT(128, 7, 5, 6),
+    TQ_SPLIT(128, 4, 2, 1, 4), TQ_SPLIT(128, 8, 3, 1, 4), TQ_SPLIT(128, 3, 3, 1, 4),
+    TQ_SPLIT(128, 4, 4, 1, 4), TQ_SPLIT(128, 4, 3, 1, 4), TQ_SPLIT(128, 2, 2, 1, 4),
+    TQ_SPLIT(128, 8, 4, 1, 4), TQ_SPLIT(128, 4, 4, 2, 4), TQ_SPLIT(128, 8, 3, 2, 4),
+    TQ_SPLIT(128, 1, 1, 1, 4), TQ_SPLIT(128, 7, 5, 2, 4),
+    TQ_SPLIT(128, 3, 3, 2, 4), TQ_SPLIT(128, 4, 2, 2, 4),
     // head_dim 256
-    TQ_SPLIT(256, 4, 4, 4), TQ_SPLIT(256, 8, 3, 4), TQ_SPLIT(256, 3, 3, 2), TQ_SPLIT(256, 8, 4, 1),
-    TQ_SPLIT(256, 2, 2, 8),
+    TQ_SPLIT(256, 4, 4, 1, 4), TQ_SPLIT(256, 8, 3, 1, 2), TQ_SPLIT(256, 3, 3, 1, 4),
+    TQ_SPLIT(256, 8, 4, 1, 2), TQ_SPLIT(256, 2, 2, 2, 4),
 };
 #undef TQ_SPLIT
 
-const SplitEntry* find_split(int d, int bk, int bv, int g) {
+const SplitEntry* find_split(int d, int bk, int bv, int group) {
+  const SplitEntry* best = nullptr;
   for (const SplitEntry& e : kSplitTable)
-    if (e.d == d && e.bk == bk && e.bv == bv && e.g == g) return &e;
-  return nullptr;
+    if (e.d == d && e.bk == bk && e.bv == bv && group <= 4 * e.nhg &&
+        (!best || e.nhg < best->nhg))
+      best = &e;
+  return best;
 }
 
 }  // namespace
 
 AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
   AttendPlan p{};
-  // Enough workgroups to give each of the 256 CUs several to interleave, but
-  // at least one full round of tiles (4 wavefronts x 64 tokens) per workgroup.
+  // About 1024 workgroups (four per CU) and at least two tiles per wavefront.
   const long long units = (long long)batch * n_kv_heads;
-  const long long target_wgs = 2048;
+  const long long target_wgs = 1024;
+  const long long quantum = 4 * kTile;
   long long tps = ((long long)max_len * units + target_wgs - 1) / target_wgs;
-  const long long round = (long long)kWaves * kTile;
-  tps = ((tps + round - 1) / round) * round;
-  if (tps < round) tps = round;
+  tps = ((tps + quantum - 1) / quantum) * quantum;
+  if (tps < 2 * quantum) tps = 2 * quantum;
   p.tokens_per_split = (int)tps;
   p.splits = (int)((max_len + tps - 1) / tps);
   if (p.splits < 1) p.splits = 1;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  p.qhat_bytes = align((size_t)batch * n_q_heads * dim * sizeof(float));
+  p.qhat_bytes = 0;
   p.part_acc_bytes = align((size_t)batch * n_q_heads * p.splits * dim * sizeof(float));
   p.part_ml_bytes = align((size_t)batch * n_q_heads * p.splits * 2 * sizeof(float));
-  p.total_bytes = p.qhat_bytes + p.part_acc_bytes + p.part_ml_bytes;
+  p.total_bytes = p.part_acc_bytes + p.part_ml_bytes;
   return p;
 }
 
@@ -430,49 +666,34 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_q_hea
   const SplitEntry* ent = find_split(dim, k_bits, v_bits, group);
   if (!ent) return hipErrorInvalidValue;
   char* ws = (char*)workspace;
-  float* qhat = (float*)ws;
-  float* pacc = (float*)(ws + plan.qhat_bytes);
-  float* pml = (float*)(ws + plan.qhat_bytes + plan.part_acc_bytes);
+  float* pacc = (float*)ws;
+  float* pml = (float*)(ws + plan.part_acc_bytes);
   const float qscale = scale * kLog2e / (float)dim;
   hipError_t err;
+  if (ev_before && (err = hipEventRecord(ev_before, stream)) != hipSuccess) return err;
+  err = ent->fn(plan, batch, n_kv_heads, group, q, k_codes, k_norms, v_codes, v_norms, lengths,
+                max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, stream);
+  if (err != hipSuccess) return err;
+  if (ev_after && (err = hipEventRecord(ev_after, stream)) != hipSuccess) return err;
+  const dim3 cgrid(n_q_heads, batch);
   switch (dim) {
     case 64:
-      hipLaunchKernelGGL(rotate_q_kernel<64>, dim3(n_q_heads, batch), dim3(64), 0, stream,
-                         (const __half*)q, qhat, qscale, k_sign);
+      hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
+                         lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
+                         v_sign);
       break;
     case 128:
-      hipLaunchKernelGGL(rotate_q_kernel<128>, dim3(n_q_heads, batch), dim3(64), 0, stream,
-                         (const __half*)q, qhat, qscale, k_sign);
+      hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
+                         lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
+                         v_sign);
       break;
     case 256:
-      hipLaunchKernelGGL(rotate_q_kernel<256>, dim3(n_q_heads, batch), dim3(64), 0, stream,
-                         (const __half*)q, qhat, qscale, k_sign);
+      hipLaunchKernelGGL(combine_kernel<256>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
+                         lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
+                         v_sign);
       break;
     default:
       return hipErrorInvalidValue;
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev_before && (err = hipEventRecord(ev_before, stream)) != hipSuccess) return err;
-  err = ent->fn(plan, batch, n_kv_heads, qhat, k_codes, k_norms, v_codes, v_norms, lengths,
-                max_ctx, max_len, pacc, pml, tabs, stream);
-  if (err != hipSuccess) return err;
-  if (ev_after && (err = hipEventRecord(ev_after, stream)) != hipSuccess) return err;
-  switch (dim) {
-    case 64:
-      hipLaunchKernelGGL(combine_kernel<64>, dim3(n_q_heads, batch), dim3(64), 0, stream, pacc,
-                         pml, lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
-                         v_sign);
-      break;
-    case 128:
-      hipLaunchKernelGGL(combine_kernel<128>, dim3(n_q_heads, batch), dim3(64), 0, stream, pacc,
-                         pml, lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
-                         v_sign);
-      break;
-    case 256:
-      hipLaunchKernelGGL(combine_kernel<256>, dim3(n_q_heads, batch), dim3(64), 0, stream, pacc,
-                         pml, lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
-                         v_sign);
-      break;
   }
   return hipGetLastError();
 }

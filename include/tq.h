@@ -107,7 +107,8 @@ size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int d
  * dequantisation without expanding the cache).
  *   kc, vc:     codecs of the K and V caches (same dim; bits may differ).
  *   q_fp16:     [batch][n_q_heads][dim] fp16, contiguous.
- *   k_codes:    [batch][n_kv_heads][max_ctx][dim*kc_bits/8] bytes, contiguous.
+ *   k_codes:    [batch][n_kv_heads][max_ctx][dim*kc_bits/8] bytes, contiguous,
+ *               16-byte aligned (v_codes likewise).
  *   k_norms:    [batch][n_kv_heads][max_ctx] fp32.  v_codes / v_norms likewise.
  *   lengths:    device int32[batch]; sequence b attends to rows [0, lengths[b]).
  *               Values are clamped to max_len on the device, so the cache is

@@ -172,10 +172,10 @@ def _attend_case(d, kb, vb, G, lengths, Hkv=2, seed=0, T=None, kscale=1.0, vscal
 
 SUPPORTED_SMALL = [
     (64, 4, 4, 2), (64, 3, 3, 8), (64, 4, 4, 1), (64, 3, 3, 4), (64, 8, 3, 4), (64, 2, 2, 2),
-    (64, 1, 1, 2), (64, 5, 7, 2), (64, 6, 6, 16), (64, 8, 8, 1),
+    (64, 1, 1, 2), (64, 5, 7, 2), (64, 6, 6, 16), (64, 4, 4, 5), (64, 8, 3, 7),
     (128, 4, 2, 3), (128, 8, 3, 4), (128, 3, 3, 4), (128, 4, 4, 4), (128, 4, 3, 4), (128, 2, 2, 4),
-    (128, 8, 4, 4), (128, 4, 4, 8), (128, 8, 3, 8), (128, 4, 2, 1), (128, 3, 3, 2), (128, 8, 8, 2),
-    (128, 1, 1, 4), (128, 7, 5, 6),
+    (128, 8, 4, 4), (128, 4, 4, 8), (128, 8, 3, 8), (128, 4, 2, 1), (128, 3, 3, 2), (128, 8, 3, 6),
+    (128, 1, 1, 4), (128, 7, 5, 6), (128, 3, 3, 5), (128, 4, 2, 8),
     (256, 4, 4, 4), (256, 8, 3, 4), (256, 3, 3, 2), (256, 8, 4, 1), (256, 2, 2, 8),
 ]
 
