@@ -28,9 +28,12 @@
 //      softmax online softmax in base 2 (log2 e folded into q^), per head
 //              running max from a cross-lane reduction; weights p * nV_t.
 //      values  A[h][j] += sum_t w[h][t] * cV[idxV[t][j]]
-//              lanes own coordinates; per token the lane decodes its codes
-//              from the tile's V rows (staged in LDS) and the weights of the
-//              4 heads are broadcast the same way as q^.
+//              lanes own coordinates. During the scores phase the lane that
+//              holds token t unpacks t's V codes into 16-bit table offsets and
+//              writes them to an LDS table, token-major; here lane l reads
+//              its column (one 2-byte load per token, no unpacking) and looks
+//              the centroid up. The 4 heads' weights are broadcast the same
+//              way as q^.
 //    Centroid tables live in LDS replicated once per bank (16 copies of
 //    8-byte code-pair entries, or 32 copies of 4-byte entries), so a lookup
 //    is conflict-free whatever the codes; codes of <= 3 bits are looked up
@@ -76,10 +79,24 @@ __device__ __forceinline__ v4f mfma_bcast(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wavefront, returned in every lane: DPP within each 16-lane
+// row (quad swaps, half-row and row mirrors), then the four row results.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -121,18 +138,24 @@ struct Cfg {
   static constexpr int NVS = VPAIR ? D / 128 : D / 64; // V lookups per lane per token
   static constexpr int RKW = D * BK / 32;              // dwords per K row
   static constexpr int RVW = D * BV / 32;              // dwords per V row
-  static constexpr int VSTR = ((RVW + 2) & 1) ? RVW + 2 : RVW + 3;  // odd stride: lead pad, row, tail pad
+  static constexpr int NVF = VPAIR ? D / 2 : D;        // V lookups per token
+  // V lookup offsets of a tile, 16 bits each, token-major: a row of NVF/2
+  // dwords per token, stride = 2 mod 4 dwords so 8-byte row writes hit
+  // distinct banks
+  static constexpr int VAS = NVF / 2 + 2;
   static constexpr int KT_BYTES = (1 << KF) * 128;     // 16 x 8 B or 32 x 4 B per entry
   static constexpr int VT_BYTES = (1 << VF) * 128;
-  static constexpr int STAGE_DW = kTile * VSTR;
-  static constexpr int STAGE_DW_Q = STAGE_DW > D ? STAGE_DW : D;   // also holds one rotated query
+  static constexpr int VA_DW = kTile * VAS;
+  static constexpr int VA_DW_Q = VA_DW > D ? VA_DW : D;   // also holds one rotated query
   static constexpr int WBUF_F = kTile * 4 * NHG;
-  static constexpr int WAVE_BYTES = (STAGE_DW_Q + WBUF_F) * 4;
+  static constexpr int WAVE_BYTES = (VA_DW_Q + WBUF_F) * 4;
   static constexpr int MAIN_BYTES = KT_BYTES + VT_BYTES + WAVES * WAVE_BYTES;
   static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * D) * 4;
   static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
-  static_assert(LDS_BYTES <= 65536, "LDS budget");
+  static_assert(VAS % 4 == 2, "V offset row stride");
+  static_assert(KT_BYTES <= 32768 && VT_BYTES <= 32768, "16-bit table offsets");
+  static_assert(LDS_BYTES <= 163840, "LDS budget");
 };
 
 template <class C>
@@ -143,7 +166,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     int group, int max_ctx, int max_len, int tokens_per_split, float qscale,
     float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign) {
   constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
-  constexpr int RKW = C::RKW, RVW = C::RVW, VSTR = C::VSTR;
+  constexpr int RKW = C::RKW, RVW = C::RVW, VAS = C::VAS;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -157,8 +180,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   unsigned char* kt = lds;
   unsigned char* vt = lds + C::KT_BYTES;
-  uint32_t* stage = (uint32_t*)(lds + C::KT_BYTES + C::VT_BYTES + wave * C::WAVE_BYTES);
-  float* wbuf = (float*)(stage + C::STAGE_DW_Q);
+  uint32_t* vabuf = (uint32_t*)(lds + C::KT_BYTES + C::VT_BYTES + wave * C::WAVE_BYTES);
+  float* wbuf = (float*)(vabuf + C::VA_DW_Q);
 
   const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_ctx;
   const uint32_t* __restrict__ kbase = (const uint32_t*)k_codes + kvrow0 * RKW;
@@ -248,7 +271,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) Q[hg][m] = 0.f;
   {
-    float* qbuf = (float*)stage;
+    float* qbuf = (float*)vabuf;
     const __half* qb = q + ((long long)b * n_q_heads + (long long)g * G) * D;
     sfor<4 * NHG>([&](auto HH) {
       constexpr int h = HH;
@@ -306,15 +329,6 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int a = 0; a < C::NACC; ++a) acc[a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  // V lookup positions of this lane: field index f_k = 64k + lane, bit o_k =
-  // VF * f_k of the row; the staged row starts one dword into its slot.
-  int vdw[C::NVS], vsh[C::NVS];
-#pragma unroll
-  for (int k = 0; k < C::NVS; ++k) {
-    const int o = C::VF * (64 * k + lane) + 32 - 7;
-    vdw[k] = o >> 5;
-    vsh[k] = o & 31;
-  }
   const uint32_t koff = C::KPAIR ? (uint32_t)(lane & 15) << 3 : (uint32_t)(lane & 31) << 2;
   const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 15) << 3 : (uint32_t)(lane & 31) << 2;
   constexpr uint32_t KMASK = ((1u << C::KF) - 1u) << 7;
@@ -324,9 +338,16 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     const int next = tile + WAVES * kTile;
     const bool valid = tile + lane < t_end;
 
-    // stage this tile's V rows for the lanes-over-coordinates phase
-#pragma unroll
-    for (int i = 0; i < RVW; ++i) stage[lane * VSTR + 1 + i] = vw[i];
+    // this token's V lookup offsets (code << 7), two per dword, into row `lane`
+    // of the tile's offset table: the values phase reads them column-wise
+    sfor<C::NVF / 4>([&](auto PI) {
+      constexpr int f = 4 * PI;
+      const uint32_t a0 = field_at7<C::VF * f>(vw) & VMASK;
+      const uint32_t a1 = field_at7<C::VF * (f + 1)>(vw) & VMASK;
+      const uint32_t a2 = field_at7<C::VF * (f + 2)>(vw) & VMASK;
+      const uint32_t a3 = field_at7<C::VF * (f + 3)>(vw) & VMASK;
+      *(uint2*)(vabuf + lane * VAS + f / 2) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
+    });
 
     // ---- scores on the matrix cores
     v4f s0[NHG], s1[NHG];
@@ -394,13 +415,12 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         Wr[hg][m] = wbuf[((16 * m + (lane >> 2)) * NHG + hg) * 4 + (lane & 3)];
 
     // ---- values on the matrix cores, lanes over coordinates
+    const unsigned short* va16 = (const unsigned short*)vabuf;
     sfor<kTile>([&](auto TI) {
       constexpr int t = TI;
-      const uint32_t* row = stage + t * VSTR;
 #pragma unroll
       for (int k = 0; k < C::NVS; ++k) {
-        const uint32_t x = __builtin_amdgcn_alignbit(row[vdw[k] + 1], row[vdw[k]], vsh[k]);
-        const uint32_t addr = (x & VMASK) | voff;
+        const uint32_t addr = (uint32_t)va16[t * 2 * VAS + 64 * k + lane] | voff;
         if constexpr (C::VPAIR) {
           const v2f c = *(const v2f*)(vt + addr);
 #pragma unroll
