@@ -28,16 +28,17 @@
 //      softmax online softmax in base 2 (log2 e folded into q^), per head
 //              running max from a cross-lane reduction; weights p * nV_t.
 //      values  A[h][j] += sum_t w[h][t] * cV[idxV[t][j]]
-//              lanes own coordinates. During the scores phase the lane that
-//              holds token t unpacks t's V codes into 16-bit table offsets and
-//              writes them to an LDS table, token-major; here lane l reads
-//              its column (one 2-byte load per token, no unpacking) and looks
-//              the centroid up. The 4 heads' weights are broadcast the same
-//              way as q^.
-//    Centroid tables live in LDS replicated once per bank (16 copies of
-//    8-byte code-pair entries, or 32 copies of 4-byte entries), so a lookup
-//    is conflict-free whatever the codes; codes of <= 3 bits are looked up
-//    two coordinates at a time. The query rotation q^ = (scale log2 e / d)
+//              lanes own coordinates. The lane holding token t stages t's
+//              packed V row in LDS; per token each lane reads the two dwords
+//              that hold its code(s), funnel-shifts them and looks the
+//              centroid up. The 4 heads' weights are broadcast the same way
+//              as q^.
+//    The online softmax moves its running maximum only when a tile's
+//    maximum exceeds it by more than 2^8, so the rescale is rare.
+//    Centroid tables live in LDS replicated once per bank (a 256-byte row
+//    per code: 32 copies of an 8-byte code-pair entry or 64 copies of a
+//    4-byte entry), so a lookup is conflict-free whatever the codes; codes of
+//    <= 3 bits are looked up two coordinates at a time. The query rotation q^ = (scale log2 e / d)
 //    H (sigma_K (.) q) is done by every wavefront in its prologue.
 //    The wavefronts merge (max, sum, accumulator) through LDS and write one
 //    partial per (sequence, query head, split).
@@ -98,10 +99,17 @@ __device__ __forceinline__ float wave_max(float v) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+// Sum over the wavefront, returned in every lane (same DPP pattern).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Order this wavefront's LDS writes before its following LDS reads.
@@ -111,52 +119,89 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Bits [o - 7, o + 25) of the register row w (o a compile-time bit offset),
-// so that the field starting at bit o lands at bit 7.
+// Bits [O - 8, O + 24) of the register row w (O a compile-time bit offset),
+// so that the field starting at bit O lands at bit 8.
 template <int O, int NW>
-__device__ __forceinline__ uint32_t field_at7(const uint32_t (&w)[NW]) {
+__device__ __forceinline__ uint32_t field_at8(const uint32_t (&w)[NW]) {
   constexpr int wi = O >> 5, sh = O & 31;
-  if constexpr (sh >= 7) {
-    if constexpr (wi + 1 < NW && sh > 7)
-      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh - 7);
+  if constexpr (sh >= 8) {
+    if constexpr (wi + 1 < NW && sh > 8)
+      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh - 8);
     else
-      return w[wi] >> (sh - 7);
+      return w[wi] >> (sh - 8);
   } else {
-    return w[wi] << (7 - sh);
+    return w[wi] << (8 - sh);
   }
 }
 
+// Centroid tables live in LDS as one 256-byte row per code (or code pair):
+// 64 copies of a 4-byte centroid, or 32 copies of an 8-byte centroid pair, so
+// that every lane reads its own copy and a lookup never has a bank conflict,
+// whatever the codes. A lookup address is (code << 8) | lane_offset.
 template <int D_, int BK_, int BV_, int NHG_, int WAVES_>
-struct Cfg {
+struct CfgBase {
   static constexpr int D = D_, BK = BK_, BV = BV_, NHG = NHG_, WAVES = WAVES_;
   static constexpr int E = D / 64;                     // coordinates per lane (rotation)
   static constexpr bool KPAIR = BK <= 3;               // K looked up two coordinates at a time
-  static constexpr bool VPAIR = BV <= 3 && D >= 128;   // V likewise (pair tables <= 8 KB)
+  static constexpr bool VPAIR = BV <= 3 && D >= 128;   // V likewise
   static constexpr int KF = KPAIR ? 2 * BK : BK;       // bits per K lookup
   static constexpr int VF = VPAIR ? 2 * BV : BV;       // bits per V lookup
   static constexpr int NKL = KPAIR ? D / 2 : D;        // K lookups per token
   static constexpr int NVS = VPAIR ? D / 128 : D / 64; // V lookups per lane per token
   static constexpr int RKW = D * BK / 32;              // dwords per K row
   static constexpr int RVW = D * BV / 32;              // dwords per V row
-  static constexpr int NVF = VPAIR ? D / 2 : D;        // V lookups per token
-  // V lookup offsets of a tile, 16 bits each, token-major: a row of NVF/2
-  // dwords per token, stride = 2 mod 4 dwords so 8-byte row writes hit
-  // distinct banks
-  static constexpr int VAS = NVF / 2 + 2;
-  static constexpr int KT_BYTES = (1 << KF) * 128;     // 16 x 8 B or 32 x 4 B per entry
-  static constexpr int VT_BYTES = (1 << VF) * 128;
-  static constexpr int VA_DW = kTile * VAS;
-  static constexpr int VA_DW_Q = VA_DW > D ? VA_DW : D;   // also holds one rotated query
-  static constexpr int WBUF_F = kTile * 4 * NHG;
-  static constexpr int WAVE_BYTES = (VA_DW_Q + WBUF_F) * 4;
-  static constexpr int MAIN_BYTES = KT_BYTES + VT_BYTES + WAVES * WAVE_BYTES;
+  // V rows of a tile staged in LDS, one per token: 2 dwords of lead padding,
+  // the row, tail padding; stride = 2 mod 4 dwords so 8-byte row writes of
+  // 32 consecutive lanes hit distinct banks.
+  static constexpr int VSTR = ((RVW + 3) % 4 == 2) ? RVW + 3
+                              : ((RVW + 4) % 4 == 2) ? RVW + 4
+                              : ((RVW + 5) % 4 == 2) ? RVW + 5 : RVW + 6;
+  static constexpr int VT_BYTES = (1 << VF) * 256;
+  static constexpr int KT_BYTES = (1 << KF) * 256;
+  static constexpr int VS_BYTES = kTile * VSTR * 4;     // per wavefront
+  static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights of a tile
+  static constexpr int QS_BYTES = 4 * NHG * D * 4;      // rotated queries, before the first tile
+  static constexpr int WQ_BYTES = WAVES * WB_BYTES > QS_BYTES ? WAVES * WB_BYTES : QS_BYTES;
+  static constexpr int CEN_BYTES = 2 * 256 * 4;         // plain centroid tables while filling
+  static constexpr int MAIN_BYTES = VT_BYTES + KT_BYTES + WAVES * VS_BYTES + WQ_BYTES + CEN_BYTES;
   static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * D) * 4;
   static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
-  static_assert(VAS % 4 == 2, "V offset row stride");
-  static_assert(KT_BYTES <= 32768 && VT_BYTES <= 32768, "16-bit table offsets");
-  static_assert(LDS_BYTES <= 163840, "LDS budget");
 };
+
+constexpr int kLdsPerCU = 163840;
+
+// Wavefronts per workgroup: as many as the LDS allows (16, 12, 8 or 4); the
+// centroid tables are shared by all of them. Several head groups with large
+// K tables need more registers than 16 wavefronts leave (128 per lane).
+template <int D, int BK, int BV, int NHG>
+constexpr int cfg_waves() {
+  constexpr bool heavy = NHG >= 4 || (NHG >= 2 && (CfgBase<D, BK, BV, NHG, 4>::KF >= 8 || D >= 256));
+  if (!heavy && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
+  if (!heavy && CfgBase<D, BK, BV, NHG, 12>::LDS_BYTES <= kLdsPerCU) return 12;
+  if (CfgBase<D, BK, BV, NHG, 8>::LDS_BYTES <= kLdsPerCU) return 8;
+  return 4;
+}
+template <int D, int BK, int BV, int NHG>
+struct Cfg : CfgBase<D, BK, BV, NHG, cfg_waves<D, BK, BV, NHG>()> {
+  using B = CfgBase<D, BK, BV, NHG, 4>;
+  static_assert(B::VSTR % 4 == 2 && B::VSTR >= B::RVW + 3, "V row stride");
+  static_assert(B::VT_BYTES < 65536, "K table base must fit a DS offset");
+  static_assert(CfgBase<D, BK, BV, NHG, 4>::LDS_BYTES <= kLdsPerCU, "LDS budget");
+};
+
+// One tile's worth of this lane's token: packed K and V rows and the norms.
+template <class C>
+struct TileRegs {
+  uint32_t kw[C::RKW];
+  uint32_t vw[C::RVW];
+  float nk, nv;
+};
+
+// Rescale threshold of the online softmax (log2 units): the running maximum
+// is only moved when a tile's maximum exceeds it by more than this, so
+// weights stay below 2^8 and the rescale is rare.
+constexpr float kRescaleSlack = 8.f;
 
 template <class C>
 __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
@@ -166,7 +211,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     int group, int max_ctx, int max_len, int tokens_per_split, float qscale,
     float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign) {
   constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
-  constexpr int RKW = C::RKW, RVW = C::RVW, VAS = C::VAS;
+  constexpr int RKW = C::RKW, RVW = C::RVW, VSTR = C::VSTR;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -178,10 +223,12 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   const int G = group;
   const int n_q_heads = n_kv_heads * G;
 
-  unsigned char* kt = lds;
-  unsigned char* vt = lds + C::KT_BYTES;
-  uint32_t* vabuf = (uint32_t*)(lds + C::KT_BYTES + C::VT_BYTES + wave * C::WAVE_BYTES);
-  float* wbuf = (float*)(vabuf + C::VA_DW_Q);
+  unsigned char* vt = lds;
+  unsigned char* kt = lds + C::VT_BYTES;
+  uint32_t* vstage = (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + wave * C::VS_BYTES);
+  float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES);
+  float* wbuf = wq + wave * (C::WB_BYTES / 4);
+  float* cen = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + C::WQ_BYTES);
 
   const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_ctx;
   const uint32_t* __restrict__ kbase = (const uint32_t*)k_codes + kvrow0 * RKW;
@@ -189,8 +236,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   const float* __restrict__ knb = k_norms + kvrow0;
   const float* __restrict__ vnb = v_norms + kvrow0;
 
-  // ---- tile registers: this lane's token rows and norms
-  auto load_tile = [&](int tile, uint32_t (&kw)[RKW], uint32_t (&vw)[RVW], float& nk, float& nv) {
+  // ---- tile registers: this lane's token rows and norms (zeros past the end)
+  auto load_tile = [&](int tile, TileRegs<C>& r) {
     const int t = tile + lane;
     if (t < t_end) {
       const uint32_t* kr = kbase + (long long)t * RKW;
@@ -199,122 +246,109 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
         for (int i = 0; i < RKW; i += 4) {
           const uint4 x = *(const uint4*)(kr + i);
-          kw[i] = x.x; kw[i + 1] = x.y; kw[i + 2] = x.z; kw[i + 3] = x.w;
+          r.kw[i] = x.x; r.kw[i + 1] = x.y; r.kw[i + 2] = x.z; r.kw[i + 3] = x.w;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < RKW; i += 2) {
           const uint2 x = *(const uint2*)(kr + i);
-          kw[i] = x.x; kw[i + 1] = x.y;
+          r.kw[i] = x.x; r.kw[i + 1] = x.y;
         }
       }
       if constexpr (RVW % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < RVW; i += 4) {
           const uint4 x = *(const uint4*)(vr + i);
-          vw[i] = x.x; vw[i + 1] = x.y; vw[i + 2] = x.z; vw[i + 3] = x.w;
+          r.vw[i] = x.x; r.vw[i + 1] = x.y; r.vw[i + 2] = x.z; r.vw[i + 3] = x.w;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < RVW; i += 2) {
           const uint2 x = *(const uint2*)(vr + i);
-          vw[i] = x.x; vw[i + 1] = x.y;
+          r.vw[i] = x.x; r.vw[i + 1] = x.y;
         }
       }
-      nk = knb[t];
-      nv = vnb[t];
+      r.nk = knb[t];
+      r.nv = vnb[t];
     } else {
 #pragma unroll
-      for (int i = 0; i < RKW; ++i) kw[i] = 0u;
+      for (int i = 0; i < RKW; ++i) r.kw[i] = 0u;
 #pragma unroll
-      for (int i = 0; i < RVW; ++i) vw[i] = 0u;
-      nk = 0.f;
-      nv = 0.f;
+      for (int i = 0; i < RVW; ++i) r.vw[i] = 0u;
+      r.nk = 0.f;
+      r.nv = 0.f;
     }
   };
 
-  uint32_t kw[RKW], vw[RVW];
-  float nk, nv;
-  int tile = t_begin + wave * kTile;
-  if (tile < t_end) load_tile(tile, kw, vw, nk, nv);
+  // the first tile of this wavefront is requested before anything else
+  constexpr int kStride = WAVES * kTile;
+  const int tile0 = t_begin + wave * kTile;
+  TileRegs<C> ra;
+  if (tile0 < t_end) load_tile(tile0, ra);
 
-  // ---- centroid tables, one copy per LDS bank
-  {
-    const int nthr = 64 * WAVES;
-    if constexpr (C::KPAIR) {
-      constexpr int M = (1 << C::BK) - 1;
-      for (int i = threadIdx.x; i < (1 << C::KF) * 16; i += nthr) {
-        const int pr = i >> 4;
-        ((v2f*)kt)[i] = v2f{tabs.k_centroids[pr & M], tabs.k_centroids[pr >> C::BK]};
-      }
-    } else {
-      for (int i = threadIdx.x; i < (1 << C::KF) * 32; i += nthr)
-        ((float*)kt)[i] = tabs.k_centroids[i >> 5];
+  // ---- centroid tables: plain copies from the kernel arguments, then one
+  //      replicated 256-byte row per code (pair)
+  const int nthr = 64 * WAVES;
+  for (int i = threadIdx.x; i < 512; i += nthr)
+    cen[i] = i < 256 ? tabs.v_centroids[i] : tabs.k_centroids[i - 256];
+  __syncthreads();
+  auto fill = [&](unsigned char* tab, const float* c, int bits, bool pair) {
+    const int rows = 1 << (pair ? 2 * bits : bits);
+    const int mask = (1 << bits) - 1;
+    for (int i = threadIdx.x; i < rows * 16; i += nthr) {
+      const int e = i >> 4;
+      const v4f x = pair ? v4f{c[e & mask], c[e >> bits], c[e & mask], c[e >> bits]}
+                         : v4f{c[e], c[e], c[e], c[e]};
+      ((v4f*)tab)[i] = x;
     }
-    if constexpr (C::VPAIR) {
-      constexpr int M = (1 << C::BV) - 1;
-      for (int i = threadIdx.x; i < (1 << C::VF) * 16; i += nthr) {
-        const int pr = i >> 4;
-        ((v2f*)vt)[i] = v2f{tabs.v_centroids[pr & M], tabs.v_centroids[pr >> C::BV]};
-      }
-    } else {
-      for (int i = threadIdx.x; i < (1 << C::VF) * 32; i += nthr)
-        ((float*)vt)[i] = tabs.v_centroids[i >> 5];
-    }
-  }
+  };
+  fill(vt, cen, C::BV, C::VPAIR);
+  fill(kt, cen + 256, C::BK, C::KPAIR);
 
-  // ---- rotated queries in the broadcast layout: lane 4c + v of VGPR Q[hg][m]
-  //      holds q^[4 hg + v][16 m + c]
-  float Q[NHG][D / 16];
-#pragma unroll
-  for (int hg = 0; hg < NHG; ++hg)
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) Q[hg][m] = 0.f;
+  // ---- rotated queries: wavefront w rotates heads w, w + WAVES, ... into LDS
   {
-    float* qbuf = (float*)vabuf;
     const __half* qb = q + ((long long)b * n_q_heads + (long long)g * G) * D;
-    sfor<4 * NHG>([&](auto HH) {
-      constexpr int h = HH;
-      if (h < G) {
-        float u[E];
+    for (int h = wave; h < G; h += WAVES) {
+      float u[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = E * lane + e;
+        const float x = __half2float(qb[h * D + j]);
+        u[e] = ((ksign.bits[j >> 5] >> (j & 31)) & 1u) ? -x : x;
+      }
+#pragma unroll
+      for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((e & hs) == 0) {
+            const float a0 = u[e], a1 = u[e + hs];
+            u[e] = a0 + a1;
+            u[e + hs] = a0 - a1;
+          }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const bool upper = (lane & m) != 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const int j = E * lane + e;
-          const float x = __half2float(qb[h * D + j]);
-          u[e] = ((ksign.bits[j >> 5] >> (j & 31)) & 1u) ? -x : x;
-        }
-#pragma unroll
-        for (int hs = 1; hs < E; hs <<= 1)
-#pragma unroll
-          for (int e = 0; e < E; ++e)
-            if ((e & hs) == 0) {
-              const float a0 = u[e], a1 = u[e + hs];
-              u[e] = a0 + a1;
-              u[e + hs] = a0 - a1;
-            }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-          const bool upper = (lane & m) != 0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float p = __shfl_xor(u[e], m);
-            u[e] = upper ? (p - u[e]) : (u[e] + p);
-          }
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int e = 0; e < E; ++e) qbuf[E * lane + e] = u[e] * qscale;
-        wave_lds_sync();
-        const bool mine = (lane & 3) == (h & 3);
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) {
-          const float x = qbuf[16 * m + (lane >> 2)];
-          Q[h / 4][m] = mine ? x : Q[h / 4][m];
+          const float p = __shfl_xor(u[e], m);
+          u[e] = upper ? (p - u[e]) : (u[e] + p);
         }
       }
-    });
+#pragma unroll
+      for (int e = 0; e < E; ++e) wq[h * D + E * lane + e] = u[e] * qscale;
+    }
   }
-  __syncthreads();  // tables ready
+  __syncthreads();  // tables and rotated queries ready
+
+  // broadcast layout: lane 4c + v of VGPR Q[hg][m] holds q^[4 hg + v][16 m + c]
+  float Q[NHG][D / 16];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int h = 4 * hg + (lane & 3);
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < G ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
+  }
+  __syncthreads();  // the query area becomes the weight buffers
 
   // ---- per-wave online-softmax state
   float m_run[NHG][4];
@@ -329,25 +363,30 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int a = 0; a < C::NACC; ++a) acc[a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint32_t koff = C::KPAIR ? (uint32_t)(lane & 15) << 3 : (uint32_t)(lane & 31) << 2;
-  const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 15) << 3 : (uint32_t)(lane & 31) << 2;
-  constexpr uint32_t KMASK = ((1u << C::KF) - 1u) << 7;
-  constexpr uint32_t VMASK = ((1u << C::VF) - 1u) << 7;
+  const uint32_t koff = C::KPAIR ? (uint32_t)(lane & 31) << 3 : (uint32_t)lane << 2;
+  const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 31) << 3 : (uint32_t)lane << 2;
+  constexpr uint32_t KMASK = ((1u << C::KF) - 1u) << 8;
+  constexpr uint32_t VMASK = ((1u << C::VF) - 1u) << 8;
 
-  for (; tile < t_end; tile += WAVES * kTile) {
-    const int next = tile + WAVES * kTile;
+  // V fields of this lane: field 64k + lane of each staged row, read from bit
+  // o - 8 of the padded row so the field lands at bit 8
+  int vdw[C::NVS], vsh[C::NVS];
+#pragma unroll
+  for (int k = 0; k < C::NVS; ++k) {
+    const int o = C::VF * (64 * k + lane) + 64 - 8;
+    vdw[k] = o >> 5;
+    vsh[k] = o & 31;
+  }
+
+  // One tile: scores, online softmax, values. `r` is consumed and refilled
+  // with the wavefront's next tile as soon as its rows have been used.
+  auto process = [&](int tile, TileRegs<C>& r) {
     const bool valid = tile + lane < t_end;
 
-    // this token's V lookup offsets (code << 7), two per dword, into row `lane`
-    // of the tile's offset table: the values phase reads them column-wise
-    sfor<C::NVF / 4>([&](auto PI) {
-      constexpr int f = 4 * PI;
-      const uint32_t a0 = field_at7<C::VF * f>(vw) & VMASK;
-      const uint32_t a1 = field_at7<C::VF * (f + 1)>(vw) & VMASK;
-      const uint32_t a2 = field_at7<C::VF * (f + 2)>(vw) & VMASK;
-      const uint32_t a3 = field_at7<C::VF * (f + 3)>(vw) & VMASK;
-      *(uint2*)(vabuf + lane * VAS + f / 2) = uint2{a0 | (a1 << 16), a2 | (a3 << 16)};
-    });
+    // stage this token's V row (row `lane`, after 2 dwords of padding)
+#pragma unroll
+    for (int i = 0; i < RVW; i += 2)
+      *(uint2*)(vstage + lane * VSTR + 2 + i) = uint2{r.vw[i], r.vw[i + 1]};
 
     // ---- scores on the matrix cores
     v4f s0[NHG], s1[NHG];
@@ -358,8 +397,15 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     }
     sfor<C::NKL>([&](auto FI) {
       constexpr int f = FI;
-      const uint32_t x = field_at7<C::KF * f>(kw);
-      const uint32_t addr = (x & KMASK) | koff;
+      constexpr int bit = C::KF * f;
+      uint32_t addr;
+      if constexpr (C::KF == 8) {
+        // whole byte: one byte permute builds (code << 8) | koff
+        addr = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
+                                     0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
+      } else {
+        addr = (field_at8<bit>(r.kw) & KMASK) | koff;
+      }
       if constexpr (C::KPAIR) {
         const v2f c = *(const v2f*)(kt + addr);
         constexpr int j0 = 2 * f, j1 = 2 * f + 1;
@@ -380,27 +426,31 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
     });
 
-    const float nv_cur = nv;
-    const float nk_cur = nk;
-    // prefetch the next tile while this one is finished
-    if (next < t_end) load_tile(next, kw, vw, nk, nv);
+    const float nv_cur = r.nv;
+    const float nk_cur = r.nk;
+    // the rows are consumed: refill with this wavefront's next tile
+    const int ahead = tile + kStride;
+    if (ahead < t_end) load_tile(ahead, r);
 
-    // ---- online softmax (base 2) and value weights
+    // ---- online softmax (base 2) with a lazily moved maximum
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
-      v4f s = (s0[hg] + s1[hg]) * nk_cur;
+      const v4f s = (s0[hg] + s1[hg]) * nk_cur;
       v4f w;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float sv = valid ? s[v] : -INFINITY;
-        const float mn = fmaxf(m_run[hg][v], wave_max(sv));
-        const float alpha = exp2f(m_run[hg][v] - mn);
-        const float p = exp2f(sv - mn);
-        l_run[hg][v] = l_run[hg][v] * alpha + p;
-        m_run[hg][v] = mn;
-        w[v] = p * nv_cur;
+        const float mt = wave_max(sv);
+        if (mt > m_run[hg][v] + kRescaleSlack) {  // wavefront-uniform
+          const float alpha = exp2f(m_run[hg][v] - mt);
+          l_run[hg][v] *= alpha;
 #pragma unroll
-        for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
+          for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
+          m_run[hg][v] = mt;
+        }
+        const float p = exp2f(sv - m_run[hg][v]);
+        l_run[hg][v] += p;
+        w[v] = p * nv_cur;
       }
       *(v4f*)(wbuf + (lane * NHG + hg) * 4) = w;
     }
@@ -415,12 +465,13 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         Wr[hg][m] = wbuf[((16 * m + (lane >> 2)) * NHG + hg) * 4 + (lane & 3)];
 
     // ---- values on the matrix cores, lanes over coordinates
-    const unsigned short* va16 = (const unsigned short*)vabuf;
     sfor<kTile>([&](auto TI) {
       constexpr int t = TI;
+      const uint32_t* row = vstage + t * VSTR;
 #pragma unroll
       for (int k = 0; k < C::NVS; ++k) {
-        const uint32_t addr = (uint32_t)va16[t * 2 * VAS + 64 * k + lane] | voff;
+        const uint32_t x = __builtin_amdgcn_alignbit(row[vdw[k] + 1], row[vdw[k]], vsh[k]);
+        const uint32_t addr = (x & VMASK) | voff;
         if constexpr (C::VPAIR) {
           const v2f c = *(const v2f*)(vt + addr);
 #pragma unroll
@@ -438,7 +489,9 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
     });
     wave_lds_sync();
-  }
+  };
+
+  for (int tile = tile0; tile < t_end; tile += kStride) process(tile, ra);
 
   // ---- merge the wavefronts of this workgroup and write the split partial
   float lsum[NHG][4];
@@ -450,18 +503,27 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) acc[0][hg] += acc[1][hg];
   }
-  __syncthreads();  // all wavefronts are done with tables and staging
-  float* mbuf = (float*)lds;                    // [WAVES][4 NHG][2]
-  float* abuf = mbuf + WAVES * 4 * NHG * 2;     // [WAVES][4][D]
+  __syncthreads();  // all wavefronts are done with tables and buffers
+  float* mbuf = (float*)lds;                    // [WAVES][4 NHG] maxima
+  float* abuf = mbuf + WAVES * 4 * NHG * 2;     // [WAVES][4][D] rescaled accumulators
   if (lane == 0) {
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        mbuf[(wave * 4 * NHG + 4 * hg + v) * 2] = m_run[hg][v];
-        mbuf[(wave * 4 * NHG + 4 * hg + v) * 2 + 1] = lsum[hg][v];
-      }
+      for (int v = 0; v < 4; ++v) mbuf[wave * 4 * NHG + 4 * hg + v] = m_run[hg][v];
   }
+  __syncthreads();
+  // this wavefront's factor 2^(m_w - M) per head, M the workgroup maximum
+  float fw[NHG][4];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float M = -INFINITY;
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[w * 4 * NHG + 4 * hg + v]);
+      fw[hg][v] = m_run[hg][v] == -INFINITY ? 0.f : exp2f(m_run[hg][v] - M);
+      if (lane == 0) mbuf[WAVES * 4 * NHG + wave * 4 * NHG + 4 * hg + v] = fw[hg][v] * lsum[hg][v];
+    }
   const int S = gridDim.x;
   sfor<NHG>([&](auto HGI) {
     constexpr int hg = HGI;
@@ -469,15 +531,16 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float* dst = abuf + (wave * 4 + v) * D;
+      const float f = fw[hg][v];
       if constexpr (C::VPAIR) {
 #pragma unroll
         for (int k = 0; k < C::NVS; ++k) {
-          dst[2 * (64 * k + lane)] = acc[2 * k][hg][v];
-          dst[2 * (64 * k + lane) + 1] = acc[2 * k + 1][hg][v];
+          dst[2 * (64 * k + lane)] = acc[2 * k][hg][v] * f;
+          dst[2 * (64 * k + lane) + 1] = acc[2 * k + 1][hg][v] * f;
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = acc[k][hg][v];
+        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = acc[k][hg][v] * f;
       }
     }
     __syncthreads();
@@ -485,20 +548,16 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       const int v = idx / D, j = idx - v * D;
       const int h = 4 * hg + v;
       if (h >= G) continue;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[(w * 4 * NHG + h) * 2]);
-      float a = 0.f, L = 0.f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float mw = mbuf[(w * 4 * NHG + h) * 2];
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        a = fmaf(f, abuf[(w * 4 + v) * D + j], a);
-        L = fmaf(f, mbuf[(w * 4 * NHG + h) * 2 + 1], L);
-      }
+      float a = 0.f;
+      for (int w = 0; w < WAVES; ++w) a += abuf[(w * 4 + v) * D + j];
       const long long prow = ((long long)b * n_q_heads + (long long)g * G + h) * S + split;
       part_acc[prow * D + j] = a;
       if (j == 0) {
+        float M = -INFINITY, L = 0.f;
+        for (int w = 0; w < WAVES; ++w) {
+          M = fmaxf(M, mbuf[w * 4 * NHG + h]);
+          L += mbuf[WAVES * 4 * NHG + w * 4 * NHG + h];
+        }
         part_ml[prow * 2] = M;
         part_ml[prow * 2 + 1] = L;
       }
@@ -617,25 +676,24 @@ struct SplitEntry {
   SplitFn fn;
 };
 
-// Instantiated (head_dim, K bits, V bits, groups of 4 query heads, wavefronts
-// per workgroup). A group size G is served by the entry with the smallest
-// nhg such that G <= 4 * nhg.
-#define TQ_SPLIT(D, BK, BV, NHG, W) {D, BK, BV, NHG, &launch_split<Cfg<D, BK, BV, NHG, W>>}
+// Instantiated (head_dim, K bits, V bits, groups of 4 query heads). A group
+// size G is served by the entry with the smallest nhg such that G <= 4 * nhg.
+#define TQ_SPLIT(D, BK, BV, NHG) {D, BK, BV, NHG, &launch_split<Cfg<D, BK, BV, NHG>>}
 const SplitEntry kSplitTable[] = {
     // head_dim 64
-    TQ_SPLIT(64, 4, 4, 1, 4), TQ_SPLIT(64, 3, 3, 2, 4), TQ_SPLIT(64, 3, 3, 1, 4),
-    TQ_SPLIT(64, 8, 3, 1, 4), TQ_SPLIT(64, 2, 2, 1, 4), TQ_SPLIT(64, 1, 1, 1, 4),
-    TQ_SPLIT(64, 5, 7, 1, 4), TQ_SPLIT(64, 6, 6, 4, 4), TQ_SPLIT(64, 4, 4, 2, 4),
-    TQ_SPLIT(64, 8, 3, 2, 4),
+    TQ_SPLIT(64, 4, 4, 1), TQ_SPLIT(64, 3, 3, 2), TQ_SPLIT(64, 3, 3, 1),
+    TQ_SPLIT(64, 8, 3, 1), TQ_SPLIT(64, 2, 2, 1), TQ_SPLIT(64, 1, 1, 1),
+    TQ_SPLIT(64, 5, 7, 1), TQ_SPLIT(64, 6, 6, 4), TQ_SPLIT(64, 4, 4, 2),
+    TQ_SPLIT(64, 8, 3, 2),
     // head_dim 128
-    TQ_SPLIT(128, 4, 2, 1, 4), TQ_SPLIT(128, 8, 3, 1, 4), TQ_SPLIT(128, 3, 3, 1, 4),
-    TQ_SPLIT(128, 4, 4, 1, 4), TQ_SPLIT(128, 4, 3, 1, 4), TQ_SPLIT(128, 2, 2, 1, 4),
-    TQ_SPLIT(128, 8, 4, 1, 4), TQ_SPLIT(128, 4, 4, 2, 4), TQ_SPLIT(128, 8, 3, 2, 4),
-    TQ_SPLIT(128, 1, 1, 1, 4), TQ_SPLIT(128, 7, 5, 2, 4),
-    TQ_SPLIT(128, 3, 3, 2, 4), TQ_SPLIT(128, 4, 2, 2, 4),
+    TQ_SPLIT(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
+    TQ_SPLIT(128, 4, 4, 1), TQ_SPLIT(128, 4, 3, 1), TQ_SPLIT(128, 2, 2, 1),
+    TQ_SPLIT(128, 8, 4, 1), TQ_SPLIT(128, 4, 4, 2), TQ_SPLIT(128, 8, 3, 2),
+    TQ_SPLIT(128, 1, 1, 1), TQ_SPLIT(128, 7, 5, 2),
+    TQ_SPLIT(128, 3, 3, 2), TQ_SPLIT(128, 4, 2, 2),
     // head_dim 256
-    TQ_SPLIT(256, 4, 4, 1, 4), TQ_SPLIT(256, 8, 3, 1, 2), TQ_SPLIT(256, 3, 3, 1, 4),
-    TQ_SPLIT(256, 8, 4, 1, 2), TQ_SPLIT(256, 2, 2, 2, 4),
+    TQ_SPLIT(256, 4, 4, 1), TQ_SPLIT(256, 8, 3, 1), TQ_SPLIT(256, 3, 3, 1),
+    TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2),
 };
 #undef TQ_SPLIT
 
@@ -652,13 +710,14 @@ const SplitEntry* find_split(int d, int bk, int bv, int group) {
 
 AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
   AttendPlan p{};
-  // About 1024 workgroups (four per CU) and at least two tiles per wavefront.
+  // One workgroup per CU per round (256 CUs) and whole tiles for every
+  // wavefront of the largest (16-wavefront) workgroups.
   const long long units = (long long)batch * n_kv_heads;
-  const long long target_wgs = 1024;
-  const long long quantum = 4 * kTile;
+  const long long target_wgs = 256;
+  const long long quantum = 16 * kTile;
   long long tps = ((long long)max_len * units + target_wgs - 1) / target_wgs;
   tps = ((tps + quantum - 1) / quantum) * quantum;
-  if (tps < 2 * quantum) tps = 2 * quantum;
+  if (tps < quantum) tps = quantum;
   p.tokens_per_split = (int)tps;
   p.splits = (int)((max_len + tps - 1) / tps);
   if (p.splits < 1) p.splits = 1;
