@@ -119,16 +119,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Bits [O - 8, O + 24) of the register row w (O a compile-time bit offset),
-// so that the field starting at bit O lands at bit 8.
-template <int O, int NW>
+// The F-bit field starting at bit O of the register row w (O a compile-time
+// bit offset), moved so that it starts at bit 8; bits above it are garbage.
+// The next register is read only when the field straddles into it.
+template <int O, int F, int NW>
 __device__ __forceinline__ uint32_t field_at8(const uint32_t (&w)[NW]) {
   constexpr int wi = O >> 5, sh = O & 31;
-  if constexpr (sh >= 8) {
-    if constexpr (wi + 1 < NW && sh > 8)
-      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh - 8);
-    else
-      return w[wi] >> (sh - 8);
+  if constexpr (sh + F > 32) {
+    static_assert(wi + 1 < NW && sh > 8, "straddling field");
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh - 8);
+  } else if constexpr (sh >= 8) {
+    return w[wi] >> (sh - 8);
   } else {
     return w[wi] << (8 - sh);
   }
@@ -150,20 +151,18 @@ struct CfgBase {
   static constexpr int NVS = VPAIR ? D / 128 : D / 64; // V lookups per lane per token
   static constexpr int RKW = D * BK / 32;              // dwords per K row
   static constexpr int RVW = D * BV / 32;              // dwords per V row
-  // V rows of a tile staged in LDS, one per token: 2 dwords of lead padding,
-  // the row, tail padding; stride = 2 mod 4 dwords so 8-byte row writes of
-  // 32 consecutive lanes hit distinct banks.
-  static constexpr int VSTR = ((RVW + 3) % 4 == 2) ? RVW + 3
-                              : ((RVW + 4) % 4 == 2) ? RVW + 4
-                              : ((RVW + 5) % 4 == 2) ? RVW + 5 : RVW + 6;
+  // V rows of a tile staged contiguously in LDS (row t at dword 2 + t RVW,
+  // 2 dwords of padding on each side): a lane reads the two dwords around its
+  // field, which may reach from the dword before the row to the dword after
+  // it (a neighbouring row or padding; those bits are masked off).
   static constexpr int VT_BYTES = (1 << VF) * 256;
   static constexpr int KT_BYTES = (1 << KF) * 256;
-  static constexpr int VS_BYTES = kTile * VSTR * 4;     // per wavefront
+  static constexpr int VS_BYTES = (kTile * RVW + 4) * 4;  // per wavefront
   static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights of a tile
-  static constexpr int QS_BYTES = 4 * NHG * D * 4;      // rotated queries, before the first tile
-  static constexpr int WQ_BYTES = WAVES * WB_BYTES > QS_BYTES ? WAVES * WB_BYTES : QS_BYTES;
+  static constexpr int QS_BYTES = 4 * NHG * D * 4;      // rotated queries
   static constexpr int CEN_BYTES = 2 * 256 * 4;         // plain centroid tables while filling
-  static constexpr int MAIN_BYTES = VT_BYTES + KT_BYTES + WAVES * VS_BYTES + WQ_BYTES + CEN_BYTES;
+  static constexpr int MAIN_BYTES =
+      VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + CEN_BYTES;
   static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * D) * 4;
   static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
@@ -171,21 +170,31 @@ struct CfgBase {
 
 constexpr int kLdsPerCU = 163840;
 
-// Wavefronts per workgroup: as many as the LDS allows (16, 12, 8 or 4); the
-// centroid tables are shared by all of them. Several head groups with large
-// K tables need more registers than 16 wavefronts leave (128 per lane).
+// Rough count of the VGPRs one lane holds through the tile loop: rotated
+// queries, the tile's rows and norms, value accumulators, score, weight and
+// softmax state, V field positions.
+template <class B>
+constexpr int vgpr_estimate() {
+  return B::NHG * B::D / 16 + B::RKW + B::RVW + 2 + B::NACC * B::NHG * 4 + B::NHG * 20 +
+         2 * B::NVS;
+}
+
+// Wavefronts per workgroup: as many as the LDS and the register file allow
+// (16, 12, 8 or 4; 128, 168 or 256 VGPRs per lane); the centroid tables are
+// shared by all of them.
 template <int D, int BK, int BV, int NHG>
 constexpr int cfg_waves() {
-  constexpr bool heavy = NHG >= 4 || (NHG >= 2 && (CfgBase<D, BK, BV, NHG, 4>::KF >= 8 || D >= 256));
-  if (!heavy && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
-  if (!heavy && CfgBase<D, BK, BV, NHG, 12>::LDS_BYTES <= kLdsPerCU) return 12;
+  using B = CfgBase<D, BK, BV, NHG, 4>;
+  constexpr int need = vgpr_estimate<B>() + 24;  // + addresses, temporaries
+  if (NHG < 4 && need <= 128 && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
+  if (NHG < 4 && need <= 168 && CfgBase<D, BK, BV, NHG, 12>::LDS_BYTES <= kLdsPerCU) return 12;
   if (CfgBase<D, BK, BV, NHG, 8>::LDS_BYTES <= kLdsPerCU) return 8;
   return 4;
 }
 template <int D, int BK, int BV, int NHG>
 struct Cfg : CfgBase<D, BK, BV, NHG, cfg_waves<D, BK, BV, NHG>()> {
   using B = CfgBase<D, BK, BV, NHG, 4>;
-  static_assert(B::VSTR % 4 == 2 && B::VSTR >= B::RVW + 3, "V row stride");
+  static_assert(B::RVW % 2 == 0, "V rows are staged with 8-byte writes");
   static_assert(B::VT_BYTES < 65536, "K table base must fit a DS offset");
   static_assert(CfgBase<D, BK, BV, NHG, 4>::LDS_BYTES <= kLdsPerCU, "LDS budget");
 };
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     int group, int max_ctx, int max_len, int tokens_per_split, float qscale,
     float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign) {
   constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
-  constexpr int RKW = C::RKW, RVW = C::RVW, VSTR = C::VSTR;
+  constexpr int RKW = C::RKW, RVW = C::RVW;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -226,9 +235,9 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   unsigned char* vt = lds;
   unsigned char* kt = lds + C::VT_BYTES;
   uint32_t* vstage = (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + wave * C::VS_BYTES);
-  float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES);
-  float* wbuf = wq + wave * (C::WB_BYTES / 4);
-  float* cen = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + C::WQ_BYTES);
+  float* wbuf = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + wave * C::WB_BYTES);
+  float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * (C::VS_BYTES + C::WB_BYTES));
+  float* cen = wq + C::QS_BYTES / 4;
 
   const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_ctx;
   const uint32_t* __restrict__ kbase = (const uint32_t*)k_codes + kvrow0 * RKW;
@@ -236,61 +245,80 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   const float* __restrict__ knb = k_norms + kvrow0;
   const float* __restrict__ vnb = v_norms + kvrow0;
 
-  // ---- tile registers: this lane's token rows and norms (zeros past the end)
-  auto load_tile = [&](int tile, TileRegs<C>& r) {
-    const int t = tile + lane;
-    if (t < t_end) {
-      const uint32_t* kr = kbase + (long long)t * RKW;
-      const uint32_t* vr = vbase + (long long)t * RVW;
-      if constexpr (RKW % 4 == 0) {
+  // ---- tile registers: this lane's token rows and norms. Lanes past the
+  //      range end load the range's last row instead (always in bounds); their
+  //      scores are masked to -inf, so the rows never contribute.
+  auto load_tile = [&](int tile, TileRegs<C>& r) __attribute__((always_inline)) {
+    const int t = min(tile + lane, t_end - 1);
+    const uint32_t* kr = kbase + (long long)t * RKW;
+    const uint32_t* vr = vbase + (long long)t * RVW;
+    // written in the order they are consumed (V norm and row, staged first;
+    // then K norm and row): vector loads complete in order, so the scores
+    // can start on the first pieces of the K row while the rest is in flight
+    r.nv = vnb[t];
+    if constexpr (RVW % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < RKW; i += 4) {
-          const uint4 x = *(const uint4*)(kr + i);
-          r.kw[i] = x.x; r.kw[i + 1] = x.y; r.kw[i + 2] = x.z; r.kw[i + 3] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < RKW; i += 2) {
-          const uint2 x = *(const uint2*)(kr + i);
-          r.kw[i] = x.x; r.kw[i + 1] = x.y;
-        }
+      for (int i = 0; i < RVW; i += 4) {
+        const uint4 x = *(const uint4*)(vr + i);
+        r.vw[i] = x.x; r.vw[i + 1] = x.y; r.vw[i + 2] = x.z; r.vw[i + 3] = x.w;
       }
-      if constexpr (RVW % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < RVW; i += 4) {
-          const uint4 x = *(const uint4*)(vr + i);
-          r.vw[i] = x.x; r.vw[i + 1] = x.y; r.vw[i + 2] = x.z; r.vw[i + 3] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < RVW; i += 2) {
-          const uint2 x = *(const uint2*)(vr + i);
-          r.vw[i] = x.x; r.vw[i + 1] = x.y;
-        }
-      }
-      r.nk = knb[t];
-      r.nv = vnb[t];
     } else {
 #pragma unroll
-      for (int i = 0; i < RKW; ++i) r.kw[i] = 0u;
+      for (int i = 0; i < RVW; i += 2) {
+        const uint2 x = *(const uint2*)(vr + i);
+        r.vw[i] = x.x; r.vw[i + 1] = x.y;
+      }
+    }
+    r.nk = knb[t];
+    if constexpr (RKW % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < RVW; ++i) r.vw[i] = 0u;
-      r.nk = 0.f;
-      r.nv = 0.f;
+      for (int i = 0; i < RKW; i += 4) {
+        const uint4 x = *(const uint4*)(kr + i);
+        r.kw[i] = x.x; r.kw[i + 1] = x.y; r.kw[i + 2] = x.z; r.kw[i + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RKW; i += 2) {
+        const uint2 x = *(const uint2*)(kr + i);
+        r.kw[i] = x.x; r.kw[i + 1] = x.y;
+      }
     }
   };
 
-  // the first tile of this wavefront is requested before anything else
-  constexpr int kStride = WAVES * kTile;
-  const int tile0 = t_begin + wave * kTile;
-  TileRegs<C> ra;
-  if (tile0 < t_end) load_tile(tile0, ra);
-
-  // ---- centroid tables: plain copies from the kernel arguments, then one
-  //      replicated 256-byte row per code (pair)
+  // ---- prologue, before any tile row is requested: fetch the centroid
+  //      tables, this wavefront's query rows and the sign words, build the LDS
+  //      tables and rotate the queries.
   const int nthr = 64 * WAVES;
-  for (int i = threadIdx.x; i < 512; i += nthr)
-    cen[i] = i < 256 ? tabs.v_centroids[i] : tabs.k_centroids[i - 256];
+  constexpr int kCenPer = (512 + 64 * WAVES - 1) / (64 * WAVES);
+  float cenv[kCenPer];
+#pragma unroll
+  for (int u = 0; u < kCenPer; ++u) {
+    const int i = threadIdx.x + u * nthr;
+    cenv[u] = i < 256 ? tabs.v_centroids[i] : (i < 512 ? tabs.k_centroids[i - 256] : 0.f);
+  }
+  constexpr int kHeadsPerWave = (4 * NHG + WAVES - 1) / WAVES;  // G <= 4 NHG
+  const __half* qb = q + ((long long)b * n_q_heads + (long long)g * G) * D;
+  __half qx[kHeadsPerWave][E];
+#pragma unroll
+  for (int r = 0; r < kHeadsPerWave; ++r) {
+    const int h = min(wave + r * WAVES, G - 1);  // in bounds; surplus rows unused
+#pragma unroll
+    for (int e = 0; e < E; ++e) qx[r][e] = qb[h * D + E * lane + e];
+  }
+  // sign word of this lane's coordinates E lane .. E lane + E - 1 (one word:
+  // E <= 4 consecutive coordinates never straddle a 32-bit boundary)
+  uint32_t sword = 0;
+#pragma unroll
+  for (int w = 0; w < D / 32; ++w)
+    if ((E * lane) >> 5 == w) sword = ksign.bits[w];
+
+  // ---- centroid tables: plain copies, then one replicated 256-byte row per
+  //      code (pair)
+#pragma unroll
+  for (int u = 0; u < kCenPer; ++u) {
+    const int i = threadIdx.x + u * nthr;
+    if (i < 512) cen[i] = cenv[u];
+  }
   __syncthreads();
   auto fill = [&](unsigned char* tab, const float* c, int bits, bool pair) {
     const int rows = 1 << (pair ? 2 * bits : bits);
@@ -306,15 +334,16 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   fill(kt, cen + 256, C::BK, C::KPAIR);
 
   // ---- rotated queries: wavefront w rotates heads w, w + WAVES, ... into LDS
-  {
-    const __half* qb = q + ((long long)b * n_q_heads + (long long)g * G) * D;
-    for (int h = wave; h < G; h += WAVES) {
+#pragma unroll
+  for (int r = 0; r < kHeadsPerWave; ++r) {
+    const int h = wave + r * WAVES;
+    if (h < G) {
       float u[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int j = E * lane + e;
-        const float x = __half2float(qb[h * D + j]);
-        u[e] = ((ksign.bits[j >> 5] >> (j & 31)) & 1u) ? -x : x;
+        const float x = __half2float(qx[r][e]);
+        u[e] = ((sword >> (j & 31)) & 1u) ? -x : x;
       }
 #pragma unroll
       for (int hs = 1; hs < E; hs <<= 1)
@@ -348,7 +377,14 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < G ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
   }
-  __syncthreads();  // the query area becomes the weight buffers
+
+  // Only now the first tile. Once the memory pipeline is saturated a wavefront
+  // stalls in issuing vector loads, so no workgroup barrier may follow them
+  // until the merge: each wavefront runs its tiles independently.
+  constexpr int kStride = WAVES * kTile;
+  const int tile0 = t_begin + wave * kTile;
+  TileRegs<C> ra;
+  load_tile(tile0, ra);  // in bounds even for a wavefront without tiles (rows clamped)
 
   // ---- per-wave online-softmax state
   float m_run[NHG][4];
@@ -380,13 +416,13 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   // One tile: scores, online softmax, values. `r` is consumed and refilled
   // with the wavefront's next tile as soon as its rows have been used.
-  auto process = [&](int tile, TileRegs<C>& r) {
+  auto process = [&](int tile, TileRegs<C>& r) __attribute__((always_inline)) {
     const bool valid = tile + lane < t_end;
 
     // stage this token's V row (row `lane`, after 2 dwords of padding)
 #pragma unroll
     for (int i = 0; i < RVW; i += 2)
-      *(uint2*)(vstage + lane * VSTR + 2 + i) = uint2{r.vw[i], r.vw[i + 1]};
+      *(uint2*)(vstage + 2 + lane * RVW + i) = uint2{r.vw[i], r.vw[i + 1]};
 
     // ---- scores on the matrix cores
     v4f s0[NHG], s1[NHG];
@@ -404,7 +440,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         addr = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
                                      0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
       } else {
-        addr = (field_at8<bit>(r.kw) & KMASK) | koff;
+        addr = (field_at8<bit, C::KF>(r.kw) & KMASK) | koff;
       }
       if constexpr (C::KPAIR) {
         const v2f c = *(const v2f*)(kt + addr);
@@ -467,7 +503,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     // ---- values on the matrix cores, lanes over coordinates
     sfor<kTile>([&](auto TI) {
       constexpr int t = TI;
-      const uint32_t* row = vstage + t * VSTR;
+      const uint32_t* row = vstage + t * RVW;
 #pragma unroll
       for (int k = 0; k < C::NVS; ++k) {
         const uint32_t x = __builtin_amdgcn_alignbit(row[vdw[k] + 1], row[vdw[k]], vsh[k]);
@@ -491,7 +527,10 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     wave_lds_sync();
   };
 
-  for (int tile = tile0; tile < t_end; tile += kStride) process(tile, ra);
+  // the first tile is peeled off the loop so that its register waits follow
+  // the order its loads were issued in
+  if (tile0 < t_end) process(tile0, ra);
+  for (int tile = tile0 + kStride; tile < t_end; tile += kStride) process(tile, ra);
 
   // ---- merge the wavefronts of this workgroup and write the split partial
   float lsum[NHG][4];
@@ -567,7 +606,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
 // ---------------------------------------------------------------- 2. combine
 
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 1024;
+constexpr int kCombineUnroll = 4;  // splits per thread whose loads are in flight together
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
@@ -576,7 +616,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     int tokens_per_split, float* __restrict__ out, SignArg sign) {
   constexpr int E = D / 64;
   constexpr int NG = kCombineThreads / D;  // split groups
-  __shared__ float s_red[kCombineThreads];
+  constexpr int U = kCombineUnroll;
   __shared__ float s_acc[NG][D];
   __shared__ float s_l[NG];
   const int tid = threadIdx.x;
@@ -585,25 +625,37 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int len = min(lengths[b], max_len);
   const int ns = len > 0 ? min(splits, (len + tokens_per_split - 1) / tokens_per_split) : 0;
   const float* ml = part_ml + row * splits * 2;
+  // sign word of coordinates E lane .. E lane + E - 1 (scalar loads, early)
+  uint32_t sword = 0;
+#pragma unroll
+  for (int w = 0; w < D / 32; ++w)
+    if ((E * (tid & 63)) >> 5 == w) sword = sign.bits[w];
 
-  // global max over the valid splits
+  // every wavefront takes the maximum over the valid splits itself
   float M = -INFINITY;
-  for (int s = tid; s < ns; s += kCombineThreads) M = fmaxf(M, ml[2 * s]);
-  s_red[tid] = M;
-  __syncthreads();
-  for (int w = kCombineThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-    __syncthreads();
-  }
-  M = s_red[0];
+  for (int s = tid & 63; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
 
-  // rescaled sums: thread (group grp, coordinate j) over splits s = grp mod NG
+  // rescaled sums: thread (group grp, coordinate j) over splits s = grp mod NG,
+  // U splits at a time with all their loads issued before any is used
   const int j = tid % D, grp = tid / D;
+  const float* pa = part_acc + row * splits * D + j;
   float a = 0.f, L = 0.f;
-  for (int s = grp; s < ns; s += NG) {
-    const float f = exp2f(ml[2 * s] - M);
-    a = fmaf(f, part_acc[(row * splits + s) * D + j], a);
-    L = fmaf(f, ml[2 * s + 1], L);
+  for (int s0 = grp; s0 < ns; s0 += NG * U) {
+    float mv[U], lv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u * NG, ns - 1);  // clamped: surplus slots get weight 0
+      mv[u] = ml[2 * s];
+      lv[u] = ml[2 * s + 1];
+      av[u] = pa[(long long)s * D];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = s0 + u * NG < ns ? exp2f(mv[u] - M) : 0.f;
+      a = fmaf(f, av[u], a);
+      L = fmaf(f, lv[u], L);
+    }
   }
   s_acc[grp][j] = a;
   if (j == 0) s_l[grp] = L;
@@ -646,7 +698,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int e = 0; e < E; ++e) {
       const int jj = E * lane + e;
       const float v = u[e] * invd;
-      out[row * D + jj] = ((sign.bits[jj >> 5] >> (jj & 31)) & 1u) ? -v : v;
+      out[row * D + jj] = ((sword >> (jj & 31)) & 1u) ? -v : v;
     }
   }
 }
