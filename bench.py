@@ -76,6 +76,57 @@ def copy_calibration(mb, steps):
                       "read_plus_write_GBps": moved / (ms * 1e-3) / 1e9}), flush=True)
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attend_split_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "compressed_domain_decode_amd", "csrc", "attend.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, each scaled by what the counter reads for a copy of known
+    size; None unless the record is for this workload and for the kernel source
+    as it is now (the counters describe one build of the kernel)."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_RECORD):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != src_hash:
+        return None
+    fetch = float(rec["fetch_size_kib"]) * float(rec["fetch_scale"]) * 1024
+    write = float(rec["write_size_kib"]) * float(rec["write_scale"]) * 1024
+    return int(round(fetch + write))
+
+
+def read_calibration(nbytes, ncopies, warmup, steps):
+    """A plain streaming read (tq_stream_read) of the same byte count, cold: cycled
+    through as many buffers as there are cache copies. The bandwidth a kernel
+    reading that much can reach on this device: the measured ceiling."""
+    import torch
+    import compressed_domain_decode_amd as tq
+    n16 = max(1, nbytes // 16)
+    bufs = [torch.ones(n16 * 4, dtype=torch.int32, device="cuda:0") for _ in range(ncopies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for i in range(warmup):
+        tq.tq_stream_read(bufs[i % ncopies], sink)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        tq.tq_stream_read(bufs[i % ncopies], sink)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    del bufs
+    return {"kernel": "stream_read_kernel (tq_stream_read)", "bytes": n16 * 16,
+            "us_median": round(us, 3), "GBps": round(n16 * 16 / (us * 1e-6) / 1e9, 2)}
+
+
 class Hip:
     """hipEvent helpers through the HIP runtime (events on an explicit stream)."""
 
@@ -288,6 +339,7 @@ def main():
 
     alg_bytes = workloads.algorithmic_bytes(lengths_np, Hkv, d, wl.k_bits, wl.v_bits)
     ctx_tokens = int(lengths_np.sum())
+    read_cal = read_calibration(alg_bytes, ncopies, args.warmup, max(args.steps, 20))
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     result = {
@@ -320,10 +372,12 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "avg_us": round(split_avg_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": alg_bytes,
+            "frac_of_measured_read": round(achieved / read_cal["GBps"], 4),
         },
+        "read_calibration": read_cal,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

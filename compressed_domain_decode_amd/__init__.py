@@ -31,7 +31,7 @@ TQ_ERR_NOMEM = -5
 EXPORTED = (
     "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
     "tq_encode", "tq_attend_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
-    "tq_status_string", "tq_last_error", "tq_set_split_events",
+    "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
 )
 
 
@@ -76,6 +76,8 @@ _lib.tq_decode_attend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I, _P
                                   ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_decode_attend.restype = _I
 _lib.tq_set_split_events.argtypes = [_P, _P]
+_lib.tq_stream_read.restype = _I
+_lib.tq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.tq_set_split_events.restype = _I
 _lib.tq_status_string.argtypes = [_I]
 _lib.tq_status_string.restype = ctypes.c_char_p
@@ -236,6 +238,16 @@ def tq_set_split_events(before, after) -> None:
     """Record caller-owned hipEvent_t handles (ints) around the split-attend
     kernel of subsequent tq_decode_attend calls on this thread; None, None stops."""
     _check(_lib.tq_set_split_events(before, after))
+
+
+def tq_stream_read(buf, sink, stream=None) -> None:
+    """Measurement aid: a plain streaming read of the whole (contiguous, 16-byte
+    aligned) device tensor buf; sink is a device tensor of at least 4 bytes."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.tq_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
+                               ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
 
 
 def library_path() -> str:

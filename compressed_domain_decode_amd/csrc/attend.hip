@@ -45,6 +45,7 @@
 // 2. combine: log-sum-exp merge of the split partials, normalisation, inverse
 //    Walsh-Hadamard transform (cross-lane butterfly), sign flip, 1/d.
 #include <hip/hip_fp16.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -710,18 +711,26 @@ hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, int g
                         const void* q, const uint8_t* kc, const float* kn, const uint8_t* vc,
                         const float* vn, const int32_t* lengths, int max_ctx, int max_len,
                         float qscale, float* pacc, float* pml, const AttendTables& tabs,
-                        const SignArg& ksign, hipStream_t stream) {
-  hipLaunchKernelGGL((attend_split_kernel<C>), dim3(plan.splits, n_kv_heads, batch),
-                     dim3(64 * C::WAVES), 0, stream, (const __half*)q, kc, kn, vc, vn, lengths,
-                     n_kv_heads, group, max_ctx, max_len, plan.tokens_per_split, qscale, pacc,
-                     pml, tabs, ksign);
+                        const SignArg& ksign, hipEvent_t ev_start, hipEvent_t ev_stop,
+                        hipStream_t stream) {
+  const dim3 grid(plan.splits, n_kv_heads, batch), block(64 * C::WAVES);
+  if (ev_start) {
+    // events bound to this dispatch: they time the kernel itself, not the queue
+    hipExtLaunchKernelGGL((attend_split_kernel<C>), grid, block, 0, stream, ev_start, ev_stop, 0,
+                          (const __half*)q, kc, kn, vc, vn, lengths, n_kv_heads, group, max_ctx,
+                          max_len, plan.tokens_per_split, qscale, pacc, pml, tabs, ksign);
+  } else {
+    hipLaunchKernelGGL((attend_split_kernel<C>), grid, block, 0, stream, (const __half*)q, kc, kn,
+                       vc, vn, lengths, n_kv_heads, group, max_ctx, max_len,
+                       plan.tokens_per_split, qscale, pacc, pml, tabs, ksign);
+  }
   return hipGetLastError();
 }
 
 typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, int, const void*, const uint8_t*,
                               const float*, const uint8_t*, const float*, const int32_t*, int,
                               int, float, float*, float*, const AttendTables&, const SignArg&,
-                              hipStream_t);
+                              hipEvent_t, hipEvent_t, hipStream_t);
 
 struct SplitEntry {
   int d, bk, bv, nhg;
@@ -801,11 +810,9 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_q_hea
   float* pml = (float*)(ws + plan.part_acc_bytes);
   const float qscale = scale * kLog2e / (float)dim;
   hipError_t err;
-  if (ev_before && (err = hipEventRecord(ev_before, stream)) != hipSuccess) return err;
   err = ent->fn(plan, batch, n_kv_heads, group, q, k_codes, k_norms, v_codes, v_norms, lengths,
-                max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, stream);
+                max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, ev_before, ev_after, stream);
   if (err != hipSuccess) return err;
-  if (ev_after && (err = hipEventRecord(ev_after, stream)) != hipSuccess) return err;
   const dim3 cgrid(n_q_heads, batch);
   switch (dim) {
     case 64:

@@ -49,4 +49,7 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_q_hea
                          void* workspace, const AttendPlan& plan, hipEvent_t ev_before,
                          hipEvent_t ev_after, hipStream_t stream);
 
+// Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace tq

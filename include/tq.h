@@ -96,8 +96,8 @@ tq_status tq_encode(const tq_codec* c, const void* x_fp16, int n_tok, int n_head
                     int64_t c_stride_tok, int64_t c_stride_head, float* norms,
                     int64_t n_stride_tok, int64_t n_stride_head, void* stream);
 
-/* Workspace bytes tq_decode_attend needs for this shape (split partials and
- * the rotated queries). A pure function of its arguments; 0 on invalid input. */
+/* Workspace bytes tq_decode_attend needs for this shape (the per-split
+ * partial results). A pure function of its arguments; 0 on invalid input. */
 size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int dim,
                                  int max_len);
 
@@ -120,8 +120,8 @@ size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int d
  *               h / (n_q_heads / n_kv_heads).
  *   workspace:  device buffer of at least tq_attend_workspace_bytes(...) bytes,
  *               256-byte aligned; its contents need not be initialised.
- * Three kernels are enqueued (query rotation, split attend, combine + inverse
- * rotation). Results agree with softmax attention over the dequantised cache
+ * Two kernels are enqueued: split attend (the query rotation runs in its
+ * prologue) and combine + inverse rotation. Results agree with softmax attention over the dequantised cache
  * (computed in fp64) to about 1e-5 absolute for unit-scale inputs; fp32 sums
  * in a different order make the low bits differ from any serial evaluation.
  */
@@ -133,11 +133,20 @@ tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Measurement hook (per calling thread): while `before` and `after` are
- * non-NULL, each tq_decode_attend records the hipEvent_t `before` on its stream
- * immediately before the split-attend kernel and `after` immediately after it,
- * so a caller can time that kernel alone with hipEventElapsedTime. The events
- * are created and owned by the caller. Pass NULL, NULL to stop. */
+ * non-NULL, each tq_decode_attend launches its split-attend kernel with the
+ * hipEvent_t `before` and `after` bound to that dispatch (hipExtLaunchKernel
+ * start and stop events), so hipEventElapsedTime(before, after) is the
+ * kernel's own execution time. The events are created and owned by the
+ * caller. Pass NULL, NULL to stop. */
 tq_status tq_set_split_events(void* before, void* after);
+
+/* Measurement aid: enqueue a plain streaming read of `bytes` bytes at the
+ * device buffer buf (16-byte aligned, bytes a multiple of 16) on `stream`. It
+ * reads every byte once and writes nothing in practice (at most 4 bytes at
+ * sink, a caller-owned device word, for one input pattern), so its time is the
+ * read bandwidth the device reaches for a transfer of that size: the measured
+ * ceiling next to the nominal peak. bytes == 0 does nothing. */
+tq_status tq_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
 
 /* Number of context splits tq_decode_attend launches for this shape (for
  * measurement and tests); 0 on invalid input. */

@@ -156,3 +156,14 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+def test_stream_read_validation():
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    lib.tq_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tq_stream_read(None, 0, None, None) == tq.TQ_OK          # nothing to read
+    assert lib.tq_stream_read(None, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_stream_read(FAKE, 64, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_stream_read(FAKE + 8, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG  # alignment
+    assert lib.tq_stream_read(FAKE, 60, FAKE, None) == tq.TQ_ERR_INVALID_ARG      # size
+    assert "tq_stream_read" in tq.tq_last_error()
