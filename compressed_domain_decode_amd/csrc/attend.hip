@@ -162,8 +162,9 @@ struct CfgBase {
   static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights of a tile
   static constexpr int QS_BYTES = 4 * NHG * D * 4;      // rotated queries
   static constexpr int CEN_BYTES = 2 * 256 * 4;         // plain centroid tables while filling
+  static constexpr int GATE_BYTES = (WAVES * 4 + 15) / 16 * 16;  // first-tile arrival flags
   static constexpr int MAIN_BYTES =
-      VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + CEN_BYTES;
+      VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + CEN_BYTES + GATE_BYTES;
   static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * D) * 4;
   static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
@@ -186,7 +187,7 @@ constexpr int vgpr_estimate() {
 template <int D, int BK, int BV, int NHG>
 constexpr int cfg_waves() {
   using B = CfgBase<D, BK, BV, NHG, 4>;
-  constexpr int need = vgpr_estimate<B>() + 24;  // + addresses, temporaries
+  constexpr int need = vgpr_estimate<B>() + 28;  // + addresses, temporaries
   if (NHG < 4 && need <= 128 && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
   if (NHG < 4 && need <= 168 && CfgBase<D, BK, BV, NHG, 12>::LDS_BYTES <= kLdsPerCU) return 12;
   if (CfgBase<D, BK, BV, NHG, 8>::LDS_BYTES <= kLdsPerCU) return 8;
@@ -212,6 +213,46 @@ struct TileRegs {
 // is only moved when a tile's maximum exceeds it by more than this, so
 // weights stay below 2^8 and the rescale is rare.
 constexpr float kRescaleSlack = 8.f;
+
+// First tiles in flight per workgroup. Wavefronts 0 .. kGateDepth-1 request
+// their first tile at once; wavefront w >= kGateDepth requests its first tile
+// when the first tile of wavefront w - kGateDepth has arrived. Requested all at
+// once, every tile would share the memory pipeline and arrive only near the
+// end; gated, tiles arrive in order and the first ones are computed while the
+// later ones stream in. The gate only orders requests: a wavefront that waited
+// kGateSpins polls goes ahead anyway.
+constexpr int kGateDepth = 4;
+constexpr int kGateSpins = 1 << 16;
+
+// Flag word in LDS read and written with LDS instructions the compiler does not
+// order against vector memory, so polling never waits for this wavefront's own
+// outstanding row loads.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ int flag_read(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ void flag_write(uint32_t addr, int v) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// s_waitcnt on the vector-memory counter only (N outstanding at most).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS only: it does not wait for the caller's
+// outstanding global loads (tile rows requested before the barrier).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <class C>
 __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
@@ -239,6 +280,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   float* wbuf = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + wave * C::WB_BYTES);
   float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * (C::VS_BYTES + C::WB_BYTES));
   float* cen = wq + C::QS_BYTES / 4;
+  int* gate = (int*)(cen + C::CEN_BYTES / 4);
 
   const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_ctx;
   const uint32_t* __restrict__ kbase = (const uint32_t*)k_codes + kvrow0 * RKW;
@@ -313,14 +355,31 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   for (int w = 0; w < D / 32; ++w)
     if ((E * lane) >> 5 == w) sword = ksign.bits[w];
 
-  // ---- centroid tables: plain copies, then one replicated 256-byte row per
-  //      code (pair)
+  // ---- centroid tables: plain copies (the small loads are consumed before any
+  //      tile row is requested, so these waits cover only them), then one
+  //      replicated 256-byte row per code (pair)
 #pragma unroll
   for (int u = 0; u < kCenPer; ++u) {
     const int i = threadIdx.x + u * nthr;
     if (i < 512) cen[i] = cenv[u];
   }
-  __syncthreads();
+  float qf[kHeadsPerWave][E];
+#pragma unroll
+  for (int r = 0; r < kHeadsPerWave; ++r)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      qf[r][e] = __half2float(qx[r][e]);
+      asm volatile("" : "+v"(qf[r][e]) : : "memory");  // converted here, before the tile loads
+    }
+  if (threadIdx.x < WAVES) gate[threadIdx.x] = 0;
+
+  lds_barrier();
+  // the ungated wavefronts request their first tile now: every wavefront's
+  // small loads are done, and the rest of the prologue overlaps the transfer
+  constexpr int kStride = WAVES * kTile;
+  const int tile0 = t_begin + wave * kTile;
+  TileRegs<C> ra;
+  if (wave < kGateDepth) load_tile(tile0, ra);  // in bounds even without tiles (rows clamped)
   auto fill = [&](unsigned char* tab, const float* c, int bits, bool pair) {
     const int rows = 1 << (pair ? 2 * bits : bits);
     const int mask = (1 << bits) - 1;
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int j = E * lane + e;
-        const float x = __half2float(qx[r][e]);
+        const float x = qf[r][e];
         u[e] = ((sword >> (j & 31)) & 1u) ? -x : x;
       }
 #pragma unroll
@@ -368,7 +427,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       for (int e = 0; e < E; ++e) wq[h * D + E * lane + e] = u[e] * qscale;
     }
   }
-  __syncthreads();  // tables and rotated queries ready
+  lds_barrier();  // tables, rotated queries and gate flags ready
 
   // broadcast layout: lane 4c + v of VGPR Q[hg][m] holds q^[4 hg + v][16 m + c]
   float Q[NHG][D / 16];
@@ -379,13 +438,18 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < G ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
   }
 
-  // Only now the first tile. Once the memory pipeline is saturated a wavefront
-  // stalls in issuing vector loads, so no workgroup barrier may follow them
-  // until the merge: each wavefront runs its tiles independently.
-  constexpr int kStride = WAVES * kTile;
-  const int tile0 = t_begin + wave * kTile;
-  TileRegs<C> ra;
-  load_tile(tile0, ra);  // in bounds even for a wavefront without tiles (rows clamped)
+  // The gated wavefronts request their first tile once the first tile of
+  // wavefront w - kGateDepth has arrived. No workgroup barrier follows until
+  // the merge: a wavefront may stall in issuing vector loads while the memory
+  // pipeline is full, and each one runs its tiles independently.
+  if (wave >= kGateDepth) {
+    const uint32_t ga = lds_addr(gate + (wave - kGateDepth));
+    for (int i = 0; i < kGateSpins && flag_read(ga) == 0; ++i) __builtin_amdgcn_s_sleep(1);
+    load_tile(tile0, ra);
+  }
+  // this wavefront's first tile has arrived: open the gate of wavefront w + kGateDepth
+  wait_vmcnt<0>();
+  flag_write(lds_addr(gate + wave), 1);
 
   // ---- per-wave online-softmax state
   float m_run[NHG][4];
