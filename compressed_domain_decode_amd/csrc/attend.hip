@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 #include <utility>
 
 #include "kernels.hpp"
@@ -172,13 +173,22 @@ struct CfgBase {
 
 constexpr int kLdsPerCU = 163840;
 
+// Software-pipeline depths of the tile loop: K lookups per batch, tokens per
+// batch of the values phase.
+constexpr int kKBatch = 8;
+constexpr int kVBatch = 4;
+
 // Rough count of the VGPRs one lane holds through the tile loop: rotated
-// queries, the tile's rows and norms, value accumulators, score, weight and
-// softmax state, V field positions.
+// queries, norms, value accumulators, weight and softmax state, V field
+// positions, the V row being staged, plus the larger of the scores phase (the
+// K row, two batches of lookups, four accumulator chains) and the values
+// phase (three batches of staged dwords, two of lookups).
 template <class B>
 constexpr int vgpr_estimate() {
-  return B::NHG * B::D / 16 + B::RKW + B::RVW + 2 + B::NACC * B::NHG * 4 + B::NHG * 20 +
-         2 * B::NVS;
+  constexpr int base = B::NHG * B::D / 16 + 2 + B::NACC * B::NHG * 4 + B::NHG * 20 + 2 * B::NVS;
+  constexpr int kphase = B::RKW + 2 * kKBatch * (B::KPAIR ? 2 : 1) + 16 * B::NHG;
+  constexpr int vphase = 3 * kVBatch * B::NVS * 2 + 2 * kVBatch * B::NVS * (B::VPAIR ? 2 : 1);
+  return base + (kphase > vphase ? kphase : vphase);
 }
 
 // Wavefronts per workgroup: as many as the LDS and the register file allow
@@ -187,7 +197,7 @@ constexpr int vgpr_estimate() {
 template <int D, int BK, int BV, int NHG>
 constexpr int cfg_waves() {
   using B = CfgBase<D, BK, BV, NHG, 4>;
-  constexpr int need = vgpr_estimate<B>() + 28;  // + addresses, temporaries
+  constexpr int need = vgpr_estimate<B>() + 24;  // + addresses, temporaries
   if (NHG < 4 && need <= 128 && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
   if (NHG < 4 && need <= 168 && CfgBase<D, BK, BV, NHG, 12>::LDS_BYTES <= kLdsPerCU) return 12;
   if (CfgBase<D, BK, BV, NHG, 8>::LDS_BYTES <= kLdsPerCU) return 8;
@@ -489,43 +499,65 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int i = 0; i < RVW; i += 2)
       *(uint2*)(vstage + 2 + lane * RVW + i) = uint2{r.vw[i], r.vw[i + 1]};
 
-    // ---- scores on the matrix cores
-    v4f s0[NHG], s1[NHG];
+    // ---- scores on the matrix cores. The lookups of batch j + 1 are issued
+    //      before the products of batch j, so a batch's LDS latency hides
+    //      behind the previous batch's MFMAs; four accumulator chains.
+    using KLut = std::conditional_t<C::KPAIR, v2f, float>;
+    v4f sc[4][NHG];
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) {
-      s0[hg] = v4f{0.f, 0.f, 0.f, 0.f};
-      s1[hg] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg) sc[a4][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto k_lookup = [&](auto BI, KLut (&dst)[kKBatch]) __attribute__((always_inline)) {
+      sfor<kKBatch>([&](auto II) {
+        constexpr int f = BI * kKBatch + II;
+        constexpr int bit = C::KF * f;
+        uint32_t addr;
+        if constexpr (C::KF == 8) {
+          // whole byte: one byte permute builds (code << 8) | koff
+          addr = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
+                                       0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
+        } else {
+          addr = (field_at8<bit, C::KF>(r.kw) & KMASK) | koff;
+        }
+        dst[II] = *(const KLut*)(kt + addr);
+      });
+    };
+    auto k_mfma = [&](auto BI, const KLut (&src)[kKBatch]) __attribute__((always_inline)) {
+      sfor<kKBatch>([&](auto II) {
+        constexpr int f = BI * kKBatch + II;
+        if constexpr (C::KPAIR) {
+          constexpr int j0 = 2 * f, j1 = 2 * f + 1, a0 = 2 * (f % 2);
+#pragma unroll
+          for (int hg = 0; hg < NHG; ++hg) {
+            sc[a0][hg] = mfma_bcast<j0 % 16>(Q[hg][j0 / 16], src[II].x, sc[a0][hg]);
+            sc[a0 + 1][hg] = mfma_bcast<j1 % 16>(Q[hg][j1 / 16], src[II].y, sc[a0 + 1][hg]);
+          }
+        } else {
+#pragma unroll
+          for (int hg = 0; hg < NHG; ++hg)
+            sc[f % 4][hg] = mfma_bcast<f % 16>(Q[hg][f / 16], src[II], sc[f % 4][hg]);
+        }
+      });
+    };
+    {
+      constexpr int NKB = C::NKL / kKBatch;
+      KLut lb0[kKBatch], lb1[kKBatch];
+      k_lookup(std::integral_constant<int, 0>{}, lb0);
+      sfor<NKB>([&](auto BI) {
+        constexpr int bb = BI;
+        if constexpr (bb % 2 == 0) {
+          if constexpr (bb + 1 < NKB) k_lookup(std::integral_constant<int, bb + 1>{}, lb1);
+          k_mfma(BI, lb0);
+        } else {
+          if constexpr (bb + 1 < NKB) k_lookup(std::integral_constant<int, bb + 1>{}, lb0);
+          k_mfma(BI, lb1);
+        }
+      });
     }
-    sfor<C::NKL>([&](auto FI) {
-      constexpr int f = FI;
-      constexpr int bit = C::KF * f;
-      uint32_t addr;
-      if constexpr (C::KF == 8) {
-        // whole byte: one byte permute builds (code << 8) | koff
-        addr = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
-                                     0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
-      } else {
-        addr = (field_at8<bit, C::KF>(r.kw) & KMASK) | koff;
-      }
-      if constexpr (C::KPAIR) {
-        const v2f c = *(const v2f*)(kt + addr);
-        constexpr int j0 = 2 * f, j1 = 2 * f + 1;
+    v4f s0[NHG];
 #pragma unroll
-        for (int hg = 0; hg < NHG; ++hg) {
-          s0[hg] = mfma_bcast<j0 % 16>(Q[hg][j0 / 16], c.x, s0[hg]);
-          s1[hg] = mfma_bcast<j1 % 16>(Q[hg][j1 / 16], c.y, s1[hg]);
-        }
-      } else {
-        const float c = *(const float*)(kt + addr);
-#pragma unroll
-        for (int hg = 0; hg < NHG; ++hg) {
-          if constexpr (f % 2 == 0)
-            s0[hg] = mfma_bcast<f % 16>(Q[hg][f / 16], c, s0[hg]);
-          else
-            s1[hg] = mfma_bcast<f % 16>(Q[hg][f / 16], c, s1[hg]);
-        }
-      }
-    });
+    for (int hg = 0; hg < NHG; ++hg) s0[hg] = (sc[0][hg] + sc[1][hg]) + (sc[2][hg] + sc[3][hg]);
 
     const float nv_cur = r.nv;
     const float nk_cur = r.nk;
@@ -536,20 +568,20 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     // ---- online softmax (base 2) with a lazily moved maximum
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
-      const v4f s = (s0[hg] + s1[hg]) * nk_cur;
+      const v4f s = s0[hg] * nk_cur;
       v4f w;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float sv = valid ? s[v] : -INFINITY;
         const float mt = wave_max(sv);
         if (mt > m_run[hg][v] + kRescaleSlack) {  // wavefront-uniform
-          const float alpha = exp2f(m_run[hg][v] - mt);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
           l_run[hg][v] *= alpha;
 #pragma unroll
           for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
           m_run[hg][v] = mt;
         }
-        const float p = exp2f(sv - m_run[hg][v]);
+        const float p = __builtin_amdgcn_exp2f(sv - m_run[hg][v]);
         l_run[hg][v] += p;
         w[v] = p * nv_cur;
       }
@@ -565,30 +597,68 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       for (int m = 0; m < 4; ++m)
         Wr[hg][m] = wbuf[((16 * m + (lane >> 2)) * NHG + hg) * 4 + (lane & 3)];
 
-    // ---- values on the matrix cores, lanes over coordinates
-    sfor<kTile>([&](auto TI) {
-      constexpr int t = TI;
-      const uint32_t* row = vstage + t * RVW;
+    // ---- values on the matrix cores, lanes over coordinates. Three stages
+    //      over batches of tokens: the staged dwords around this lane's
+    //      fields (two batches ahead), the centroid lookups (one batch
+    //      ahead), the products.
+    using VLut = std::conditional_t<C::VPAIR, v2f, float>;
+    constexpr int TB = kVBatch, NTB = kTile / TB;
+    auto v_stage = [&](auto JI, uint2 (&dst)[TB][C::NVS]) __attribute__((always_inline)) {
+      sfor<TB>([&](auto TI) {
+        constexpr int t = JI * TB + TI;
+        const uint32_t* row = vstage + t * RVW;
 #pragma unroll
-      for (int k = 0; k < C::NVS; ++k) {
-        const uint32_t x = __builtin_amdgcn_alignbit(row[vdw[k] + 1], row[vdw[k]], vsh[k]);
-        const uint32_t addr = (x & VMASK) | voff;
-        if constexpr (C::VPAIR) {
-          const v2f c = *(const v2f*)(vt + addr);
+        for (int k = 0; k < C::NVS; ++k) dst[TI][k] = uint2{row[vdw[k]], row[vdw[k] + 1]};
+      });
+    };
+    auto v_lookup = [&](const uint2 (&xs)[TB][C::NVS], VLut (&dst)[TB][C::NVS]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int hg = 0; hg < NHG; ++hg) {
-            acc[2 * k][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], c.x, acc[2 * k][hg]);
-            acc[2 * k + 1][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], c.y, acc[2 * k + 1][hg]);
-          }
-        } else {
-          const float c = *(const float*)(vt + addr);
-          constexpr int par = (C::NVS == 1) ? (t & 1) : 0;
+      for (int tt = 0; tt < TB; ++tt)
 #pragma unroll
-          for (int hg = 0; hg < NHG; ++hg)
-            acc[k + par][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], c, acc[k + par][hg]);
+        for (int k = 0; k < C::NVS; ++k) {
+          const uint32_t x = __builtin_amdgcn_alignbit(xs[tt][k].y, xs[tt][k].x, vsh[k]);
+          dst[tt][k] = *(const VLut*)(vt + ((x & VMASK) | voff));
         }
-      }
-    });
+    };
+    auto v_mfma = [&](auto JI, const VLut (&cs)[TB][C::NVS]) __attribute__((always_inline)) {
+      sfor<TB>([&](auto TI) {
+        constexpr int t = JI * TB + TI;
+#pragma unroll
+        for (int k = 0; k < C::NVS; ++k) {
+          if constexpr (C::VPAIR) {
+#pragma unroll
+            for (int hg = 0; hg < NHG; ++hg) {
+              acc[2 * k][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], cs[TI][k].x, acc[2 * k][hg]);
+              acc[2 * k + 1][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], cs[TI][k].y, acc[2 * k + 1][hg]);
+            }
+          } else {
+            constexpr int par = (C::NVS == 1) ? (t & 1) : 0;
+#pragma unroll
+            for (int hg = 0; hg < NHG; ++hg)
+              acc[k + par][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], cs[TI][k], acc[k + par][hg]);
+          }
+        }
+      });
+    };
+    {
+      uint2 xs0[TB][C::NVS], xs1[TB][C::NVS], xs2[TB][C::NVS];
+      VLut cv0[TB][C::NVS], cv1[TB][C::NVS];
+      v_stage(std::integral_constant<int, 0>{}, xs0);
+      v_stage(std::integral_constant<int, 1>{}, xs1);
+      v_lookup(xs0, cv0);
+      // batch j: stage j + 2 into xs[(j + 2) % 3], look up j + 1 from xs[(j + 1) % 3]
+      // into cv[(j + 1) % 2], multiply batch j from cv[j % 2]
+      sfor<NTB>([&](auto JI) {
+        constexpr int j = JI;
+        auto& xs_next2 = (j + 2) % 3 == 0 ? xs0 : (j + 2) % 3 == 1 ? xs1 : xs2;
+        auto& xs_next1 = (j + 1) % 3 == 0 ? xs0 : (j + 1) % 3 == 1 ? xs1 : xs2;
+        auto& cv_next = (j + 1) % 2 == 0 ? cv0 : cv1;
+        auto& cv_cur = j % 2 == 0 ? cv0 : cv1;
+        if constexpr (j + 2 < NTB) v_stage(std::integral_constant<int, j + 2>{}, xs_next2);
+        if constexpr (j + 1 < NTB) v_lookup(xs_next1, cv_next);
+        v_mfma(JI, cv_cur);
+      });
+    }
     wave_lds_sync();
   };
 
