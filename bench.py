@@ -254,11 +254,14 @@ def main():
     footprint = B * Hkv * T * (kr + vr + 8)
     ncopies = 1 if args.cold_bytes <= 0 else max(2, math.ceil(args.cold_bytes / footprint))
 
+    def token_major(x, codes, norms, row, t0, t1):
+        """[t][b*h][...] views of tokens t0..t1 of a [B][Hkv][T][...] cache."""
+        return (x.view(B * Hkv, T, d).permute(1, 0, 2)[t0:t1],
+                codes.view(B * Hkv, T, row).permute(1, 0, 2)[t0:t1],
+                norms.view(B * Hkv, T).permute(1, 0)[t0:t1])
+
     def encode_into(codec, x, codes, norms, t0, t1):
-        xv = x.view(B * Hkv, T, d).permute(1, 0, 2)[t0:t1]
-        cv = codes.view(B * Hkv, T, codec.row_bytes).permute(1, 0, 2)[t0:t1]
-        nv = norms.view(B * Hkv, T).permute(1, 0)[t0:t1]
-        tq.tq_encode(codec, xv, cv, nv)
+        tq.tq_encode(codec, *token_major(x, codes, norms, codec.row_bytes, t0, t1))
 
     copies = []
     for i in range(ncopies):
@@ -278,9 +281,9 @@ def main():
 
     def step(i):
         kcd, knd, vcd, vnd = copies[i % ncopies]
-        if P:
-            encode_into(kc, k_dev, kcd, knd, T - P, T)
-            encode_into(vc, v_dev, vcd, vnd, T - P, T)
+        if P:  # append the pending batch to both caches in one launch
+            tq.tq_encode_kv(kc, *token_major(k_dev, kcd, knd, kr, T - P, T),
+                            vc, *token_major(v_dev, vcd, vnd, vr, T - P, T))
         tq.tq_decode_attend(kc, vc, q_dev, kcd, knd, vcd, vnd, lengths, max_len, scale, out, ws)
 
     stream = torch.cuda.current_stream()

@@ -30,7 +30,7 @@ TQ_ERR_NOMEM = -5
 # C symbols the header declares; the ABI test checks the library exports each.
 EXPORTED = (
     "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
-    "tq_encode", "tq_attend_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
+    "tq_encode", "tq_encode_kv", "tq_attend_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
 )
 
@@ -68,6 +68,17 @@ _lib.tq_row_bytes.argtypes = [_I, _I]
 _lib.tq_row_bytes.restype = _I
 _lib.tq_encode.argtypes = [_P, _P, _I, _I, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]
 _lib.tq_encode.restype = _I
+
+
+class _EncodeJob(ctypes.Structure):
+    """Mirror of tq_encode_job."""
+    _fields_ = [("codec", _P), ("x_fp16", _P), ("x_stride_tok", _I64), ("x_stride_head", _I64),
+                ("codes", _P), ("c_stride_tok", _I64), ("c_stride_head", _I64),
+                ("norms", _P), ("n_stride_tok", _I64), ("n_stride_head", _I64)]
+
+
+_lib.tq_encode_kv.argtypes = [ctypes.POINTER(_EncodeJob), ctypes.POINTER(_EncodeJob), _I, _I, _P]
+_lib.tq_encode_kv.restype = _I
 _lib.tq_attend_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.tq_attend_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_attend_num_splits.argtypes = [_I, _I, _I, _I, _I]
@@ -181,11 +192,7 @@ def tq_row_bytes(dim: int, bits: int) -> int:
 
 # ------------------------------------------------------------------ encode
 
-def tq_encode(codec: Codec, x, codes, norms, stream=None) -> None:
-    """Encode x[n_tok][n_head][dim] (fp16, any strides, last dim contiguous) into
-    codes[n_tok][n_head][row_bytes] (uint8) and norms[n_tok][n_head] (fp32).
-    Strides are read from the tensors, so views into a [B][H][T][...] cache
-    (e.g. cache[b].transpose(0, 1)[t0:t1]) encode in place."""
+def _encode_views(codec: Codec, x, codes, norms):
     n_tok, n_head, d = x.shape
     if d != codec.dim or x.stride(2) != 1:
         raise TQError(TQ_ERR_INVALID_ARG, "x must be [n_tok][n_head][dim] with contiguous dim")
@@ -193,9 +200,33 @@ def tq_encode(codec: Codec, x, codes, norms, stream=None) -> None:
         raise TQError(TQ_ERR_INVALID_ARG, "codes must be [n_tok][n_head][row_bytes], row contiguous")
     if tuple(norms.shape) != (n_tok, n_head):
         raise TQError(TQ_ERR_INVALID_ARG, "norms must be [n_tok][n_head]")
-    _check(_lib.tq_encode(codec.handle, _ptr(x), n_tok, n_head, x.stride(0), x.stride(1),
-                          _ptr(codes), codes.stride(0), codes.stride(1), _ptr(norms),
-                          norms.stride(0), norms.stride(1), _stream_ptr(stream)))
+    return _EncodeJob(codec.handle, _ptr(x), x.stride(0), x.stride(1), _ptr(codes),
+                      codes.stride(0), codes.stride(1), _ptr(norms), norms.stride(0),
+                      norms.stride(1))
+
+
+def tq_encode(codec: Codec, x, codes, norms, stream=None) -> None:
+    """Encode x[n_tok][n_head][dim] (fp16, any strides, last dim contiguous) into
+    codes[n_tok][n_head][row_bytes] (uint8) and norms[n_tok][n_head] (fp32).
+    Strides are read from the tensors, so views into a [B][H][T][...] cache
+    (e.g. cache[b].transpose(0, 1)[t0:t1]) encode in place."""
+    j = _encode_views(codec, x, codes, norms)
+    n_tok, n_head = x.shape[0], x.shape[1]
+    _check(_lib.tq_encode(j.codec, j.x_fp16, n_tok, n_head, j.x_stride_tok, j.x_stride_head,
+                          j.codes, j.c_stride_tok, j.c_stride_head, j.norms, j.n_stride_tok,
+                          j.n_stride_head, _stream_ptr(stream)))
+
+
+def tq_encode_kv(kc: Codec, k, k_codes, k_norms, vc: Codec, v, v_codes, v_norms,
+                 stream=None) -> None:
+    """tq_encode of K (with kc) and of V (with vc) in one launch; k and v have
+    the same [n_tok][n_head] grid, the other rules are tq_encode's."""
+    if tuple(k.shape[:2]) != tuple(v.shape[:2]):
+        raise TQError(TQ_ERR_INVALID_ARG, "k and v must share [n_tok][n_head]")
+    jk = _encode_views(kc, k, k_codes, k_norms)
+    jv = _encode_views(vc, v, v_codes, v_norms)
+    _check(_lib.tq_encode_kv(ctypes.byref(jk), ctypes.byref(jv), k.shape[0], k.shape[1],
+                             _stream_ptr(stream)))
 
 
 # ------------------------------------------------------------------ attend

@@ -46,6 +46,57 @@ tq::SignArg sign_arg(const tq_codec* c) {
   return s;
 }
 
+// Validate the jobs of one encode call and launch them together.
+tq_status encode_jobs(const char* fn, const tq_encode_job* jobs, int n_jobs, int n_tok,
+                      int n_head, void* stream) {
+  for (int i = 0; i < n_jobs; ++i) {
+    const tq_encode_job& j = jobs[i];
+    if (!j.codec) return fail(TQ_ERR_INVALID_ARG, "%s: codec %d is NULL", fn, i);
+    if (j.codec->tabs.dim != jobs[0].codec->tabs.dim)
+      return fail(TQ_ERR_INVALID_ARG, "%s: codecs of different dim (%d, %d)", fn,
+                  jobs[0].codec->tabs.dim, j.codec->tabs.dim);
+  }
+  if (n_tok < 0 || n_head < 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: negative count (n_tok %d, n_head %d)", fn, n_tok,
+                n_head);
+  if (n_tok == 0 || n_head == 0) return ok();
+  tq::EncodeArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_tok = n_tok;
+  args.n_head = n_head;
+  args.n_jobs = n_jobs;
+  for (int i = 0; i < n_jobs; ++i) {
+    const tq_encode_job& j = jobs[i];
+    if (!j.x_fp16 || !j.codes || !j.norms)
+      return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer in job %d", fn, i);
+    if (((uintptr_t)j.codes & 3) || (j.c_stride_tok & 3) || (j.c_stride_head & 3))
+      return fail(TQ_ERR_INVALID_ARG,
+                  "%s: codes pointer and strides must be multiples of 4 bytes (job %d)", fn, i);
+    if (((uintptr_t)j.x_fp16 & 1) || ((uintptr_t)j.norms & 3))
+      return fail(TQ_ERR_INVALID_ARG, "%s: misaligned x or norms pointer (job %d)", fn, i);
+    tq::EncodeJob& e = args.job[i];
+    e.x = j.x_fp16;
+    e.xs_tok = j.x_stride_tok;
+    e.xs_head = j.x_stride_head;
+    e.codes = j.codes;
+    e.cs_tok = j.c_stride_tok;
+    e.cs_head = j.c_stride_head;
+    e.norms = j.norms;
+    e.ns_tok = j.n_stride_tok;
+    e.ns_head = j.n_stride_head;
+    e.bits = j.codec->tabs.bits;
+    e.sign = sign_arg(j.codec);
+    std::memcpy(e.boundaries, j.codec->tabs.boundaries, sizeof(float) * ((1 << e.bits) - 1));
+  }
+  const long long nvec = (long long)n_tok * n_head;
+  if (nvec > 0x7fffffffLL - 64)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: more than 2^31 - 65 vectors", fn);
+  hipError_t err = tq::launch_encode(jobs[0].codec->tabs.dim, args, (hipStream_t)stream);
+  if (err != hipSuccess)
+    return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,29 +163,17 @@ tq_status tq_encode(const tq_codec* c, const void* x_fp16, int n_tok, int n_head
                     int64_t x_stride_tok, int64_t x_stride_head, uint8_t* codes,
                     int64_t c_stride_tok, int64_t c_stride_head, float* norms,
                     int64_t n_stride_tok, int64_t n_stride_head, void* stream) {
-  if (!c) return fail(TQ_ERR_INVALID_ARG, "tq_encode: codec is NULL");
-  if (n_tok < 0 || n_head < 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_encode: negative count (n_tok %d, n_head %d)", n_tok,
-                n_head);
-  if (n_tok == 0 || n_head == 0) return ok();
-  if (!x_fp16 || !codes || !norms) return fail(TQ_ERR_INVALID_ARG, "tq_encode: NULL pointer");
-  if (((uintptr_t)codes & 3) || (c_stride_tok & 3) || (c_stride_head & 3))
-    return fail(TQ_ERR_INVALID_ARG,
-                "tq_encode: codes pointer and strides must be multiples of 4 bytes");
-  if (((uintptr_t)x_fp16 & 1) || ((uintptr_t)norms & 3))
-    return fail(TQ_ERR_INVALID_ARG, "tq_encode: misaligned x or norms pointer");
-  const long long nvec = (long long)n_tok * n_head;
-  if ((nvec + 3) / 4 > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "tq_encode: too many vectors");
-  tq::EncodeTables tabs;
-  tabs.sign = sign_arg(c);
-  std::memcpy(tabs.boundaries, c->tabs.boundaries, sizeof(tabs.boundaries));
-  hipError_t err = tq::launch_encode(c->tabs.dim, c->tabs.bits, x_fp16, n_tok, n_head,
-                                     x_stride_tok, x_stride_head, codes, c_stride_tok,
-                                     c_stride_head, norms, n_stride_tok, n_stride_head, tabs,
-                                     (hipStream_t)stream);
-  if (err != hipSuccess)
-    return fail(TQ_ERR_HIP, "tq_encode: launch failed: %s", hipGetErrorString(err));
-  return ok();
+  const tq_encode_job job = {c,     x_fp16,       x_stride_tok, x_stride_head,
+                             codes, c_stride_tok, c_stride_head, norms,
+                             n_stride_tok, n_stride_head};
+  return encode_jobs("tq_encode", &job, 1, n_tok, n_head, stream);
+}
+
+tq_status tq_encode_kv(const tq_encode_job* k, const tq_encode_job* v, int n_tok, int n_head,
+                       void* stream) {
+  if (!k || !v) return fail(TQ_ERR_INVALID_ARG, "tq_encode_kv: job is NULL");
+  const tq_encode_job jobs[2] = {*k, *v};
+  return encode_jobs("tq_encode_kv", jobs, 2, n_tok, n_head, stream);
 }
 
 tq_status tq_set_split_events(void* before, void* after) {

@@ -11,17 +11,38 @@
 //   idx_j = #{k : beta_k < z_j}       (boundary count, the pages' boundary-sum)
 //   row = idx packed LSB-first, bit k of idx_j at stream bit bits*j + k
 //
-// Mapping: one 64-lane wavefront per vector; lane l owns the E = d/64
-// contiguous coordinates E*l .. E*l+E-1. In-lane butterfly stages first, then
-// cross-lane stages through __shfl_xor (DPP / ds_swizzle). The norm's tree is
-// the in-lane pairwise sum followed by an xor-butterfly with ascending lane
-// masks, which is the canonical tree evaluated in every lane (fp add is
-// commutative, so the partner order does not matter). Packing: lane l's E
-// codes form an E*bits-bit chunk at stream offset E*bits*l; output lane w
-// gathers the chunks that overlap dword w with wavefront shuffles and stores
-// one dword, so a row is written with coalesced 4-byte stores.
+// Mapping: L lanes per vector, lane s owning the E = d/L consecutive
+// coordinates E*s .. E*s+E-1; a wavefront holds 64/L vectors. Two layouts:
+//   wide    L = 64 (E = d/64): the most lanes per vector, for the short
+//           latency-bound launches of a cache append (a few hundred vectors);
+//   narrow  L = d/8 (E = 8): the least cross-lane work per coordinate, for
+//           bulk encodes (prefill), where throughput decides.
+// The butterfly runs its in-lane stages first, then its cross-lane stages in
+// ascending lane-mask order, i.e. all stages in ascending bit order. The
+// norm's tree is the in-lane pairwise sum followed by an xor butterfly with
+// ascending lane masks: the canonical tree, evaluated in every lane of the
+// vector (fp addition is commutative, so the partner order does not matter).
+// Cross-lane exchanges are VALU operations only: DPP inside a 16-lane row for
+// lane masks 1, 2, 4, 8, and the gfx950 permlane swaps for masks 16 and 32.
+//
+// Boundary count: up to 15 boundaries (bits <= 4) are compared linearly from
+// scalar registers. Above that the count is split in two levels: 15 coarse
+// boundaries (every 2^(bits-4)-th, from scalar registers) select a cell, and
+// the 2^(bits-4) - 1 boundaries inside the cell are read from LDS in one round
+// and compared. Both give #{k : beta_k < z} exactly because beta is sorted.
+//
+// Packing: lane s's E codes form a CH = E*bits-bit chunk at stream bit CH*s.
+// The G = 8/gcd(CH, 8) lanes of a byte-aligned group OR their chunks together
+// (DPP tree), and the group's first lane stores the group's whole bytes.
+//
+// Several jobs (e.g. the K and V caches of one appended token batch) share a
+// launch: blockIdx.y selects the job, and the bit width is a block-uniform
+// run-time switch.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -30,163 +51,268 @@ namespace tq {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+// Below this many narrow-layout wavefronts (one per SIMD) the launch is
+// latency-bound and the wide layout is used.
+constexpr long long kNarrowMinWaves = 1024;
+// Vector indices of the last workgroup stay below 2^31.
+constexpr long long kMaxEncodeVectors = 0x7fffffffLL - 64;
 
-template <int D, int BITS>
-__global__ __launch_bounds__(256) void encode_kernel(
-    const __half* __restrict__ x, int n_tok, int n_head, long long xs_tok, long long xs_head,
-    uint8_t* __restrict__ codes, long long cs_tok, long long cs_head, float* __restrict__ norms,
-    long long ns_tok, long long ns_head, EncodeTables tabs) {
-  constexpr int E = D / 64;
-  constexpr int NB = (1 << BITS) - 1;
-  constexpr int CHUNK = E * BITS;          // bits per lane, <= 32
-  constexpr int NW = D * BITS / 32;        // output dwords per row
-  constexpr bool kSearch = BITS >= 5;      // binary search in LDS above 16 levels
-  __shared__ float s_bnd[kSearch ? 256 : 1];
-  if (kSearch) {
-    for (int i = threadIdx.x; i < NB; i += blockDim.x) s_bnd[i] = tabs.boundaries[i];
-    __syncthreads();
-  }
+// Value of lane (lane ^ M) for a 32-bit word, M a power of two below 64.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   const int lane = threadIdx.x & 63;
-  const long long nvec = (long long)n_tok * n_head;
-  const long long v = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (v >= nvec) return;
-  const int t = (int)(v / n_head);
-  const int h = (int)(v - (long long)t * n_head);
-
-  const __half* xv = x + (long long)t * xs_tok + (long long)h * xs_head + E * lane;
-  double u[E], sq[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const double xe = (double)__half2float(xv[e]);
-    const int j = E * lane + e;
-    const bool neg = (tabs.sign.bits[j >> 5] >> (j & 31)) & 1u;
-    u[e] = neg ? -xe : xe;
-    sq[e] = xe * xe;
-  }
-  // squared norm: canonical pairwise tree
-  double s;
-  if constexpr (E == 1) {
-    s = sq[0];
-  } else if constexpr (E == 2) {
-    s = sq[0] + sq[1];
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    // banks 1, 3 (lanes 4-7, 12-15 of a row) read lane - 4; banks 0, 2 read lane + 4
+    const uint32_t r = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xA, false);
+    return __builtin_amdgcn_update_dpp(r, v, 0x104, 0xF, 0x5, false);
+  } else if constexpr (M == 8) {
+    // banks 2, 3 (lanes 8-15 of a row) read lane - 8; banks 0, 1 read lane + 8
+    const uint32_t r = __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xC, false);
+    return __builtin_amdgcn_update_dpp(r, v, 0x108, 0xF, 0x3, false);
+  } else if constexpr (M == 16) {
+    // swap odd rows of the first copy with even rows of the second
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? p[0] : p[1];
   } else {
-    s = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    static_assert(M == 32, "lane mask");
+    // swap the upper half of the first copy with the lower half of the second
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? p[0] : p[1];
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
-  const double nrm = __builtin_sqrt(s);
+}
 
-  // Walsh-Hadamard butterfly, in-lane stages then cross-lane stages
-#pragma unroll
-  for (int hs = 1; hs < E; hs <<= 1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if ((e & hs) == 0) {
-        const double a = u[e], b = u[e + hs];
-        u[e] = a + b;
-        u[e + hs] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const double p = __shfl_xor(u[e], m);
-      u[e] = upper ? (p - u[e]) : (u[e] + p);
-    }
-  }
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  const uint32_t lo = xor_lane<M>((uint32_t)v);
+  const uint32_t hi = xor_lane<M>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
 
-  // boundary count and per-lane chunk of packed bits
-  uint32_t chunk = 0;
+template <int M>
+__device__ __forceinline__ double xor_lane_f64(double x) {
+  return __builtin_bit_cast(double, xor_lane64<M>(__builtin_bit_cast(uint64_t, x)));
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+// #{k : beta_k < z} over the job's 2^BITS - 1 sorted boundaries. Above 15
+// boundaries: two levels (kTwoLevel: 30 compares, one LDS round) or a binary
+// search over the LDS copy (BITS dependent LDS rounds, BITS compares).
+template <int BITS, bool kTwoLevel>
+__device__ __forceinline__ uint32_t count_below(double z, const EncodeJob& jb,
+                                                const float* s_bnd) {
+  if constexpr (BITS <= 4) {
+    uint32_t idx = 0;
+#pragma unroll
+    for (int k = 0; k < (1 << BITS) - 1; ++k) idx += ((double)jb.boundaries[k] < z) ? 1u : 0u;
+    return idx;
+  } else if constexpr (kTwoLevel) {
+    constexpr int S = 1 << (BITS - 4);  // boundaries per coarse cell, the last one coarse
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) c += ((double)jb.boundaries[k * S + S - 1] < z) ? 1u : 0u;
+    const float* cell = s_bnd + c * S;
+    uint32_t f = 0;
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) f += ((double)cell[i] < z) ? 1u : 0u;
+    return c * S + f;
+  } else {
+    uint32_t idx = 0;  // invariant: the first idx boundaries are below z
+#pragma unroll
+    for (int step = 1 << (BITS - 1); step > 0; step >>= 1)
+      if ((double)s_bnd[idx + step - 1] < z) idx += step;
+    return idx;
+  }
+}
+
+// Quantise this lane's E coordinates and store its share of the packed row.
+template <int E, int BITS>
+__device__ __forceinline__ void quantize_store(const double (&u)[E], double nrm, int sub,
+                                               const EncodeJob& jb, const float* s_bnd,
+                                               uint8_t* row) {
+  constexpr int CH = E * BITS;                          // chunk bits per lane, <= 64
+  constexpr int G = CH % 8 == 0 ? 1 : 8 / gcd_c(CH, 8);  // lanes per byte-aligned group
+  constexpr int NBY = G * CH / 8;                       // bytes a group stores
+  static_assert(G * CH <= 64, "group chunk fits 64 bits");
+  uint64_t chunk = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double z = (nrm == 0.0) ? 0.0 : u[e] / nrm;
-    uint32_t idx = 0;
-    if constexpr (kSearch) {
-#pragma unroll
-      for (int step = 1 << (BITS - 1); step > 0; step >>= 1)
-        if ((double)s_bnd[idx + step - 1] < z) idx += step;
-    } else {
-#pragma unroll
-      for (int k = 0; k < NB; ++k) idx += ((double)tabs.boundaries[k] < z) ? 1u : 0u;
-    }
-    chunk |= idx << (BITS * e);
+    chunk |= (uint64_t)count_below<BITS, (E <= 4)>(z, jb, s_bnd) << (BITS * e);
   }
-
-  // gather the chunks overlapping output dword w = lane
-  constexpr int R = 32 / CHUNK + 2;
-  const int w = lane < NW ? lane : 0;
-  const int l0 = (32 * w) / CHUNK;
-  uint32_t word = 0;
+  // OR-tree over the group: after the stage with mask m, every lane whose
+  // index is a multiple of 2m holds the chunks of its 2m lanes.
+  if constexpr (G >= 2) chunk |= xor_lane64<1>(chunk) << CH;
+  if constexpr (G >= 4) chunk |= xor_lane64<2>(chunk) << (2 * CH);
+  if constexpr (G >= 8) chunk |= xor_lane64<4>(chunk) << (4 * CH);
+  if (sub % G != 0) return;
+  uint8_t* dst = row + (sub / G) * NBY;
+  if constexpr (NBY % 4 == 0) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int src = l0 + r;
-    const uint32_t val = (uint32_t)__shfl((int)chunk, src < 64 ? src : 63);
-    const int off = CHUNK * src - 32 * w;
-    if (src < 64 && off < 32 && off > -CHUNK) word |= off >= 0 ? (val << off) : (val >> (-off));
+    for (int i = 0; i < NBY / 4; ++i) ((uint32_t*)dst)[i] = (uint32_t)(chunk >> (32 * i));
+  } else if constexpr (NBY % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < NBY / 2; ++i) ((uint16_t*)dst)[i] = (uint16_t)(chunk >> (16 * i));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBY; ++i) dst[i] = (uint8_t)(chunk >> (8 * i));
   }
-  if (lane < NW) {
-    uint32_t* row = (uint32_t*)(codes + (long long)t * cs_tok + (long long)h * cs_head);
-    row[lane] = word;
-  }
-  if (lane == 0) norms[(long long)t * ns_tok + (long long)h * ns_head] = (float)nrm;
 }
 
-template <int D, int BITS>
-hipError_t launch_one(const void* x, int n_tok, int n_head, int64_t xs_tok, int64_t xs_head,
-                      uint8_t* codes, int64_t cs_tok, int64_t cs_head, float* norms,
-                      int64_t ns_tok, int64_t ns_head, const EncodeTables& tabs,
-                      hipStream_t stream) {
-  const long long nvec = (long long)n_tok * n_head;
-  const long long blocks = (nvec + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((encode_kernel<D, BITS>), dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
-                     0, stream, (const __half*)x, n_tok, n_head, (long long)xs_tok,
-                     (long long)xs_head, codes, (long long)cs_tok, (long long)cs_head, norms,
-                     (long long)ns_tok, (long long)ns_head, tabs);
+template <int D, int L>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+  constexpr int E = D / L;     // coordinates per lane
+  constexpr int VPW = 64 / L;  // vectors per wavefront
+  static_assert(L >= 8 && L <= 64 && E >= 1 && E <= 8, "layout");
+  __shared__ float s_bnd[256];
+
+  const EncodeJob& jb = a.job[blockIdx.y];
+  // The scalars the first vector load depends on come in one round of scalar
+  // loads (the empty asm keeps the compiler from splitting it).
+  int n_tok = a.n_tok, n_head = a.n_head, bits = jb.bits;
+  uint32_t magic = a.head_magic, shift = a.head_shift;
+  long long xs_tok = jb.xs_tok, xs_head = jb.xs_head;
+  asm volatile("" : "+s"(n_tok), "+s"(n_head), "+s"(bits), "+s"(magic), "+s"(shift),
+               "+s"(xs_tok), "+s"(xs_head));
+
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & (L - 1);
+  const int nvec = n_tok * n_head;  // < 2^31 - 64, checked on the host
+  const int v = ((int)blockIdx.x * kWavesPerBlock + (int)(threadIdx.x >> 6)) * VPW + lane / L;
+  const bool live = v < nvec;  // whole vectors: the L lanes of a vector agree
+  // Lanes past the end read vector 0, so the load needs no branch (a branch
+  // would make the compiler wait for it before the boundary copy below).
+  const int vl = live ? v : 0;
+  const int t = (int)(((uint64_t)(uint32_t)vl * magic) >> shift);
+  const int h = vl - t * n_head;
+  const __half* xv = (const __half*)jb.x + (long long)t * xs_tok + (long long)h * xs_head + E * sub;
+  __half xh[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) xh[e] = xv[e];
+  uint32_t words[D / 32];
+#pragma unroll
+  for (int w = 0; w < D / 32; ++w) words[w] = jb.sign.bits[w];
+
+  if (bits >= 5) {  // block-uniform: LDS copy of the boundaries for the count
+    static_assert(64 * kWavesPerBlock >= 255, "one boundary per thread");
+    if ((int)threadIdx.x < (1 << bits) - 1) s_bnd[threadIdx.x] = jb.boundaries[threadIdx.x];
+    __syncthreads();
+  }
+  if (!live) return;
+
+  // signs of coordinates E*sub .. E*sub+E-1 (one word; E divides 32)
+  uint32_t sw = words[0];
+#pragma unroll
+  for (int w = 1; w < D / 32; ++w) sw = ((E * sub) >> 5 == w) ? words[w] : sw;
+  const uint32_t sgn = sw >> ((E * sub) & 31);
+  double xd[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) xd[e] = (double)__half2float(xh[e]);
+
+  double u[E], sq[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    u[e] = ((sgn >> e) & 1u) ? -xd[e] : xd[e];
+    sq[e] = xd[e] * xd[e];
+  }
+  // squared norm: canonical pairwise tree, in-lane levels then cross-lane
+#pragma unroll
+  for (int w = 1; w < E; w <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; i += 2 * w) sq[i] = sq[i] + sq[i + w];
+  double s = sq[0];
+  if constexpr (L > 1) s = s + xor_lane_f64<1>(s);
+  if constexpr (L > 2) s = s + xor_lane_f64<2>(s);
+  if constexpr (L > 4) s = s + xor_lane_f64<4>(s);
+  if constexpr (L > 8) s = s + xor_lane_f64<8>(s);
+  if constexpr (L > 16) s = s + xor_lane_f64<16>(s);
+  if constexpr (L > 32) s = s + xor_lane_f64<32>(s);
+  const double nrm = __builtin_sqrt(s);
+
+  // Walsh-Hadamard butterfly: in-lane stages, then cross-lane stages
+#pragma unroll
+  for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((e & hs) == 0) {
+        const double p = u[e], q = u[e + hs];
+        u[e] = p + q;
+        u[e + hs] = p - q;
+      }
+  auto cross = [&](auto mtag) __attribute__((always_inline)) {
+    constexpr int m = decltype(mtag)::value;
+    const bool upper = (sub & m) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double pv = xor_lane_f64<m>(u[e]);
+      u[e] = upper ? (pv - u[e]) : (u[e] + pv);
+    }
+  };
+  if constexpr (L > 1) cross(std::integral_constant<int, 1>{});
+  if constexpr (L > 2) cross(std::integral_constant<int, 2>{});
+  if constexpr (L > 4) cross(std::integral_constant<int, 4>{});
+  if constexpr (L > 8) cross(std::integral_constant<int, 8>{});
+  if constexpr (L > 16) cross(std::integral_constant<int, 16>{});
+  if constexpr (L > 32) cross(std::integral_constant<int, 32>{});
+
+  if (sub == 0) jb.norms[(long long)t * jb.ns_tok + (long long)h * jb.ns_head] = (float)nrm;
+  uint8_t* row = jb.codes + (long long)t * jb.cs_tok + (long long)h * jb.cs_head;
+  switch (bits) {
+    case 1: quantize_store<E, 1>(u, nrm, sub, jb, s_bnd, row); break;
+    case 2: quantize_store<E, 2>(u, nrm, sub, jb, s_bnd, row); break;
+    case 3: quantize_store<E, 3>(u, nrm, sub, jb, s_bnd, row); break;
+    case 4: quantize_store<E, 4>(u, nrm, sub, jb, s_bnd, row); break;
+    case 5: quantize_store<E, 5>(u, nrm, sub, jb, s_bnd, row); break;
+    case 6: quantize_store<E, 6>(u, nrm, sub, jb, s_bnd, row); break;
+    case 7: quantize_store<E, 7>(u, nrm, sub, jb, s_bnd, row); break;
+    default: quantize_store<E, 8>(u, nrm, sub, jb, s_bnd, row); break;
+  }
+}
+
+template <int D, int L>
+hipError_t launch_layout(EncodeArgs& a, hipStream_t stream) {
+  const long long nvec = (long long)a.n_tok * a.n_head;
+  const long long per_block = (long long)kWavesPerBlock * (64 / L);
+  const long long blocks = (nvec + per_block - 1) / per_block;
+  hipLaunchKernelGGL((encode_kernel<D, L>), dim3((unsigned)blocks, (unsigned)a.n_jobs),
+                     dim3(64 * kWavesPerBlock), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dim(int bits, const void* x, int n_tok, int n_head, int64_t xs_tok,
-                      int64_t xs_head, uint8_t* codes, int64_t cs_tok, int64_t cs_head,
-                      float* norms, int64_t ns_tok, int64_t ns_head, const EncodeTables& tabs,
-                      hipStream_t stream) {
-#define TQ_ENC_CASE(B)                                                                      \
-  case B:                                                                                   \
-    return launch_one<D, B>(x, n_tok, n_head, xs_tok, xs_head, codes, cs_tok, cs_head,     \
-                            norms, ns_tok, ns_head, tabs, stream);
-  switch (bits) {
-    TQ_ENC_CASE(1)
-    TQ_ENC_CASE(2)
-    TQ_ENC_CASE(3)
-    TQ_ENC_CASE(4)
-    TQ_ENC_CASE(5)
-    TQ_ENC_CASE(6)
-    TQ_ENC_CASE(7)
-    TQ_ENC_CASE(8)
-  }
-#undef TQ_ENC_CASE
-  return hipErrorInvalidValue;
+hipError_t launch_dim(EncodeArgs& a, hipStream_t stream) {
+  const long long vecs = (long long)a.n_tok * a.n_head * a.n_jobs;
+  const long long narrow_waves = (vecs + (64 / (D / 8)) - 1) / (64 / (D / 8));
+  if (narrow_waves < kNarrowMinWaves) return launch_layout<D, (D < 64 ? D : 64)>(a, stream);
+  return launch_layout<D, D / 8>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_encode(int dim, int bits, const void* x, int n_tok, int n_head,
-                         int64_t xs_tok, int64_t xs_head, uint8_t* codes, int64_t cs_tok,
-                         int64_t cs_head, float* norms, int64_t ns_tok, int64_t ns_head,
-                         const EncodeTables& tabs, hipStream_t stream) {
+hipError_t launch_encode(int dim, EncodeArgs& args, hipStream_t stream) {
+  if (args.n_jobs < 1 || args.n_jobs > kMaxEncodeJobs) return hipErrorInvalidValue;
+  if (args.n_tok < 1 || args.n_head < 1 ||
+      (long long)args.n_tok * args.n_head > kMaxEncodeVectors)
+    return hipErrorInvalidValue;
+  for (int i = 0; i < args.n_jobs; ++i)
+    if (args.job[i].bits < 1 || args.job[i].bits > 8) return hipErrorInvalidValue;
+  // Division by the invariant n_head through a multiply and shift (Granlund and
+  // Montgomery, "Division by invariant integers using multiplication", 1994):
+  // with l = ceil(log2 n_head) and m = ceil(2^(31+l) / n_head) < 2^32,
+  // floor(v * m / 2^(31+l)) = floor(v / n_head) for every 0 <= v < 2^31.
+  const uint64_t dv = (uint64_t)args.n_head;
+  uint32_t l = 0;
+  while ((1ull << l) < dv) ++l;
+  args.head_shift = 31 + l;
+  args.head_magic = (uint32_t)(((1ull << (31 + l)) + dv - 1) / dv);
   switch (dim) {
-    case 64:
-      return launch_dim<64>(bits, x, n_tok, n_head, xs_tok, xs_head, codes, cs_tok, cs_head,
-                            norms, ns_tok, ns_head, tabs, stream);
-    case 128:
-      return launch_dim<128>(bits, x, n_tok, n_head, xs_tok, xs_head, codes, cs_tok, cs_head,
-                             norms, ns_tok, ns_head, tabs, stream);
-    case 256:
-      return launch_dim<256>(bits, x, n_tok, n_head, xs_tok, xs_head, codes, cs_tok, cs_head,
-                             norms, ns_tok, ns_head, tabs, stream);
+    case 64: return launch_dim<64>(args, stream);
+    case 128: return launch_dim<128>(args, stream);
+    case 256: return launch_dim<256>(args, stream);
   }
   return hipErrorInvalidValue;
 }

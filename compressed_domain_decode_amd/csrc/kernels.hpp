@@ -11,9 +11,27 @@ namespace tq {
 struct SignArg {
   uint32_t bits[8];            // bit j set: sign_j = -1
 };
-struct EncodeTables {
+// One set of n_tok x n_head vectors to encode with one codec.
+struct EncodeJob {
+  const void* x;               // fp16; vector (t, h) at element t*xs_tok + h*xs_head
+  long long xs_tok, xs_head;
+  uint8_t* codes;              // row (t, h) at byte t*cs_tok + h*cs_head (4-byte aligned)
+  long long cs_tok, cs_head;
+  float* norms;                // norm (t, h) at element t*ns_tok + h*ns_head
+  long long ns_tok, ns_head;
+  int bits;
+  int pad_;
   SignArg sign;
-  float boundaries[256];
+  float boundaries[256];       // 2^bits - 1 used
+};
+constexpr int kMaxEncodeJobs = 2;
+struct EncodeArgs {
+  int n_tok, n_head;           // n_tok * n_head < 2^31
+  int n_jobs;                  // 1 .. kMaxEncodeJobs, all of the same dim
+  uint32_t head_magic;         // t = (v * head_magic) >> head_shift equals v / n_head
+  uint32_t head_shift;         //   for 0 <= v < 2^31 (set by launch_encode)
+  int pad_;
+  EncodeJob job[kMaxEncodeJobs];
 };
 struct AttendTables {
   float k_centroids[256];
@@ -33,10 +51,9 @@ AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int ma
 
 // Launchers: return hipSuccess or the launch error. Shapes are validated by
 // the caller (the C ABI layer) before these are reached.
-hipError_t launch_encode(int dim, int bits, const void* x, int n_tok, int n_head,
-                         int64_t xs_tok, int64_t xs_head, uint8_t* codes, int64_t cs_tok,
-                         int64_t cs_head, float* norms, int64_t ns_tok, int64_t ns_head,
-                         const EncodeTables& tabs, hipStream_t stream);
+// All jobs of one call go out in a single launch. Fails with
+// hipErrorInvalidValue if the grid would exceed 2^31 - 1 workgroups.
+hipError_t launch_encode(int dim, EncodeArgs& args, hipStream_t stream);
 
 bool attend_supported(int dim, int k_bits, int v_bits, int group);
 

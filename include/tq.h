@@ -96,6 +96,31 @@ tq_status tq_encode(const tq_codec* c, const void* x_fp16, int n_tok, int n_head
                     int64_t c_stride_tok, int64_t c_stride_head, float* norms,
                     int64_t n_stride_tok, int64_t n_stride_head, void* stream);
 
+/* One vector set of an encode call: a codec and the x / codes / norms arrays
+ * with their strides, exactly as the arguments of tq_encode. */
+typedef struct {
+  const tq_codec* codec;
+  const void* x_fp16;
+  int64_t x_stride_tok, x_stride_head;
+  uint8_t* codes;
+  int64_t c_stride_tok, c_stride_head;
+  float* norms;
+  int64_t n_stride_tok, n_stride_head;
+} tq_encode_job;
+
+/*
+ * Encode the K and V vectors of one appended token batch in a single launch
+ * (the PR's cache update appends keys and values together; one launch instead
+ * of two halves the fixed cost of a short append). k and v each describe
+ * n_tok x n_head vectors with the layout, alignment and exactness rules of
+ * tq_encode; their codecs must have the same dim and may differ in bits and
+ * seed. Results are identical to tq_encode(k) followed by tq_encode(v). The
+ * two jobs' outputs must not overlap. Errors as tq_encode, plus
+ * TQ_ERR_INVALID_ARG for a NULL job or codecs of different dim.
+ */
+tq_status tq_encode_kv(const tq_encode_job* k, const tq_encode_job* v, int n_tok, int n_head,
+                       void* stream);
+
 /* Workspace bytes tq_decode_attend needs for this shape (the per-split
  * partial results). A pure function of its arguments; 0 on invalid input. */
 size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int dim,

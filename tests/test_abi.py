@@ -113,6 +113,35 @@ def test_encode_validation():
     assert _lib.tq_encode(h, None, 0, 5, 0, 0, None, 0, 0, None, 0, 0, None) == tq.TQ_OK
 
 
+def test_encode_kv_validation():
+    kc = tq.tq_codec_init(128, 8, 1)
+    vc = tq.tq_codec_init(128, 3, 1)
+    other = tq.tq_codec_init(64, 3, 1)
+    J = tq._EncodeJob
+    P = ctypes.POINTER(J)
+    f = tq._lib.tq_encode_kv
+
+    def job(c, x=FAKE, codes=FAKE, cst=64, norms=FAKE):
+        return J(c.handle if c else None, x, 128, 128, codes, cst, cst, norms, 1, 1)
+
+    def call(k, v, n_tok=1, n_head=1):
+        return f(ctypes.byref(k) if k is not None else P(), ctypes.byref(v) if v is not None else P(),
+                 n_tok, n_head, None)
+
+    assert call(None, job(vc)) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(kc), None) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(None), job(vc)) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(kc), job(other)) == tq.TQ_ERR_INVALID_ARG      # dims differ
+    assert call(job(kc), job(vc), n_tok=-1) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(kc), job(vc, x=None)) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(kc), job(vc, codes=FAKE + 2)) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(kc, cst=66), job(vc)) == tq.TQ_ERR_INVALID_ARG
+    assert call(job(kc), job(vc, norms=FAKE + 2)) == tq.TQ_ERR_INVALID_ARG
+    assert "job 1" in tq.tq_last_error()
+    # nothing to do is fine and touches nothing
+    assert call(job(kc, x=None), job(vc, x=None), n_tok=0) == tq.TQ_OK
+
+
 def _attend_call(kc, vc, B=1, Hq=4, Hkv=2, max_ctx=256, max_len=256, ws=FAKE, ws_bytes=1 << 30,
                  q=FAKE, out=FAKE):
     return _lib.tq_decode_attend(kc.handle, vc.handle, q, B, Hq, Hkv, FAKE, FAKE, FAKE, FAKE,

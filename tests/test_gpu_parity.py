@@ -78,9 +78,8 @@ def to_dev(a):
 
 # ------------------------------------------------------------------ encode
 
-def _encode_inputs(d, seed):
+def _encode_inputs(d, seed, n=384):
     rng = np.random.default_rng(seed)
-    n = 384
     x = rng.standard_normal((n, 2, d)) * rng.uniform(1e-3, 50, size=(n, 1, 1))
     x[0] = 0.0                                   # zero vector
     x[1, 0] = 6e-8                               # fp16 subnormals only
@@ -123,6 +122,69 @@ def test_encode_strided_views_and_append():
     torch.cuda.synchronize()
     assert codes.cpu().numpy().tobytes() == oc.tobytes()
     assert norms.cpu().numpy().tobytes() == on.tobytes()
+
+
+def _bulk_layout_vectors(d):
+    """Vectors per launch from which the encoder uses its bulk layout (d/8 lanes
+    per vector): 1024 wavefronts of 512/d vectors. Smaller launches use one
+    64-lane wavefront per vector."""
+    return 1024 * (512 // d)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_encode_bulk_layout_matches_oracle(d, bits):
+    announce(f"encode bulk layout d={d} bits={bits}")
+    g, o = codecs(d, bits)
+    n = _bulk_layout_vectors(d) // 2 + 19          # 2 heads: just past the switch, ragged
+    x = _encode_inputs(d, d * 100 + bits, n=n)
+    codes, norms = gpu_encode_rows(g, x)
+    oc, on, _ = oracle.encode(o, x)
+    assert codes.tobytes() == oc.tobytes()
+    assert norms.tobytes() == on.tobytes()
+
+
+@pytest.mark.parametrize("d,kb,vb", [(128, 8, 3), (64, 3, 3), (256, 4, 6), (128, 1, 5), (64, 7, 2)])
+@pytest.mark.parametrize("T", [72, 1500])
+def test_encode_kv_matches_oracle(d, kb, vb, T):
+    """One launch for K and V (different bits and seeds) into [B][H][T][row]
+    cache views; T=72 runs the 64-lane layout, T=1500 the bulk layout. Then a
+    64-token append into cleared rows."""
+    announce(f"encode kv d={d} kb={kb} vb={vb} T={T}")
+    gk, ok = codecs(d, kb, 42)
+    gv, ov = codecs(d, vb, 7)
+    B, H, P = 2, 4, 64
+    rng = np.random.default_rng(d + kb * 10 + vb + T)
+    k = (rng.standard_normal((B, H, T, d)) * rng.uniform(0.01, 20, (B, H, T, 1))).astype(np.float16)
+    v = (rng.standard_normal((B, H, T, d)) * rng.uniform(0.01, 20, (B, H, T, 1))).astype(np.float16)
+    k[0, 1, 3] = 0.0
+    okc, okn, _ = oracle.encode(ok, k)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    kd, vd = to_dev(k), to_dev(v)
+    kc = torch.full((B, H, T, gk.row_bytes), 0xA5, dtype=torch.uint8, device=DEV)
+    vc = torch.full((B, H, T, gv.row_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+    kn = torch.full((B, H, T), -1.0, dtype=torch.float32, device=DEV)
+    vn = torch.full((B, H, T), -1.0, dtype=torch.float32, device=DEV)
+
+    def views(t0, t1):
+        tm = lambda a, row: a.view(B * H, T, *row).permute(1, 0, *range(2, 2 + len(row)))[t0:t1]
+        return (tm(kd, (d,)), tm(kc, (gk.row_bytes,)), tm(kn, ()),
+                tm(vd, (d,)), tm(vc, (gv.row_bytes,)), tm(vn, ()))
+
+    xk, ck, nk, xv, cv, nv = views(0, T)
+    tq.tq_encode_kv(gk, xk, ck, nk, gv, xv, cv, nv)
+    torch.cuda.synchronize()
+    for got, want in ((kc, okc), (kn, okn), (vc, ovc), (vn, ovn)):
+        assert got.cpu().numpy().tobytes() == want.tobytes()
+    kc[:, :, T - P:] = 0
+    vc[:, :, T - P:] = 0
+    kn[:, :, T - P:] = 0
+    vn[:, :, T - P:] = 0
+    xk, ck, nk, xv, cv, nv = views(T - P, T)
+    tq.tq_encode_kv(gk, xk, ck, nk, gv, xv, cv, nv)
+    torch.cuda.synchronize()
+    for got, want in ((kc, okc), (kn, okn), (vc, ovc), (vn, ovn)):
+        assert got.cpu().numpy().tobytes() == want.tobytes()
 
 
 @pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
