@@ -127,6 +127,29 @@ def read_calibration(nbytes, ncopies, warmup, steps):
             "us_median": round(us, 3), "GBps": round(n16 * 16 / (us * 1e-6) / 1e9, 2)}
 
 
+def graph_us_per_call(fn, ncalls, reps):
+    """Average time of one fn(i) call when ncalls of them are replayed as one
+    graph (the launch cost of a short kernel included, as in the step)."""
+    import torch
+    for i in range(ncalls):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(ncalls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * ncalls)
+
+
 class Hip:
     """hipEvent helpers through the HIP runtime (events on an explicit stream)."""
 
@@ -340,6 +363,47 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / n_steps
 
+    # ---- the step's phases on their own (graph replay, as in the step), and the
+    #      bulk encode of a whole cache (prefill), which is not part of the step
+    phases = None
+    if graph is not None:
+
+        def append_only(i):
+            kcd, knd, vcd, vnd = copies[i % ncopies]
+            tq.tq_encode_kv(kc, *token_major(k_dev, kcd, knd, kr, T - P, T),
+                            vc, *token_major(v_dev, vcd, vnd, vr, T - P, T))
+
+        def attend_only(i):
+            kcd, knd, vcd, vnd = copies[i % ncopies]
+            tq.tq_decode_attend(kc, vc, q_dev, kcd, knd, vcd, vnd, lengths, max_len, scale, out,
+                                ws)
+
+        reps = max(2, args.steps // (4 * ncopies))
+        phases = {"timing": "graph replay, per call",
+                  "append_encode_us": round(graph_us_per_call(append_only, ncopies, reps), 3) if P else 0.0,
+                  "attend_us": round(graph_us_per_call(attend_only, ncopies, reps), 3),
+                  "split_kernel_us": round(split_avg_ms * 1e3, 3)}
+        phases["combine_and_gaps_us"] = round(phases["attend_us"] - phases["split_kernel_us"], 3)
+    kcd, knd, vcd, vnd = copies[0]
+    nbulk = 5
+    eb0 = torch.cuda.Event(enable_timing=True)
+    eb1 = torch.cuda.Event(enable_timing=True)
+    encode_into(kc, k_dev, kcd, knd, 0, T)
+    encode_into(vc, v_dev, vcd, vnd, 0, T)
+    torch.cuda.synchronize()
+    eb0.record()
+    for _ in range(nbulk):
+        encode_into(kc, k_dev, kcd, knd, 0, T)
+        encode_into(vc, v_dev, vcd, vnd, 0, T)
+    eb1.record()
+    torch.cuda.synchronize()
+    bulk_us = eb0.elapsed_time(eb1) * 1e3 / nbulk
+    bulk_vectors = 2 * B * Hkv * T
+    bulk_bytes = B * Hkv * T * (2 * 2 * d + kr + vr + 8)  # fp16 in, codes and norms out
+    bulk = {"vectors": bulk_vectors, "us_per_cache": round(bulk_us, 2),
+            "vectors_per_s": round(bulk_vectors / (bulk_us * 1e-6), 1),
+            "GBps_in_plus_out": round(bulk_bytes / (bulk_us * 1e-6) / 1e9, 2)}
+
     alg_bytes = workloads.algorithmic_bytes(lengths_np, Hkv, d, wl.k_bits, wl.v_bits)
     ctx_tokens = int(lengths_np.sum())
     read_cal = read_calibration(alg_bytes, ncopies, args.warmup, max(args.steps, 20))
@@ -381,6 +445,8 @@ def main():
             "frac_of_measured_read": round(achieved / read_cal["GBps"], 4),
         },
         "read_calibration": read_cal,
+        "phases": phases,
+        "bulk_encode_kv": bulk,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
