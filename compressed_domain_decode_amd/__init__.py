@@ -30,7 +30,8 @@ TQ_ERR_NOMEM = -5
 # C symbols the header declares; the ABI test checks the library exports each.
 EXPORTED = (
     "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
-    "tq_encode", "tq_encode_kv", "tq_attend_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
+    "tq_encode", "tq_encode_kv", "tq_attend_workspace_bytes", "tq_decode_attend_multi",
+    "tq_attend_multi_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
 )
 
@@ -86,6 +87,11 @@ _lib.tq_attend_num_splits.restype = _I
 _lib.tq_decode_attend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
                                   ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_decode_attend.restype = _I
+_lib.tq_decode_attend_multi.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
+                                        ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_decode_attend_multi.restype = _I
+_lib.tq_attend_multi_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+_lib.tq_attend_multi_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_set_split_events.argtypes = [_P, _P]
 _lib.tq_stream_read.restype = _I
 _lib.tq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
@@ -263,6 +269,38 @@ def tq_decode_attend(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms
                                  _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), max_ctx,
                                  _ptr(lengths), int(max_len), float(scale), _ptr(out),
                                  _ptr(workspace), nbytes, _stream_ptr(stream)))
+
+
+def tq_attend_multi_workspace_bytes(batch: int, n_query_tokens: int, n_q_heads: int,
+                                    n_kv_heads: int, dim: int, max_len: int) -> int:
+    return int(_lib.tq_attend_multi_workspace_bytes(batch, n_query_tokens, n_q_heads,
+                                                    n_kv_heads, dim, max_len))
+
+
+def tq_decode_attend_multi(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms,
+                           lengths, max_len: int, scale: float, out, workspace,
+                           stream=None) -> None:
+    """q [B][S][Hq][d] fp16 (S query tokens, causal among themselves); out
+    [B][S][Hq][d] fp32; lengths count the cache rows including the S new
+    ones; the rest as tq_decode_attend."""
+    B, S, Hq, d = q.shape
+    Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
+    for name, t in (("q", q), ("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
+                    ("v_norms", v_norms), ("lengths", lengths), ("out", out),
+                    ("workspace", workspace)):
+        if not t.is_contiguous():
+            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
+       tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
+       tuple(v_norms.shape) != (B, Hkv, max_ctx) or tuple(out.shape) != (B, S, Hq, d) or \
+       tuple(lengths.shape) != (B,):
+        raise TQError(TQ_ERR_INVALID_ARG, "cache / output shapes disagree")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tq_decode_attend_multi(kc.handle, vc.handle, _ptr(q), B, S, Hq, Hkv,
+                                       _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                                       _ptr(v_norms), max_ctx, _ptr(lengths), int(max_len),
+                                       float(scale), _ptr(out), _ptr(workspace), nbytes,
+                                       _stream_ptr(stream)))
 
 
 def tq_set_split_events(before, after) -> None:

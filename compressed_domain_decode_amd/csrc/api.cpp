@@ -213,62 +213,103 @@ int tq_attend_num_splits(int batch, int n_q_heads, int n_kv_heads, int dim, int 
   return tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len).splits;
 }
 
+}  // extern "C"
+
+namespace {
+
+// tq_decode_attend (n_qtok == 1) and tq_decode_attend_multi share every check
+// and the launch.
+tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
+                        const void* q_fp16, int batch, int n_qtok, int n_q_heads,
+                        int n_kv_heads, const uint8_t* k_codes, const float* k_norms,
+                        const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                        const int32_t* lengths, int max_len, float scale, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
+  if (kc->tabs.dim != vc->tabs.dim)
+    return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim,
+                vc->tabs.dim);
+  const int dim = kc->tabs.dim;
+  if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_qtok <= 0)
+    return fail(TQ_ERR_INVALID_ARG,
+                "%s: batch %d, query tokens %d, heads %d/%d must be positive", fn, batch,
+                n_qtok, n_q_heads, n_kv_heads);
+  if (n_q_heads % n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d", fn, n_q_heads,
+                n_kv_heads);
+  if ((long long)(n_q_heads / n_kv_heads) * n_qtok > 16)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: group size %d x %d query tokens > 16", fn,
+                n_q_heads / n_kv_heads, n_qtok);
+  if (batch > 65535 || n_kv_heads > 65535)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: batch or kv heads above 65535", fn);
+  if (max_len <= 0 || max_len > max_ctx)
+    return fail(TQ_ERR_INVALID_ARG, "%s: need 1 <= max_len (%d) <= max_ctx (%d)", fn, max_len,
+                max_ctx);
+  if (!q_fp16 || !k_codes || !k_norms || !v_codes || !v_norms || !lengths || !out)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (((uintptr_t)k_codes & 15) || ((uintptr_t)v_codes & 15) || ((uintptr_t)k_norms & 3) ||
+      ((uintptr_t)v_norms & 3) || ((uintptr_t)out & 3) || ((uintptr_t)lengths & 3) ||
+      ((uintptr_t)q_fp16 & 1))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale is NaN", fn);
+  const int group = n_q_heads / n_kv_heads;
+  if (!tq::attend_supported(dim, kc->tabs.bits, vc->tabs.bits, group * n_qtok))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "%s: no kernel for dim %d, K %d-bit, V %d-bit, %d heads per KV head", fn, dim,
+                kc->tabs.bits, vc->tabs.bits, group * n_qtok);
+  const tq::AttendPlan plan =
+      tq::plan_attend(batch, n_q_heads * n_qtok, n_kv_heads, dim, max_len);
+  if ((long long)plan.splits > 0x7fffffffLL)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: context too long", fn);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(TQ_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
+                workspace ? workspace_bytes : (size_t)0, plan.total_bytes);
+  if ((uintptr_t)workspace & 255)
+    return fail(TQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  tq::AttendTables tabs;
+  std::memcpy(tabs.k_centroids, kc->tabs.centroids, sizeof(tabs.k_centroids));
+  std::memcpy(tabs.v_centroids, vc->tabs.centroids, sizeof(tabs.v_centroids));
+  hipError_t err = tq::launch_attend(dim, kc->tabs.bits, vc->tabs.bits, batch, n_qtok,
+                                     n_q_heads, n_kv_heads, q_fp16, sign_arg(kc), sign_arg(vc),
+                                     tabs, k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
+                                     max_len, scale, out, workspace, plan, g_split_before,
+                                     g_split_after, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
                            int batch, int n_q_heads, int n_kv_heads,
                            const uint8_t* k_codes, const float* k_norms,
                            const uint8_t* v_codes, const float* v_norms, int max_ctx,
                            const int32_t* lengths, int max_len, float scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: codec is NULL");
-  if (kc->tabs.dim != vc->tabs.dim)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: K dim %d != V dim %d", kc->tabs.dim,
-                vc->tabs.dim);
-  const int dim = kc->tabs.dim;
-  if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: batch %d, heads %d/%d must be positive",
-                batch, n_q_heads, n_kv_heads);
-  if (n_q_heads % n_kv_heads)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: %d query heads not a multiple of %d",
-                n_q_heads, n_kv_heads);
-  if (n_q_heads / n_kv_heads > 16)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attend: group size %d > 16",
-                n_q_heads / n_kv_heads);
-  if (batch > 65535 || n_kv_heads > 65535)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attend: batch or kv heads above 65535");
-  if (max_len <= 0 || max_len > max_ctx)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: need 1 <= max_len (%d) <= max_ctx (%d)",
-                max_len, max_ctx);
-  if (!q_fp16 || !k_codes || !k_norms || !v_codes || !v_norms || !lengths || !out)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: NULL pointer");
-  if (((uintptr_t)k_codes & 15) || ((uintptr_t)v_codes & 15) || ((uintptr_t)k_norms & 3) ||
-      ((uintptr_t)v_norms & 3) || ((uintptr_t)out & 3) || ((uintptr_t)lengths & 3) ||
-      ((uintptr_t)q_fp16 & 1))
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: misaligned pointer");
-  if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: scale is NaN");
-  const int group = n_q_heads / n_kv_heads;
-  if (!tq::attend_supported(dim, kc->tabs.bits, vc->tabs.bits, group))
-    return fail(TQ_ERR_UNSUPPORTED,
-                "tq_decode_attend: no kernel for dim %d, K %d-bit, V %d-bit, group %d", dim,
-                kc->tabs.bits, vc->tabs.bits, group);
-  const tq::AttendPlan plan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
-  if ((long long)plan.splits > 0x7fffffffLL)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attend: context too long");
-  if (!workspace || workspace_bytes < plan.total_bytes)
-    return fail(TQ_ERR_WORKSPACE, "tq_decode_attend: workspace %zu bytes, need %zu",
-                workspace ? workspace_bytes : (size_t)0, plan.total_bytes);
-  if ((uintptr_t)workspace & 255)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attend: workspace must be 256-byte aligned");
-  tq::AttendTables tabs;
-  std::memcpy(tabs.k_centroids, kc->tabs.centroids, sizeof(tabs.k_centroids));
-  std::memcpy(tabs.v_centroids, vc->tabs.centroids, sizeof(tabs.v_centroids));
-  hipError_t err = tq::launch_attend(dim, kc->tabs.bits, vc->tabs.bits, batch, n_q_heads,
-                                     n_kv_heads, q_fp16, sign_arg(kc), sign_arg(vc), tabs,
-                                     k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
-                                     max_len, scale, out, workspace, plan, g_split_before,
-                                     g_split_after, (hipStream_t)stream);
-  if (err != hipSuccess)
-    return fail(TQ_ERR_HIP, "tq_decode_attend: launch failed: %s", hipGetErrorString(err));
-  return ok();
+  return decode_attend("tq_decode_attend", kc, vc, q_fp16, batch, 1, n_q_heads, n_kv_heads,
+                       k_codes, k_norms, v_codes, v_norms, max_ctx, lengths, max_len, scale,
+                       out, workspace, workspace_bytes, stream);
+}
+
+size_t tq_attend_multi_workspace_bytes(int batch, int n_query_tokens, int n_q_heads,
+                                       int n_kv_heads, int dim, int max_len) {
+  if (n_query_tokens <= 0 || (long long)n_q_heads * n_query_tokens > 0x7fffffffLL) return 0;
+  if (!attend_shape_ok(batch, n_q_heads, n_kv_heads, dim, max_len)) return 0;
+  return tq::plan_attend(batch, n_q_heads * n_query_tokens, n_kv_heads, dim, max_len)
+      .total_bytes;
+}
+
+tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                 int batch, int n_query_tokens, int n_q_heads, int n_kv_heads,
+                                 const uint8_t* k_codes, const float* k_norms,
+                                 const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                 const int32_t* lengths, int max_len, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_attend("tq_decode_attend_multi", kc, vc, q_fp16, batch, n_query_tokens,
+                       n_q_heads, n_kv_heads, k_codes, k_norms, v_codes, v_norms, max_ctx,
+                       lengths, max_len, scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

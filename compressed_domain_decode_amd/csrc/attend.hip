@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ k_codes,
     const float* __restrict__ k_norms, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ v_norms, const int32_t* __restrict__ lengths, int n_kv_heads,
-    int group, int max_ctx, int max_len, int tokens_per_split, float qscale,
+    int group, int n_qtok, int max_ctx, int max_len, int tokens_per_split, float qscale,
     float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign) {
   constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
   constexpr int RKW = C::RKW, RVW = C::RVW;
@@ -283,6 +283,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   const int t_end = min(len, t_begin + tokens_per_split);
   const int G = group;
   const int n_q_heads = n_kv_heads * G;
+  // The workgroup serves GV = G * n_qtok virtual heads: virtual head vh is
+  // query token vh / G of the sequence for query head g G + vh % G. Query
+  // token i of n_qtok sees the rows before len - n_qtok + i + 1 (causal
+  // multi-token decode); with one query token that is every row.
+  const int GV = G * n_qtok;
 
   unsigned char* vt = lds;
   unsigned char* kt = lds + C::VT_BYTES;
@@ -349,14 +354,16 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     const int i = threadIdx.x + u * nthr;
     cenv[u] = i < 256 ? tabs.v_centroids[i] : (i < 512 ? tabs.k_centroids[i - 256] : 0.f);
   }
-  constexpr int kHeadsPerWave = (4 * NHG + WAVES - 1) / WAVES;  // G <= 4 NHG
-  const __half* qb = q + ((long long)b * n_q_heads + (long long)g * G) * D;
+  constexpr int kHeadsPerWave = (4 * NHG + WAVES - 1) / WAVES;  // GV <= 4 NHG
   __half qx[kHeadsPerWave][E];
 #pragma unroll
   for (int r = 0; r < kHeadsPerWave; ++r) {
-    const int h = min(wave + r * WAVES, G - 1);  // in bounds; surplus rows unused
+    const int vh = min(wave + r * WAVES, GV - 1);  // in bounds; surplus rows unused
+    const int qi = vh / G;
+    const __half* qrow =
+        q + (((long long)b * n_qtok + qi) * n_q_heads + (long long)g * G + (vh - qi * G)) * D;
 #pragma unroll
-    for (int e = 0; e < E; ++e) qx[r][e] = qb[h * D + E * lane + e];
+    for (int e = 0; e < E; ++e) qx[r][e] = qrow[E * lane + e];
   }
   // sign word of this lane's coordinates E lane .. E lane + E - 1 (one word:
   // E <= 4 consecutive coordinates never straddle a 32-bit boundary)
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
   for (int r = 0; r < kHeadsPerWave; ++r) {
     const int h = wave + r * WAVES;
-    if (h < G) {
+    if (h < GV) {
       float u[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -445,7 +452,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 4 * hg + (lane & 3);
 #pragma unroll
-    for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < G ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
+    for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < GV ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
   }
 
   // The gated wavefronts request their first tile once the first tile of
@@ -460,6 +467,13 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   // this wavefront's first tile has arrived: open the gate of wavefront w + kGateDepth
   wait_vmcnt<0>();
   flag_write(lds_addr(gate + wave), 1);
+
+  // rows [0, vlim) are visible to virtual head 4 hg + v (wavefront-uniform)
+  int vlim[NHG][4];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) vlim[hg][v] = min(t_end, len - n_qtok + (4 * hg + v) / G + 1);
 
   // ---- per-wave online-softmax state
   float m_run[NHG][4];
@@ -492,7 +506,6 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   // One tile: scores, online softmax, values. `r` is consumed and refilled
   // with the wavefront's next tile as soon as its rows have been used.
   auto process = [&](int tile, TileRegs<C>& r) __attribute__((always_inline)) {
-    const bool valid = tile + lane < t_end;
 
     // stage this token's V row (row `lane`, after 2 dwords of padding)
 #pragma unroll
@@ -572,7 +585,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       v4f w;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float sv = valid ? s[v] : -INFINITY;
+        const float sv = tile + lane < vlim[hg][v] ? s[v] : -INFINITY;
         const float mt = wave_max(sv);
         if (mt > m_run[hg][v] + kRescaleSlack) {  // wavefront-uniform
           const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
@@ -581,7 +594,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
           for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
           m_run[hg][v] = mt;
         }
-        const float p = __builtin_amdgcn_exp2f(sv - m_run[hg][v]);
+        // a masked row weighs 0 (also before this head has seen any row)
+        const float p = sv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv - m_run[hg][v]);
         l_run[hg][v] += p;
         w[v] = p * nv_cur;
       }
@@ -721,10 +735,10 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WAVES) {
       const int v = idx / D, j = idx - v * D;
       const int h = 4 * hg + v;
-      if (h >= G) continue;
+      if (h >= GV) continue;
       float a = 0.f;
       for (int w = 0; w < WAVES; ++w) a += abuf[(w * 4 + v) * D + j];
-      const long long prow = ((long long)b * n_q_heads + (long long)g * G + h) * S + split;
+      const long long prow = (((long long)b * n_kv_heads + g) * GV + h) * S + split;
       part_acc[prow * D + j] = a;
       if (j == 0) {
         float M = -INFINITY, L = 0.f;
@@ -747,16 +761,22 @@ constexpr int kCombineUnroll = 4;  // splits per thread whose loads are in fligh
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ lengths, int max_len, int n_q_heads, int splits,
-    int tokens_per_split, float* __restrict__ out, SignArg sign) {
+    const int32_t* __restrict__ lengths, int max_len, int n_q_heads, int group, int n_qtok,
+    int splits, int tokens_per_split, float* __restrict__ out, SignArg sign) {
   constexpr int E = D / 64;
   constexpr int NG = kCombineThreads / D;  // split groups
   constexpr int U = kCombineUnroll;
   __shared__ float s_acc[NG][D];
   __shared__ float s_l[NG];
   const int tid = threadIdx.x;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const long long row = (long long)b * n_q_heads + h;
+  // partial row: virtual head hx = g GV + vh of sequence b; output row: query
+  // token vh / G, query head g G + vh % G
+  const int hx = blockIdx.x, b = blockIdx.y;
+  const int GV = group * n_qtok;
+  const long long row = (long long)b * n_q_heads * n_qtok + hx;
+  const int g = hx / GV, vh = hx - g * GV, qi = vh / group;
+  const long long orow =
+      ((long long)b * n_qtok + qi) * n_q_heads + (long long)g * group + (vh - qi * group);
   const int len = min(lengths[b], max_len);
   const int ns = len > 0 ? min(splits, (len + tokens_per_split - 1) / tokens_per_split) : 0;
   const float* ml = part_ml + row * splits * 2;
@@ -787,7 +807,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = s0 + u * NG < ns ? exp2f(mv[u] - M) : 0.f;
+      // a split where this head saw no row has maximum -inf and weighs 0
+      const float f = s0 + u * NG < ns && mv[u] != -INFINITY ? exp2f(mv[u] - M) : 0.f;
       a = fmaf(f, av[u], a);
       L = fmaf(f, lv[u], L);
     }
@@ -807,7 +828,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       float x = 0.f;
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) x += s_acc[g2][E * lane + e];
-      u[e] = ns > 0 ? x / Lt : 0.f;
+      u[e] = Lt > 0.f ? x / Lt : 0.f;  // no visible row: a zero output row
     }
     // inverse rotation: out = (1/d) sigma_V (.) H a
 #pragma unroll
@@ -833,7 +854,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int e = 0; e < E; ++e) {
       const int jj = E * lane + e;
       const float v = u[e] * invd;
-      out[row * D + jj] = ((sword >> (jj & 31)) & 1u) ? -v : v;
+      out[orow * D + jj] = ((sword >> (jj & 31)) & 1u) ? -v : v;
     }
   }
 }
@@ -842,7 +863,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 template <class C>
 hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, int group,
-                        const void* q, const uint8_t* kc, const float* kn, const uint8_t* vc,
+                        int n_qtok, const void* q, const uint8_t* kc, const float* kn,
+                        const uint8_t* vc,
                         const float* vn, const int32_t* lengths, int max_ctx, int max_len,
                         float qscale, float* pacc, float* pml, const AttendTables& tabs,
                         const SignArg& ksign, hipEvent_t ev_start, hipEvent_t ev_stop,
@@ -851,17 +873,18 @@ hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, int g
   if (ev_start) {
     // events bound to this dispatch: they time the kernel itself, not the queue
     hipExtLaunchKernelGGL((attend_split_kernel<C>), grid, block, 0, stream, ev_start, ev_stop, 0,
-                          (const __half*)q, kc, kn, vc, vn, lengths, n_kv_heads, group, max_ctx,
-                          max_len, plan.tokens_per_split, qscale, pacc, pml, tabs, ksign);
+                          (const __half*)q, kc, kn, vc, vn, lengths, n_kv_heads, group, n_qtok,
+                          max_ctx, max_len, plan.tokens_per_split, qscale, pacc, pml, tabs,
+                          ksign);
   } else {
     hipLaunchKernelGGL((attend_split_kernel<C>), grid, block, 0, stream, (const __half*)q, kc, kn,
-                       vc, vn, lengths, n_kv_heads, group, max_ctx, max_len,
+                       vc, vn, lengths, n_kv_heads, group, n_qtok, max_ctx, max_len,
                        plan.tokens_per_split, qscale, pacc, pml, tabs, ksign);
   }
   return hipGetLastError();
 }
 
-typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, int, const void*, const uint8_t*,
+typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, int, int, const void*, const uint8_t*,
                               const float*, const uint8_t*, const float*, const int32_t*, int,
                               int, float, float*, float*, const AttendTables&, const SignArg&,
                               hipEvent_t, hipEvent_t, hipStream_t);
@@ -879,13 +902,15 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(64, 4, 4, 1), TQ_SPLIT(64, 3, 3, 2), TQ_SPLIT(64, 3, 3, 1),
     TQ_SPLIT(64, 8, 3, 1), TQ_SPLIT(64, 2, 2, 1), TQ_SPLIT(64, 1, 1, 1),
     TQ_SPLIT(64, 5, 7, 1), TQ_SPLIT(64, 6, 6, 4), TQ_SPLIT(64, 4, 4, 2),
-    TQ_SPLIT(64, 8, 3, 2),
+    TQ_SPLIT(64, 8, 3, 2), TQ_SPLIT(64, 3, 3, 4),
     // head_dim 128
     TQ_SPLIT(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
     TQ_SPLIT(128, 4, 4, 1), TQ_SPLIT(128, 4, 3, 1), TQ_SPLIT(128, 2, 2, 1),
     TQ_SPLIT(128, 8, 4, 1), TQ_SPLIT(128, 4, 4, 2), TQ_SPLIT(128, 8, 3, 2),
     TQ_SPLIT(128, 1, 1, 1), TQ_SPLIT(128, 7, 5, 2),
     TQ_SPLIT(128, 3, 3, 2), TQ_SPLIT(128, 4, 2, 2),
+    // four query tokens of a group of 4 (multi-token decode)
+    TQ_SPLIT(128, 8, 3, 4), TQ_SPLIT(128, 3, 3, 4),
     // head_dim 256
     TQ_SPLIT(256, 4, 4, 1), TQ_SPLIT(256, 8, 3, 1), TQ_SPLIT(256, 3, 3, 1),
     TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2),
@@ -928,7 +953,7 @@ bool attend_supported(int dim, int k_bits, int v_bits, int group) {
   return find_split(dim, k_bits, v_bits, group) != nullptr;
 }
 
-hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_q_heads,
+hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok, int n_q_heads,
                          int n_kv_heads, const void* q, const SignArg& k_sign,
                          const SignArg& v_sign, const AttendTables& tabs,
                          const uint8_t* k_codes, const float* k_norms,
@@ -937,32 +962,33 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_q_hea
                          void* workspace, const AttendPlan& plan, hipEvent_t ev_before,
                          hipEvent_t ev_after, hipStream_t stream) {
   const int group = n_q_heads / n_kv_heads;
-  const SplitEntry* ent = find_split(dim, k_bits, v_bits, group);
+  const SplitEntry* ent = find_split(dim, k_bits, v_bits, group * n_qtok);
   if (!ent) return hipErrorInvalidValue;
   char* ws = (char*)workspace;
   float* pacc = (float*)ws;
   float* pml = (float*)(ws + plan.part_acc_bytes);
   const float qscale = scale * kLog2e / (float)dim;
   hipError_t err;
-  err = ent->fn(plan, batch, n_kv_heads, group, q, k_codes, k_norms, v_codes, v_norms, lengths,
-                max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, ev_before, ev_after, stream);
+  err = ent->fn(plan, batch, n_kv_heads, group, n_qtok, q, k_codes, k_norms, v_codes, v_norms,
+                lengths, max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, ev_before, ev_after,
+                stream);
   if (err != hipSuccess) return err;
-  const dim3 cgrid(n_q_heads, batch);
+  const dim3 cgrid(n_q_heads * n_qtok, batch);
   switch (dim) {
     case 64:
       hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
-                         lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
-                         v_sign);
+                         lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                         plan.tokens_per_split, out, v_sign);
       break;
     case 128:
       hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
-                         lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
-                         v_sign);
+                         lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                         plan.tokens_per_split, out, v_sign);
       break;
     case 256:
       hipLaunchKernelGGL(combine_kernel<256>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
-                         lengths, max_len, n_q_heads, plan.splits, plan.tokens_per_split, out,
-                         v_sign);
+                         lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                         plan.tokens_per_split, out, v_sign);
       break;
     default:
       return hipErrorInvalidValue;

@@ -57,7 +57,9 @@ hipError_t launch_encode(int dim, EncodeArgs& args, hipStream_t stream);
 
 bool attend_supported(int dim, int k_bits, int v_bits, int group);
 
-hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_q_heads,
+// n_qtok query tokens per sequence (q and out [batch][n_qtok][n_q_heads][dim]),
+// causal among themselves; plan sized for n_q_heads * n_qtok heads.
+hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok, int n_q_heads,
                          int n_kv_heads, const void* q, const SignArg& k_sign,
                          const SignArg& v_sign, const AttendTables& tabs,
                          const uint8_t* k_codes, const float* k_norms,

@@ -157,6 +157,36 @@ tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q
                            const int32_t* lengths, int max_len, float scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Multi-token decode: n_query_tokens new query rows per sequence attend the
+ * packed cache at once, causal among themselves (verifying a speculative
+ * draft, or a chunk of queries; PR #232's review threads on the multi-query
+ * NR0 attention path and on speculative decoding with draft tokens).
+ *   q_fp16: [batch][n_query_tokens][n_q_heads][dim] fp16, contiguous.
+ *   out:    [batch][n_query_tokens][n_q_heads][dim] fp32.
+ *   lengths[b] counts the cache rows of sequence b including the
+ *   n_query_tokens rows of the new tokens (already appended, e.g. with
+ *   tq_encode_kv). Query token i sees rows [0, lengths[b] - n_query_tokens +
+ *   i + 1), clamped to max_len; if that is empty its output row is zero.
+ *   Every other argument is as for tq_decode_attend, with a workspace of at
+ *   least tq_attend_multi_workspace_bytes(...) bytes. With n_query_tokens == 1
+ *   this is tq_decode_attend.
+ * Supported while (n_q_heads / n_kv_heads) * n_query_tokens <= 16 and a kernel
+ * is instantiated for that many heads per KV head (TQ_ERR_UNSUPPORTED
+ * otherwise).
+ */
+tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                 int batch, int n_query_tokens, int n_q_heads, int n_kv_heads,
+                                 const uint8_t* k_codes, const float* k_norms,
+                                 const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                 const int32_t* lengths, int max_len, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes tq_decode_attend_multi needs for this shape; 0 on invalid
+ * input. */
+size_t tq_attend_multi_workspace_bytes(int batch, int n_query_tokens, int n_q_heads,
+                                       int n_kv_heads, int dim, int max_len);
+
 /* Measurement hook (per calling thread): while `before` and `after` are
  * non-NULL, each tq_decode_attend launches its split-attend kernel with the
  * hipEvent_t `before` and `after` bound to that dispatch (hipExtLaunchKernel

@@ -215,3 +215,21 @@ def attend_rotated(kc, vc, q, k_codes, k_norms, v_codes, v_norms, lengths, scale
     """The same attention taken in the rotated basis (fp64)."""
     return _attend(_load().orc_attend_rotated, kc, vc, q, k_codes, k_norms, v_codes, v_norms,
                    lengths, scale, bh)
+
+
+def attend_causal_queries(kc, vc, q, k_codes, k_norms, v_codes, v_norms, lengths, scale=None):
+    """Multi-token decode (PR #232, review threads: the multi-query attention
+    path and speculative decoding with draft tokens): S query tokens per
+    sequence, causal among themselves. q: [B][S][Hq][d]; lengths[b] counts the
+    cache rows including the S new ones. Query token i of sequence b attends
+    the first lengths[b] - S + i + 1 rows (none if that is <= 0, a zero row).
+    That is S single-query decodes with those lengths, which is how it is
+    computed here. Returns [B][S][Hq][d] (fp64)."""
+    q = np.asarray(q)
+    B, S, Hq, d = q.shape
+    lengths = np.asarray(lengths, dtype=np.int64)
+    out = np.zeros((B, S, Hq, d), dtype=np.float64)
+    for i in range(S):
+        li = np.maximum(lengths - S + i + 1, 0).astype(np.int32)
+        out[:, i] = attend(kc, vc, q[:, i], k_codes, k_norms, v_codes, v_norms, li, scale)
+    return out

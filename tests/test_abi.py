@@ -167,6 +167,28 @@ def test_decode_attend_validation():
     assert "workspace" in tq.tq_last_error() or "aligned" in tq.tq_last_error()
 
 
+def test_decode_attend_multi_validation():
+    kc = tq.tq_codec_init(128, 8, 1)
+    vc = tq.tq_codec_init(128, 3, 1)
+    f = tq._lib.tq_decode_attend_multi
+
+    def call(S, Hq=32, Hkv=8, ws_bytes=1 << 30):
+        return f(kc.handle, vc.handle, FAKE, 1, S, Hq, Hkv, FAKE, FAKE, FAKE, FAKE, 256, FAKE,
+                 256, 0.125, FAKE, FAKE, ws_bytes, None)
+
+    assert call(0) == tq.TQ_ERR_INVALID_ARG
+    assert call(5) == tq.TQ_ERR_UNSUPPORTED          # 4 heads x 5 query tokens > 16
+    assert "query tokens" in tq.tq_last_error()
+    v5 = tq.tq_codec_init(128, 5, 1)                 # no K8/V5 kernel at all
+    assert f(kc.handle, v5.handle, FAKE, 1, 2, 32, 8, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 256,
+             0.125, FAKE, FAKE, 1 << 30, None) == tq.TQ_ERR_UNSUPPORTED
+    assert call(4, ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+    one = tq.tq_attend_workspace_bytes(1, 32, 8, 128, 4096)
+    assert tq.tq_attend_multi_workspace_bytes(1, 1, 32, 8, 128, 4096) == one
+    assert tq.tq_attend_multi_workspace_bytes(1, 4, 32, 8, 128, 4096) > one
+    assert tq.tq_attend_multi_workspace_bytes(1, 0, 32, 8, 128, 4096) == 0
+
+
 def test_workspace_and_split_plan():
     assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
     assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0

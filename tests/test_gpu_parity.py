@@ -360,3 +360,105 @@ def test_attend_workload_full_size_sampled(name):
     print(f"  {name}: worst max-abs err {worst:.3e} over {len(pairs)} sampled rows", flush=True)
     assert np.isfinite(got).all()
     assert worst <= ATOL
+
+
+# ------------------------------------------------------------------ multi-token decode
+
+def gpu_attend_multi(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np, max_len=None):
+    B, S, Hq, d = q_np.shape
+    Hkv = knorms.shape[1]
+    if max_len is None:
+        max_len = max(1, int(np.max(lengths_np)))
+    q = to_dev(q_np)
+    lengths = torch.from_numpy(np.asarray(lengths_np, dtype=np.int32)).to(DEV)
+    out = torch.full((B, S, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_attend_multi_workspace_bytes(B, S, Hq, Hkv, d, max_len),
+                     dtype=torch.uint8, device=DEV)
+    tq.tq_decode_attend_multi(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, max_len,
+                              1.0 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,kb,vb,G,S", [(128, 8, 3, 4, 2), (128, 8, 3, 4, 4), (128, 3, 3, 4, 3),
+                                         (64, 3, 3, 8, 2), (64, 4, 4, 2, 4), (128, 4, 2, 3, 2),
+                                         (64, 6, 6, 4, 4)])
+def test_attend_multi_matches_oracle(d, kb, vb, G, S):
+    """S causal query tokens per sequence: ragged lengths over several tiles and
+    splits, a sequence with exactly S rows and one with fewer rows than S (its
+    first query tokens see nothing: zero rows)."""
+    announce(f"attend multi d={d} kb={kb} vb={vb} G={G} S={S}")
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(d + 7 * kb + 13 * vb + 17 * G + S)
+    B, Hkv, T = 4, 2, 2500
+    Hq = G * Hkv
+    lengths = np.array([T, 1337, S, max(1, S - 2)])
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, S, Hq, d)).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    got = gpu_attend_multi(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths)
+    okc, okn, _ = oracle.encode(ok, k)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    want = oracle.attend_causal_queries(ok, ov, q, okc, okn, ovc, ovn, lengths)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= ATOL
+    invisible = np.maximum(lengths[3] - S + np.arange(S) + 1, 0) == 0
+    assert np.all(got[3][invisible] == 0.0)
+
+
+def test_attend_multi_one_token_equals_single_decode():
+    announce("attend multi S=1 vs single decode")
+    d, kb, vb, G = 128, 8, 3, 4
+    gk, _ = codecs(d, kb)
+    gv, _ = codecs(d, vb)
+    rng = np.random.default_rng(99)
+    B, Hkv, T = 2, 2, 3000
+    lengths = np.array([3000, 2049])
+    k = to_dev(rng.standard_normal((B, Hkv, T, d)).astype(np.float16))
+    v = to_dev(rng.standard_normal((B, Hkv, T, d)).astype(np.float16))
+    q = rng.standard_normal((B, 1, G * Hkv, d)).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(gk, k)
+    vcodes, vnorms = gpu_encode_cache(gv, v)
+    multi = gpu_attend_multi(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths)
+    single = gpu_attend(gk, gv, q[:, 0], kcodes, knorms, vcodes, vnorms, lengths)
+    assert multi[:, 0].tobytes() == single.tobytes()
+
+
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+def test_attend_multi_workload_full_size_sampled(name):
+    """The most query tokens (4, else 2) a multi-token kernel covers for each
+    workload at full size; sampled (sequence, KV head) units against the oracle."""
+    wl = workloads.WORKLOADS[name]
+    G = wl.n_q_heads // wl.n_kv_heads
+    gk, ok = codecs(wl.dim, wl.k_bits, wl.codec_seed)
+    gv, ov = codecs(wl.dim, wl.v_bits, wl.codec_seed)
+    inp = workloads.generate(wl)
+    rng = np.random.default_rng(5)
+    kc, kn = gpu_encode_cache(gk, to_dev(inp.k))
+    vc, vn = gpu_encode_cache(gv, to_dev(inp.v))
+    got = None
+    for S in (4, 2):
+        if G * S > 16:
+            continue
+        announce(f"attend multi full size {name} S={S}")
+        q = rng.standard_normal((wl.batch, S, wl.n_q_heads, wl.dim)).astype(np.float16)
+        try:
+            got = gpu_attend_multi(gk, gv, q, kc, kn, vc, vn, inp.lengths)
+            break
+        except tq.TQError as e:
+            if e.status != tq.TQ_ERR_UNSUPPORTED:
+                raise
+    assert got is not None, "no multi-token kernel for this workload"
+    del kc, kn, vc, vn
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)]
+    pick = [units[i] for i in rng.choice(len(units), size=min(3, len(units)), replace=False)]
+    for b, g in pick:
+        L = int(inp.lengths[b])
+        okc, okn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L])
+        ovc, ovn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L])
+        qs = q[b:b + 1, :, g * G:(g + 1) * G]
+        want = oracle.attend_causal_queries(ok, ov, qs, okc, okn, ovc, ovn, np.array([L]))
+        assert np.max(np.abs(got[b:b + 1, :, g * G:(g + 1) * G] - want)) <= ATOL

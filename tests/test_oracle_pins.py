@@ -397,3 +397,61 @@ def test_rows_beyond_length_are_ignored():
     knorms2[0, :, 23:] = np.nan
     b = oracle.attend(kc, vc, q, kcodes2, knorms2, vcodes, vnorms, lengths)
     np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------------------------ multi-token decode
+
+def _causal_mask_attention(q, k_hat, v_hat, lengths, group, scale):
+    """Brute force with an explicit (query token, row) mask: query token i of
+    S sits at position lengths[b] - S + i and sees the rows at or before it."""
+    B, S, Hq, d = q.shape
+    T = k_hat.shape[2]
+    out = np.zeros((B, S, Hq, d))
+    for b in range(B):
+        for i in range(S):
+            pos = lengths[b] - S + i
+            visible = np.arange(T) <= pos
+            for h in range(Hq):
+                if not visible.any():
+                    continue
+                s = scale * (k_hat[b, h // group] @ q[b, i, h])
+                s = np.where(visible, s, -np.inf)
+                p = np.exp(s - s.max())
+                out[b, i, h] = (p / p.sum()) @ v_hat[b, h // group]
+    return out
+
+
+@pytest.mark.parametrize("d,kb,vb,G,S", [(8, 3, 2, 2, 3), (16, 8, 3, 4, 4), (8, 4, 4, 1, 2)])
+def test_causal_queries_against_masked_brute_force(d, kb, vb, G, S):
+    rng = np.random.default_rng(d * 1000 + kb * 100 + vb * 10 + S)
+    B, Hkv, T = 3, 2, 9
+    Hq = G * Hkv
+    lengths = np.array([T, S, 1])            # full, exactly the new rows, fewer rows than S
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, S, Hq, d)).astype(np.float16)
+    kc, vc = oracle.Codec(d, kb, 3), oracle.Codec(d, vb, 4)
+    kcodes, knorms = _encode_cache(kc, k)
+    vcodes, vnorms = _encode_cache(vc, v)
+    k_hat = oracle.dequant(kc, kcodes, knorms)
+    v_hat = oracle.dequant(vc, vcodes, vnorms)
+    want = _causal_mask_attention(q.astype(np.float64), k_hat, v_hat, lengths, G, 1 / math.sqrt(d))
+    got = oracle.attend_causal_queries(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # sequence 2 has one row: only the last query token sees it
+    assert np.all(got[2, :S - 1] == 0.0) and np.any(got[2, S - 1] != 0.0)
+
+
+def test_one_query_token_is_the_single_decode():
+    rng = np.random.default_rng(11)
+    d, B, Hkv, G, T = 16, 2, 2, 2, 12
+    lengths = np.array([12, 5])
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, 1, G * Hkv, d)).astype(np.float16)
+    kc, vc = oracle.Codec(d, 4, 1), oracle.Codec(d, 3, 2)
+    kcodes, knorms = _encode_cache(kc, k)
+    vcodes, vnorms = _encode_cache(vc, v)
+    one = oracle.attend_causal_queries(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths)
+    ref = oracle.attend(kc, vc, q[:, 0], kcodes, knorms, vcodes, vnorms, lengths)
+    assert np.array_equal(one[:, 0], ref)
