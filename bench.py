@@ -384,6 +384,33 @@ def main():
                   "attend_us": round(graph_us_per_call(attend_only, ncopies, reps), 3),
                   "split_kernel_us": round(split_avg_ms * 1e3, 3)}
         phases["combine_and_gaps_us"] = round(phases["attend_us"] - phases["split_kernel_us"], 3)
+
+    # ---- multi-token decode over the same cache: the most query tokens per
+    #      sequence the kernels cover for this group size (causal among them)
+    multi = None
+    G = Hq // Hkv
+    S_q = max([s_ for s_ in (4, 2) if G * s_ <= 16] or [0])
+    if graph is not None and S_q:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        q_m = torch.randn((B, S_q, Hq, d), generator=gen, device=dev).half()
+        out_m = torch.empty((B, S_q, Hq, d), dtype=torch.float32, device=dev)
+        ws_m = torch.empty(tq.tq_attend_multi_workspace_bytes(B, S_q, Hq, Hkv, d, max_len),
+                           dtype=torch.uint8, device=dev)
+
+        def multi_only(i):
+            kcd, knd, vcd, vnd = copies[i % ncopies]
+            tq.tq_decode_attend_multi(kc, vc, q_m, kcd, knd, vcd, vnd, lengths, max_len, scale,
+                                      out_m, ws_m)
+
+        try:
+            us = graph_us_per_call(multi_only, ncopies, max(2, args.steps // (4 * ncopies)))
+            multi = {"query_tokens": S_q, "attend_us": round(us, 3),
+                     "GBps": round(workloads.algorithmic_bytes(lengths_np, Hkv, d, wl.k_bits,
+                                                               wl.v_bits) / (us * 1e-6) / 1e9, 2),
+                     "query_tokens_per_s": round(B * S_q / (us * 1e-6), 1)}
+        except tq.TQError as e:  # no kernel for this many heads per KV head
+            multi = {"query_tokens": S_q, "unsupported": str(e)}
     kcd, knd, vcd, vnd = copies[0]
     nbulk = 5
     eb0 = torch.cuda.Event(enable_timing=True)
@@ -446,6 +473,7 @@ def main():
         },
         "read_calibration": read_cal,
         "phases": phases,
+        "multi_token_decode": multi,
         "bulk_encode_kv": bulk,
     }
     if not args.no_cpu_baseline:

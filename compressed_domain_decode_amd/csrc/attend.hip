@@ -232,6 +232,10 @@ constexpr float kRescaleSlack = 8.f;
 // later ones stream in. The gate only orders requests: a wavefront that waited
 // kGateSpins polls goes ahead anyway.
 constexpr int kGateDepth = 4;
+// Running maximum before a head has seen any row: finite, so a masked score
+// (-inf) weighs exp2(-inf - kNoRow) = 0 without a test, and the first visible
+// row always moves the maximum (its weight rescales the empty sums by 0).
+constexpr float kNoRow = -1e30f;
 constexpr int kGateSpins = 1 << 16;
 
 // Flag word in LDS read and written with LDS instructions the compiler does not
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   for (int hg = 0; hg < NHG; ++hg) {
     l_run[hg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < 4; ++v) m_run[hg][v] = -INFINITY;
+    for (int v = 0; v < 4; ++v) m_run[hg][v] = kNoRow;
 #pragma unroll
     for (int a = 0; a < C::NACC; ++a) acc[a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -594,8 +598,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
           for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
           m_run[hg][v] = mt;
         }
-        // a masked row weighs 0 (also before this head has seen any row)
-        const float p = sv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv - m_run[hg][v]);
+        const float p = __builtin_amdgcn_exp2f(sv - m_run[hg][v]);
         l_run[hg][v] += p;
         w[v] = p * nv_cur;
       }
@@ -709,7 +712,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int v = 0; v < 4; ++v) {
       float M = -INFINITY;
       for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[w * 4 * NHG + 4 * hg + v]);
-      fw[hg][v] = m_run[hg][v] == -INFINITY ? 0.f : exp2f(m_run[hg][v] - M);
+      // 0 for a wavefront that saw no row while another did (kNoRow - M)
+      fw[hg][v] = exp2f(m_run[hg][v] - M);
       if (lane == 0) mbuf[WAVES * 4 * NHG + wave * 4 * NHG + 4 * hg + v] = fw[hg][v] * lsum[hg][v];
     }
   const int S = gridDim.x;
