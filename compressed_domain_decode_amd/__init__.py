@@ -31,7 +31,7 @@ TQ_ERR_NOMEM = -5
 EXPORTED = (
     "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
     "tq_encode", "tq_encode_kv", "tq_attend_workspace_bytes", "tq_decode_attend_multi",
-    "tq_attend_multi_workspace_bytes", "tq_decode_attend", "tq_attend_num_splits",
+    "tq_attend_multi_workspace_bytes", "tq_decode_attend_mixed", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
 )
 
@@ -90,6 +90,10 @@ _lib.tq_decode_attend.restype = _I
 _lib.tq_decode_attend_multi.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
                                         ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_decode_attend_multi.restype = _I
+_lib.tq_decode_attend_mixed.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
+                                        _P, _P, _I, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                        _P]
+_lib.tq_decode_attend_mixed.restype = _I
 _lib.tq_attend_multi_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.tq_attend_multi_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_set_split_events.argtypes = [_P, _P]
@@ -301,6 +305,35 @@ def tq_decode_attend_multi(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v
                                        _ptr(v_norms), max_ctx, _ptr(lengths), int(max_len),
                                        float(scale), _ptr(out), _ptr(workspace), nbytes,
                                        _stream_ptr(stream)))
+
+
+def tq_decode_attend_mixed(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms,
+                           lengths, max_len: int, raw_k, raw_v, raw_lengths, scale: float, out,
+                           workspace, stream=None) -> None:
+    """tq_decode_attend over the packed rows plus raw fp16 rows raw_k / raw_v
+    [B][Hkv][max_raw][d] (raw_lengths int32[B] on the device); the softmax runs
+    over both. The rest as tq_decode_attend."""
+    B, Hq, d = q.shape
+    Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
+    for name, t in (("q", q), ("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
+                    ("v_norms", v_norms), ("lengths", lengths), ("out", out),
+                    ("workspace", workspace), ("raw_k", raw_k), ("raw_v", raw_v),
+                    ("raw_lengths", raw_lengths)):
+        if not t.is_contiguous():
+            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    max_raw = raw_k.shape[2]
+    if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
+       tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
+       tuple(v_norms.shape) != (B, Hkv, max_ctx) or tuple(out.shape) != (B, Hq, d) or \
+       tuple(lengths.shape) != (B,) or tuple(raw_k.shape) != (B, Hkv, max_raw, d) or \
+       tuple(raw_v.shape) != (B, Hkv, max_raw, d) or tuple(raw_lengths.shape) != (B,):
+        raise TQError(TQ_ERR_INVALID_ARG, "cache / raw segment / output shapes disagree")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tq_decode_attend_mixed(kc.handle, vc.handle, _ptr(q), B, Hq, Hkv, _ptr(k_codes),
+                                       _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), max_ctx,
+                                       _ptr(lengths), int(max_len), _ptr(raw_k), _ptr(raw_v),
+                                       max_raw, _ptr(raw_lengths), float(scale), _ptr(out),
+                                       _ptr(workspace), nbytes, _stream_ptr(stream)))
 
 
 def tq_set_split_events(before, after) -> None:

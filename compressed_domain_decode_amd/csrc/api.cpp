@@ -224,7 +224,8 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
                         int n_kv_heads, const uint8_t* k_codes, const float* k_norms,
                         const uint8_t* v_codes, const float* v_norms, int max_ctx,
                         const int32_t* lengths, int max_len, float scale, float* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, const tq::RawSegment& raw,
+                        void* stream) {
   if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
   if (kc->tabs.dim != vc->tabs.dim)
     return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim,
@@ -272,7 +273,7 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
   hipError_t err = tq::launch_attend(dim, kc->tabs.bits, vc->tabs.bits, batch, n_qtok,
                                      n_q_heads, n_kv_heads, q_fp16, sign_arg(kc), sign_arg(vc),
                                      tabs, k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
-                                     max_len, scale, out, workspace, plan, g_split_before,
+                                     max_len, scale, out, workspace, plan, raw, g_split_before,
                                      g_split_after, (hipStream_t)stream);
   if (err != hipSuccess) return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return ok();
@@ -290,7 +291,7 @@ tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q
                            void* workspace, size_t workspace_bytes, void* stream) {
   return decode_attend("tq_decode_attend", kc, vc, q_fp16, batch, 1, n_q_heads, n_kv_heads,
                        k_codes, k_norms, v_codes, v_norms, max_ctx, lengths, max_len, scale,
-                       out, workspace, workspace_bytes, stream);
+                       out, workspace, workspace_bytes, tq::RawSegment{}, stream);
 }
 
 size_t tq_attend_multi_workspace_bytes(int batch, int n_query_tokens, int n_q_heads,
@@ -309,7 +310,33 @@ tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const v
                                  void* workspace, size_t workspace_bytes, void* stream) {
   return decode_attend("tq_decode_attend_multi", kc, vc, q_fp16, batch, n_query_tokens,
                        n_q_heads, n_kv_heads, k_codes, k_norms, v_codes, v_norms, max_ctx,
-                       lengths, max_len, scale, out, workspace, workspace_bytes, stream);
+                       lengths, max_len, scale, out, workspace, workspace_bytes,
+                       tq::RawSegment{}, stream);
+}
+
+tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                 int batch, int n_q_heads, int n_kv_heads,
+                                 const uint8_t* k_codes, const float* k_norms,
+                                 const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                 const int32_t* lengths, int max_len, const void* raw_k_fp16,
+                                 const void* raw_v_fp16, int max_raw,
+                                 const int32_t* raw_lengths, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_decode_attend_mixed";
+  if (max_raw <= 0) return fail(TQ_ERR_INVALID_ARG, "%s: max_raw %d must be positive", fn, max_raw);
+  if (!raw_k_fp16 || !raw_v_fp16 || !raw_lengths)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL raw segment pointer", fn);
+  if (((uintptr_t)raw_k_fp16 & 15) || ((uintptr_t)raw_v_fp16 & 15) ||
+      ((uintptr_t)raw_lengths & 3))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned raw segment pointer", fn);
+  tq::RawSegment raw;
+  raw.k = raw_k_fp16;
+  raw.v = raw_v_fp16;
+  raw.lengths = raw_lengths;
+  raw.max_raw = max_raw;
+  return decode_attend(fn, kc, vc, q_fp16, batch, 1, n_q_heads, n_kv_heads, k_codes, k_norms,
+                       v_codes, v_norms, max_ctx, lengths, max_len, scale, out, workspace,
+                       workspace_bytes, raw, stream);
 }
 
 }  // extern "C"

@@ -49,6 +49,15 @@ struct AttendPlan {
 
 AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len);
 
+// Raw fp16 rows attended together with the packed cache (lengths == nullptr:
+// none). k and v are [batch][n_kv_heads][max_raw][dim], 16-byte aligned.
+struct RawSegment {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* lengths = nullptr;
+  int max_raw = 0;
+};
+
 // Launchers: return hipSuccess or the launch error. Shapes are validated by
 // the caller (the C ABI layer) before these are reached.
 // All jobs of one call go out in a single launch. Fails with
@@ -65,8 +74,8 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
                          const uint8_t* k_codes, const float* k_norms,
                          const uint8_t* v_codes, const float* v_norms, int max_ctx,
                          const int32_t* lengths, int max_len, float scale, float* out,
-                         void* workspace, const AttendPlan& plan, hipEvent_t ev_before,
-                         hipEvent_t ev_after, hipStream_t stream);
+                         void* workspace, const AttendPlan& plan, const RawSegment& raw,
+                         hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream);
 
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -144,7 +144,9 @@ size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int d
  *   out:        [batch][n_q_heads][dim] fp32. Query head h reads KV head
  *               h / (n_q_heads / n_kv_heads).
  *   workspace:  device buffer of at least tq_attend_workspace_bytes(...) bytes,
- *               256-byte aligned; its contents need not be initialised.
+ *               256-byte aligned; its contents need not be initialised. It
+ *               holds one partial per (sequence, query head, split) plus one
+ *               slot for a raw segment (tq_decode_attend_mixed).
  * Two kernels are enqueued: split attend (the query rotation runs in its
  * prologue) and combine + inverse rotation. Results agree with softmax attention over the dequantised cache
  * (computed in fp64) to about 1e-5 absolute for unit-scale inputs; fp32 sums
@@ -186,6 +188,32 @@ tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const v
  * input. */
 size_t tq_attend_multi_workspace_bytes(int batch, int n_query_tokens, int n_q_heads,
                                        int n_kv_heads, int dim, int max_len);
+
+/*
+ * Decode attention over the packed cache plus a segment of raw fp16 rows
+ * attended together with it: an fp16 prefix of "sink" tokens kept
+ * uncompressed (turboquant-mlx guide, --kv-min-tokens), or the pending tokens
+ * of a two-phase cache that are not yet batch-compressed (PR #232, Design).
+ * Softmax runs over the union of the packed rows [0, lengths[b]) and the raw
+ * rows [0, raw_lengths[b]) (their order does not matter to one query).
+ *   raw_k_fp16, raw_v_fp16: [batch][n_kv_heads][max_raw][dim] fp16,
+ *       contiguous, 16-byte aligned.
+ *   raw_lengths: device int32[batch]; values are clamped to max_raw on the
+ *       device; <= 0 means no raw rows for that sequence.
+ *   lengths[b] may be 0 (raw rows only); a sequence with no row at all gets
+ *   a zero output row.
+ * Every other argument is as for tq_decode_attend, with the same workspace
+ * size (tq_attend_workspace_bytes). Three kernels are enqueued: split attend,
+ * raw-segment attend, combine.
+ */
+tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                 int batch, int n_q_heads, int n_kv_heads,
+                                 const uint8_t* k_codes, const float* k_norms,
+                                 const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                 const int32_t* lengths, int max_len, const void* raw_k_fp16,
+                                 const void* raw_v_fp16, int max_raw,
+                                 const int32_t* raw_lengths, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Measurement hook (per calling thread): while `before` and `after` are
  * non-NULL, each tq_decode_attend launches its split-attend kernel with the

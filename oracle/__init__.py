@@ -233,3 +233,37 @@ def attend_causal_queries(kc, vc, q, k_codes, k_norms, v_codes, v_norms, lengths
         li = np.maximum(lengths - S + i + 1, 0).astype(np.int32)
         out[:, i] = attend(kc, vc, q[:, i], k_codes, k_norms, v_codes, v_norms, li, scale)
     return out
+
+
+def attend_mixed(kc, vc, q, k_codes, k_norms, v_codes, v_norms, lengths, raw_k, raw_v,
+                 raw_lengths, scale=None):
+    """Softmax attention over the union of the packed rows [0, lengths[b]) and
+    raw rows raw_k/raw_v [B][Hkv][R][d] [0, raw_lengths[b]) taken as they are:
+    an fp16 "sink" prefix kept uncompressed (turboquant-mlx guide,
+    --kv-min-tokens) or pending rows not yet batch-compressed (PR #232,
+    Design). Written out directly in fp64 over the dequantised packed rows.
+    q: [B][Hq][d]; returns [B][Hq][d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = np.asarray(k_norms).shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    k_hat = dequant(kc, k_codes, k_norms)
+    v_hat = dequant(vc, v_codes, v_norms)
+    rk = np.asarray(raw_k, dtype=np.float64)
+    rv = np.asarray(raw_v, dtype=np.float64)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L = max(int(lengths[b]), 0)
+        R = max(min(int(raw_lengths[b]), rk.shape[2]), 0)
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([k_hat[b, g, :L], rk[b, g, :R]])
+            vals = np.concatenate([v_hat[b, g, :L], rv[b, g, :R]])
+            if keys.shape[0] == 0:
+                continue
+            s = scale * (keys @ q[b, h])
+            p = np.exp(s - s.max())
+            out[b, h] = (p / p.sum()) @ vals
+    return out

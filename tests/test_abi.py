@@ -189,6 +189,23 @@ def test_decode_attend_multi_validation():
     assert tq.tq_attend_multi_workspace_bytes(1, 0, 32, 8, 128, 4096) == 0
 
 
+def test_decode_attend_mixed_validation():
+    kc = tq.tq_codec_init(128, 8, 1)
+    vc = tq.tq_codec_init(128, 3, 1)
+    f = tq._lib.tq_decode_attend_mixed
+
+    def call(rk=FAKE, rv=FAKE, max_raw=128, rlen=FAKE, ws_bytes=1 << 30):
+        return f(kc.handle, vc.handle, FAKE, 1, 32, 8, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 256,
+                 rk, rv, max_raw, rlen, 0.125, FAKE, FAKE, ws_bytes, None)
+
+    assert call(max_raw=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(rk=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(rlen=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(rv=FAKE + 8) == tq.TQ_ERR_INVALID_ARG           # raw rows 16-byte aligned
+    assert "raw" in tq.tq_last_error()
+    assert call(ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+
+
 def test_workspace_and_split_plan():
     assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
     assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0

@@ -462,3 +462,108 @@ def test_attend_multi_workload_full_size_sampled(name):
         qs = q[b:b + 1, :, g * G:(g + 1) * G]
         want = oracle.attend_causal_queries(ok, ov, qs, okc, okn, ovc, ovn, np.array([L]))
         assert np.max(np.abs(got[b:b + 1, :, g * G:(g + 1) * G] - want)) <= ATOL
+
+
+# ------------------------------------------------------------------ packed + raw fp16 rows
+
+def gpu_attend_mixed(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np, rk_np, rv_np,
+                     rlen_np, max_len=None):
+    B, Hq, d = q_np.shape
+    Hkv = knorms.shape[1]
+    if max_len is None:
+        max_len = max(1, int(np.max(lengths_np)))
+    lengths = torch.from_numpy(np.asarray(lengths_np, dtype=np.int32)).to(DEV)
+    rlen = torch.from_numpy(np.asarray(rlen_np, dtype=np.int32)).to(DEV)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, max_len), dtype=torch.uint8,
+                     device=DEV)
+    tq.tq_decode_attend_mixed(kc, vc, to_dev(q_np), kcodes, knorms, vcodes, vnorms, lengths,
+                              max_len, to_dev(rk_np), to_dev(rv_np), rlen, 1.0 / math.sqrt(d),
+                              out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,kb,vb,G", [(128, 8, 3, 4), (64, 4, 4, 2), (128, 4, 2, 3),
+                                       (256, 3, 3, 4), (64, 3, 3, 8)])
+def test_attend_mixed_matches_oracle(d, kb, vb, G):
+    """Packed rows plus raw fp16 rows: a 128-row sink prefix with a long packed
+    part, a short pending suffix (37 rows), raw rows only, and packed rows
+    only (raw length 0), with raw segments over more than one 64-row step."""
+    announce(f"attend mixed d={d} kb={kb} vb={vb} G={G}")
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(d + 3 * kb + 5 * vb + 7 * G)
+    B, Hkv, T, R = 4, 2, 2100, 150
+    Hq = G * Hkv
+    lengths = np.array([T, 1500, 0, 777])
+    rlen = np.array([128, 37, R, 0])
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    rk = (rng.standard_normal((B, Hkv, R, d)) * 1.5).astype(np.float16)
+    rv = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    got = gpu_attend_mixed(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv, rlen)
+    okc, okn, _ = oracle.encode(ok, k)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    want = oracle.attend_mixed(ok, ov, q, okc, okn, ovc, ovn, lengths, rk, rv, rlen)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= ATOL
+    # raw length 0: the same bits as the packed-only call
+    single = gpu_attend(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths)
+    assert got[3].tobytes() == single[3].tobytes()
+
+
+def test_attend_mixed_no_rows_is_zero_and_raw_clamped():
+    announce("attend mixed: no rows, raw length beyond max_raw")
+    d, kb, vb, G = 128, 8, 3, 4
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(3)
+    B, Hkv, T, R = 2, 1, 300, 70
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    rk = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    rv = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    q = rng.standard_normal((B, G * Hkv, d)).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    lengths, rlen = np.array([0, 300]), np.array([0, 1000])   # 1000 is clamped to R
+    got = gpu_attend_mixed(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv, rlen,
+                           max_len=T)
+    assert np.all(got[0] == 0.0)
+    okc, okn, _ = oracle.encode(ok, k)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    want = oracle.attend_mixed(ok, ov, q, okc, okn, ovc, ovn, lengths, rk, rv, np.array([0, R]))
+    assert np.max(np.abs(got[1] - want[1])) <= ATOL
+
+
+def test_attend_mixed_workload_sink_prefix_full_size():
+    """The 32K K8/V3 workload with its first 128 tokens kept as fp16 rows (the
+    guide's --kv-min-tokens 128): sampled KV heads against the oracle."""
+    wl = workloads.WORKLOADS["llama8b_32k_k8v3"]
+    announce(f"attend mixed full size {wl.name} sink 128")
+    G = wl.n_q_heads // wl.n_kv_heads
+    gk, ok = codecs(wl.dim, wl.k_bits, wl.codec_seed)
+    gv, ov = codecs(wl.dim, wl.v_bits, wl.codec_seed)
+    inp = workloads.generate(wl)
+    S = 128
+    kc, kn = gpu_encode_cache(gk, to_dev(np.ascontiguousarray(inp.k[:, :, S:])))
+    vc, vn = gpu_encode_cache(gv, to_dev(np.ascontiguousarray(inp.v[:, :, S:])))
+    rk = np.ascontiguousarray(inp.k[:, :, :S])
+    rv = np.ascontiguousarray(inp.v[:, :, :S])
+    lengths = inp.lengths - S
+    got = gpu_attend_mixed(gk, gv, inp.q, kc, kn, vc, vn, lengths, rk, rv,
+                           np.full(wl.batch, S, dtype=np.int32))
+    del kc, kn, vc, vn
+    rng = np.random.default_rng(8)
+    for g in rng.choice(wl.n_kv_heads, size=2, replace=False):
+        L = int(lengths[0])
+        okc, okn, _ = oracle.encode(ok, inp.k[0:1, g:g + 1, S:S + L])
+        ovc, ovn, _ = oracle.encode(ov, inp.v[0:1, g:g + 1, S:S + L])
+        want = oracle.attend_mixed(ok, ov, inp.q[0:1, g * G:(g + 1) * G], okc, okn, ovc, ovn,
+                                   np.array([L]), rk[0:1, g:g + 1], rv[0:1, g:g + 1],
+                                   np.array([S]))
+        assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL

@@ -455,3 +455,42 @@ def test_one_query_token_is_the_single_decode():
     one = oracle.attend_causal_queries(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths)
     ref = oracle.attend(kc, vc, q[:, 0], kcodes, knorms, vcodes, vnorms, lengths)
     assert np.array_equal(one[:, 0], ref)
+
+
+# ------------------------------------------------------------------ packed + raw fp16 rows
+
+@pytest.mark.parametrize("d,kb,vb,G", [(16, 4, 3, 2), (8, 8, 2, 1), (16, 3, 3, 4)])
+def test_mixed_segments_reduce_to_known_attention(d, kb, vb, G):
+    rng = np.random.default_rng(d * 31 + kb * 7 + vb + G)
+    B, Hkv, T, R = 3, 2, 10, 4
+    Hq = G * Hkv
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    kc, vc = oracle.Codec(d, kb, 8), oracle.Codec(d, vb, 9)
+    kcodes, knorms = _encode_cache(kc, k)
+    vcodes, vnorms = _encode_cache(vc, v)
+    lengths = np.array([T, 7, 0])
+    rk = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    rv = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    # no raw rows: the packed-cache attention
+    none = oracle.attend_mixed(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv,
+                               np.zeros(B, dtype=np.int32))
+    np.testing.assert_allclose(none, oracle.attend(kc, vc, q, kcodes, knorms, vcodes, vnorms,
+                                                   lengths), rtol=1e-12, atol=1e-13)
+    # rows moved from the packed cache to the raw segment, as their decoded
+    # values, leave the attention unchanged
+    k_hat = oracle.dequant(kc, kcodes, knorms)
+    v_hat = oracle.dequant(vc, vcodes, vnorms)
+    moved = oracle.attend_mixed(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths - 3 * (lengths > 3),
+                                k_hat[:, :, 4:7], v_hat[:, :, 4:7], np.array([0, 3, 0]))
+    np.testing.assert_allclose(moved[1], none[1], rtol=1e-12, atol=1e-13)
+    # raw rows only (sequence 2 has no packed row): plain attention over them
+    raw_only = oracle.attend_mixed(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv,
+                                   np.array([R, R, R]))
+    want = _brute_force_attention(q.astype(np.float64), rk.astype(np.float64),
+                                  rv.astype(np.float64), np.array([R] * B), G, 1 / math.sqrt(d))
+    np.testing.assert_allclose(raw_only[2], want[2], rtol=1e-12, atol=1e-13)
+    # neither: a zero row
+    assert np.all(oracle.attend_mixed(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv,
+                                      np.array([0, 0, 0]))[2] == 0.0)
