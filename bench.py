@@ -411,6 +411,27 @@ def main():
                      "query_tokens_per_s": round(B * S_q / (us * 1e-6), 1)}
         except tq.TQError as e:  # no kernel for this many heads per KV head
             multi = {"query_tokens": S_q, "unsupported": str(e)}
+
+    # ---- packed rows plus an fp16 sink prefix of 128 rows kept uncompressed
+    mixed = None
+    if graph is not None:
+        n_raw = min(128, T - 1)
+        raw_k = k_dev[:, :, :n_raw].contiguous()
+        raw_v = v_dev[:, :, :n_raw].contiguous()
+        raw_len = torch.full((B,), n_raw, dtype=torch.int32, device=dev)
+        packed_len = torch.from_numpy(np.maximum(lengths_np - n_raw, 0).astype(np.int32)).to(dev)
+        out_x = torch.empty_like(out)
+
+        def mixed_only(i):
+            kcd, knd, vcd, vnd = copies[i % ncopies]
+            tq.tq_decode_attend_mixed(kc, vc, q_dev, kcd, knd, vcd, vnd, packed_len, max_len,
+                                      raw_k, raw_v, raw_len, scale, out_x, ws)
+
+        us = graph_us_per_call(mixed_only, ncopies, max(2, args.steps // (4 * ncopies)))
+        mbytes = workloads.algorithmic_bytes(np.maximum(lengths_np - n_raw, 0), Hkv, d,
+                                             wl.k_bits, wl.v_bits) + B * Hkv * n_raw * 2 * d * 2
+        mixed = {"raw_rows": n_raw, "attend_us": round(us, 3),
+                 "GBps": round(mbytes / (us * 1e-6) / 1e9, 2)}
     kcd, knd, vcd, vnd = copies[0]
     nbulk = 5
     eb0 = torch.cuda.Event(enable_timing=True)
@@ -474,6 +495,7 @@ def main():
         "read_calibration": read_cal,
         "phases": phases,
         "multi_token_decode": multi,
+        "mixed_sink_decode": mixed,
         "bulk_encode_kv": bulk,
     }
     if not args.no_cpu_baseline:

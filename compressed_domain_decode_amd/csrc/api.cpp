@@ -324,6 +324,8 @@ tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const v
                                  void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "tq_decode_attend_mixed";
   if (max_raw <= 0) return fail(TQ_ERR_INVALID_ARG, "%s: max_raw %d must be positive", fn, max_raw);
+  if (max_raw > 4096)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: max_raw %d above 4096 raw rows", fn, max_raw);
   if (!raw_k_fp16 || !raw_v_fp16 || !raw_lengths)
     return fail(TQ_ERR_INVALID_ARG, "%s: NULL raw segment pointer", fn);
   if (((uintptr_t)raw_k_fp16 & 15) || ((uintptr_t)raw_v_fp16 & 15) ||

@@ -716,7 +716,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       fw[hg][v] = exp2f(m_run[hg][v] - M);
       if (lane == 0) mbuf[WAVES * 4 * NHG + wave * 4 * NHG + 4 * hg + v] = fw[hg][v] * lsum[hg][v];
     }
-  const int S = gridDim.x + 1;  // partial slots per head: the splits, then the raw segment
+  const int S = gridDim.x;
   sfor<NHG>([&](auto HGI) {
     constexpr int hg = HGI;
     __syncthreads();
@@ -757,138 +757,43 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   });
 }
 
-// ---------------------------------------------------------------- 1b. raw rows
-
-// Attention partial over a segment of raw fp16 rows: an fp16 prefix of
-// "sink" tokens kept uncompressed (turboquant-mlx guide, the --kv-min-tokens
-// option), or pending tokens not yet batch-compressed (PR #232, Design: batch
-// recompression). For every query head of one (sequence, KV head) it writes
-// the last partial slot: the running maximum and sum in the split kernel's
-// base-2 units, and the weighted sum of the V rows taken into the V codec's
-// rotated basis, H(sigma_V (.) sum_t p_t v_t), which the combine kernel's
-// inverse rotation brings back (H H = d I). One wavefront per query head; 64
-// rows per step, lane = row for the scores, lanes over coordinates for V.
-constexpr int kRawWaves = 4;
-
-template <int D>
-__global__ __launch_bounds__(64 * kRawWaves) void raw_attend_kernel(
-    const __half* __restrict__ q, const __half* __restrict__ raw_k,
-    const __half* __restrict__ raw_v, const int32_t* __restrict__ raw_lengths, int max_raw,
-    int n_kv_heads, int group, float qscale2, int splits, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, SignArg vsign) {
-  constexpr int E = D / 64;
-  __shared__ float qs[kRawWaves][D];   // the wavefront's query row, scaled
-  __shared__ float ps[kRawWaves][64];  // weights of the current 64 rows
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = min(raw_lengths[b], max_raw);
-  if (R <= 0) return;  // the combine does not read the slot
-  const int G = group, n_q_heads = n_kv_heads * G;
-  const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_raw;
-  const __half* __restrict__ kb = raw_k + kvrow0 * D;
-  const __half* __restrict__ vb = raw_v + kvrow0 * D;
-  uint32_t swords[D / 32];
-#pragma unroll
-  for (int w = 0; w < D / 32; ++w) swords[w] = vsign.bits[w];
-  uint32_t sword = swords[0];
-#pragma unroll
-  for (int w = 1; w < D / 32; ++w) sword = ((E * lane) >> 5 == w) ? swords[w] : sword;
-
-  for (int h = wave; h < G; h += kRawWaves) {
-    const __half* qr = q + ((long long)b * n_q_heads + (long long)g * G + h) * D;
-#pragma unroll
-    for (int e = 0; e < E; ++e) qs[wave][E * lane + e] = __half2float(qr[E * lane + e]) * qscale2;
-    wave_lds_sync();
-    float m = kNoRow, l = 0.f, acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int t0 = 0; t0 < R; t0 += 64) {
-      // scores: lane = row (rows past the end read the last row, masked)
-      const __half* kr = kb + (long long)min(t0 + lane, R - 1) * D;
-      float sc = 0.f;
-#pragma unroll 4
-      for (int j = 0; j < D; j += 8) {
-        const uint4 w8 = *(const uint4*)(kr + j);
-        const uint32_t wv[4] = {w8.x, w8.y, w8.z, w8.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const __half2 h2 = __builtin_bit_cast(__half2, wv[u]);
-          sc = fmaf(qs[wave][j + 2 * u], __low2float(h2), sc);
-          sc = fmaf(qs[wave][j + 2 * u + 1], __high2float(h2), sc);
-        }
-      }
-      const float sv = t0 + lane < R ? sc : -INFINITY;
-      const float mt = wave_max(sv);
-      if (mt > m) {  // wavefront-uniform
-        const float alpha = exp2f(m - mt);
-        l *= alpha;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] *= alpha;
-        m = mt;
-      }
-      const float p = exp2f(sv - m);
-      l += wave_sum(p);
-      ps[wave][lane] = p;
-      wave_lds_sync();
-      // values: lanes over coordinates
-      const int nt = min(64, R - t0);
-      const __half* vr = vb + (long long)t0 * D + E * lane;
-      for (int i = 0; i < nt; ++i) {
-        const float pi = ps[wave][i];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(pi, __half2float(vr[(long long)i * D + e]), acc[e]);
-      }
-      wave_lds_sync();
-    }
-    // into the rotated basis: H (sigma_V (.) acc)
-    float u[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) u[e] = ((sword >> ((E * lane + e) & 31)) & 1u) ? -acc[e] : acc[e];
-#pragma unroll
-    for (int hs = 1; hs < E; hs <<= 1)
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((e & hs) == 0) {
-          const float x0 = u[e], x1 = u[e + hs];
-          u[e] = x0 + x1;
-          u[e + hs] = x0 - x1;
-        }
-#pragma unroll
-    for (int mk = 1; mk < 64; mk <<= 1) {
-      const bool upper = (lane & mk) != 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float pv = __shfl_xor(u[e], mk);
-        u[e] = upper ? (pv - u[e]) : (u[e] + pv);
-      }
-    }
-    const long long prow =
-        ((long long)b * n_q_heads + (long long)g * G + h) * (splits + 1) + splits;
-#pragma unroll
-    for (int e = 0; e < E; ++e) part_acc[prow * D + E * lane + e] = u[e];
-    if (lane == 0) {
-      part_ml[prow * 2] = m;
-      part_ml[prow * 2 + 1] = l;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- 2. combine
 
 constexpr int kCombineThreads = 1024;
 constexpr int kCombineUnroll = 4;  // splits per thread whose loads are in flight together
+constexpr int kMaxRawRows = 4096;  // raw fp16 rows per sequence and KV head (scores in LDS)
 
-template <int D>
+// Raw fp16 rows attended with the packed cache: an fp16 prefix of "sink"
+// tokens kept uncompressed (turboquant-mlx guide, --kv-min-tokens) or pending
+// tokens not yet batch-compressed (PR #232, Design). lengths == nullptr: none.
+struct RawArgs {
+  const __half* q;       // [B][Hq][D], the unrotated queries
+  const __half* k;       // [B][Hkv][max_raw][D]
+  const __half* v;
+  const int32_t* lengths;
+  int max_raw;
+  int n_kv_heads;
+  float qscale2;         // softmax scale * log2(e): scores in the splits' base-2 units
+};
+
+// One workgroup per (sequence, query row): merges the split partials of the
+// packed rows, adds the raw rows' attention when there are any, normalises and
+// applies the inverse rotation to the packed part. The raw part needs none:
+// its V sum is taken in the original basis and added after the rotation.
+template <int D, bool kRaw>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ lengths, int max_len, const int32_t* __restrict__ raw_lengths,
-    int n_q_heads, int group, int n_qtok, int splits, int tokens_per_split,
-    float* __restrict__ out, SignArg sign) {
+    const int32_t* __restrict__ lengths, int max_len, int n_q_heads, int group, int n_qtok,
+    int splits, int tokens_per_split, float* __restrict__ out, SignArg sign, RawArgs raw) {
   constexpr int E = D / 64;
   constexpr int NG = kCombineThreads / D;  // split groups
   constexpr int U = kCombineUnroll;
+  constexpr int RL = 16;                   // lanes per raw row for its score
+  constexpr int RPD = D / RL;              // coordinates per lane
   __shared__ float s_acc[NG][D];
+  __shared__ float s_racc[kRaw ? NG : 1][D];
   __shared__ float s_l[NG];
+  __shared__ float s_raw[kRaw ? kMaxRawRows : 1];
   const int tid = threadIdx.x;
   // partial row: virtual head hx = g GV + vh of sequence b; output row: query
   // token vh / G, query head g G + vh % G
@@ -900,12 +805,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       ((long long)b * n_qtok + qi) * n_q_heads + (long long)g * group + (vh - qi * group);
   const int len = min(lengths[b], max_len);
   const int ns = len > 0 ? min(splits, (len + tokens_per_split - 1) / tokens_per_split) : 0;
-  // slots 0 .. ns-1 are the packed splits; slot `splits` holds the raw segment
-  // when there is one (logical slot ns then maps to it)
-  const int slots = splits + 1;
-  const int nsl = ns + (raw_lengths != nullptr && raw_lengths[b] > 0 ? 1 : 0);
-  auto phys = [&](int s) { return s < ns ? s : splits; };
-  const float* ml = part_ml + row * slots * 2;
+  const int R = kRaw ? min(raw.lengths[b], raw.max_raw) : 0;
+  const float* ml = part_ml + row * splits * 2;
   // sign word of coordinates E lane .. E lane + E - 1 (scalar loads, early)
   uint32_t sword = 0;
 #pragma unroll
@@ -914,19 +815,44 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
   // every wavefront takes the maximum over the valid splits itself
   float M = -INFINITY;
-  for (int s = tid & 63; s < nsl; s += 64) M = fmaxf(M, ml[2 * phys(s)]);
+  for (int s = tid & 63; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
   M = wave_max(M);
+
+  // raw rows: scores (RL lanes per row, 64 rows per pass) into LDS, then
+  // their maximum joins M
+  if (kRaw && R > 0) {
+    const long long kv0 = ((long long)b * raw.n_kv_heads + g) * raw.max_raw;
+    const int part = tid % RL;
+    const __half* qr = raw.q + orow * D + part * RPD;
+    float qv[RPD];
+#pragma unroll
+    for (int i = 0; i < RPD; ++i) qv[i] = __half2float(qr[i]) * raw.qscale2;
+    for (int t0 = 0; t0 < R; t0 += kCombineThreads / RL) {
+      const int t = t0 + tid / RL;
+      const __half* kr = raw.k + (kv0 + min(t, R - 1)) * D + part * RPD;
+      float sc = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPD; ++i) sc = fmaf(qv[i], __half2float(kr[i]), sc);
+#pragma unroll
+      for (int m = 1; m < RL; m <<= 1) sc += __shfl_xor(sc, m);
+      if (part == 0 && t < R) s_raw[t] = sc;
+    }
+    __syncthreads();
+    float mr = -INFINITY;
+    for (int t = tid & 63; t < R; t += 64) mr = fmaxf(mr, s_raw[t]);
+    M = fmaxf(M, wave_max(mr));
+  }
 
   // rescaled sums: thread (group grp, coordinate j) over splits s = grp mod NG,
   // U splits at a time with all their loads issued before any is used
   const int j = tid % D, grp = tid / D;
-  const float* pa = part_acc + row * slots * D + j;
+  const float* pa = part_acc + row * splits * D + j;
   float a = 0.f, L = 0.f;
-  for (int s0 = grp; s0 < nsl; s0 += NG * U) {
+  for (int s0 = grp; s0 < ns; s0 += NG * U) {
     float mv[U], lv[U], av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = phys(min(s0 + u * NG, nsl - 1));  // clamped: surplus slots get weight 0
+      const int s = min(s0 + u * NG, ns - 1);  // clamped: surplus slots get weight 0
       mv[u] = ml[2 * s];
       lv[u] = ml[2 * s + 1];
       av[u] = pa[(long long)s * D];
@@ -934,27 +860,54 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // a split where this head saw no row has maximum -inf and weighs 0
-      const float f = s0 + u * NG < nsl && mv[u] != -INFINITY ? exp2f(mv[u] - M) : 0.f;
+      const float f = s0 + u * NG < ns && mv[u] != -INFINITY ? exp2f(mv[u] - M) : 0.f;
       a = fmaf(f, av[u], a);
       L = fmaf(f, lv[u], L);
     }
   }
+  // raw rows: weights and V sum in the original basis, rows t = grp mod NG,
+  // U of them with their loads in flight together
+  float ar = 0.f;
+  if (kRaw && R > 0) {
+    const __half* vcol =
+        raw.v + ((long long)b * raw.n_kv_heads + g) * raw.max_raw * D + j;
+    for (int t0 = grp; t0 < R; t0 += NG * 2 * U) {
+      float vv[2 * U], pp[2 * U];
+#pragma unroll
+      for (int u = 0; u < 2 * U; ++u) {
+        const int t = min(t0 + u * NG, R - 1);
+        vv[u] = __half2float(vcol[(long long)t * D]);
+        pp[u] = t0 + u * NG < R ? exp2f(s_raw[t] - M) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 2 * U; ++u) {
+        ar = fmaf(pp[u], vv[u], ar);
+        if (j == 0) L += pp[u];
+      }
+    }
+  }
   s_acc[grp][j] = a;
+  if constexpr (kRaw) s_racc[grp][j] = ar;
   if (j == 0) s_l[grp] = L;
   __syncthreads();
 
   if (tid < 64) {
     const int lane = tid;
-    float u[E];
+    float u[E], ur[E];
     float Lt = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) Lt += s_l[g2];
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;  // no visible row: a zero output row
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      float x = 0.f;
+      float x = 0.f, xr = 0.f;
 #pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) x += s_acc[g2][E * lane + e];
-      u[e] = Lt > 0.f ? x / Lt : 0.f;  // no visible row: a zero output row
+      for (int g2 = 0; g2 < NG; ++g2) {
+        x += s_acc[g2][E * lane + e];
+        if constexpr (kRaw) xr += s_racc[g2][E * lane + e];
+      }
+      u[e] = Lt > 0.f ? x / Lt : 0.f;
+      ur[e] = xr * inv;
     }
     // inverse rotation: out = (1/d) sigma_V (.) H a
 #pragma unroll
@@ -980,7 +933,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int e = 0; e < E; ++e) {
       const int jj = E * lane + e;
       const float v = u[e] * invd;
-      out[orow * D + jj] = ((sword >> (jj & 31)) & 1u) ? -v : v;
+      out[orow * D + jj] = (((sword >> (jj & 31)) & 1u) ? -v : v) + ur[e];
     }
   }
 }
@@ -1069,9 +1022,8 @@ AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int ma
   if (p.splits < 1) p.splits = 1;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.qhat_bytes = 0;
-  // one partial slot per split plus one for a raw (fp16) segment
-  p.part_acc_bytes = align((size_t)batch * n_q_heads * (p.splits + 1) * dim * sizeof(float));
-  p.part_ml_bytes = align((size_t)batch * n_q_heads * (p.splits + 1) * 2 * sizeof(float));
+  p.part_acc_bytes = align((size_t)batch * n_q_heads * p.splits * dim * sizeof(float));
+  p.part_ml_bytes = align((size_t)batch * n_q_heads * p.splits * 2 * sizeof(float));
   p.total_bytes = p.part_acc_bytes + p.part_ml_bytes;
   return p;
 }
@@ -1100,46 +1052,46 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
                 lengths, max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, ev_before, ev_after,
                 stream);
   if (err != hipSuccess) return err;
-  if (raw.lengths) {
-    if (n_qtok != 1) return hipErrorInvalidValue;
-    const dim3 rgrid(n_kv_heads, batch), rblock(64 * kRawWaves);
-    const float qscale2 = scale * kLog2e;
-    switch (dim) {
-      case 64:
-        hipLaunchKernelGGL(raw_attend_kernel<64>, rgrid, rblock, 0, stream, (const __half*)q,
-                           (const __half*)raw.k, (const __half*)raw.v, raw.lengths, raw.max_raw,
-                           n_kv_heads, group, qscale2, plan.splits, pacc, pml, v_sign);
-        break;
-      case 128:
-        hipLaunchKernelGGL(raw_attend_kernel<128>, rgrid, rblock, 0, stream, (const __half*)q,
-                           (const __half*)raw.k, (const __half*)raw.v, raw.lengths, raw.max_raw,
-                           n_kv_heads, group, qscale2, plan.splits, pacc, pml, v_sign);
-        break;
-      case 256:
-        hipLaunchKernelGGL(raw_attend_kernel<256>, rgrid, rblock, 0, stream, (const __half*)q,
-                           (const __half*)raw.k, (const __half*)raw.v, raw.lengths, raw.max_raw,
-                           n_kv_heads, group, qscale2, plan.splits, pacc, pml, v_sign);
-        break;
-      default:
-        return hipErrorInvalidValue;
-    }
-  }
+  if (raw.lengths && n_qtok != 1) return hipErrorInvalidValue;
+  RawArgs ra;
+  ra.q = (const __half*)q;
+  ra.k = (const __half*)raw.k;
+  ra.v = (const __half*)raw.v;
+  ra.lengths = raw.lengths;
+  ra.max_raw = raw.max_raw;
+  ra.n_kv_heads = n_kv_heads;
+  ra.qscale2 = scale * kLog2e;
   const dim3 cgrid(n_q_heads * n_qtok, batch);
   switch (dim) {
     case 64:
-      hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
-                         lengths, max_len, raw.lengths, n_q_heads, group, n_qtok, plan.splits,
-                         plan.tokens_per_split, out, v_sign);
+      if (raw.lengths)
+        hipLaunchKernelGGL((combine_kernel<64, true>), cgrid, dim3(kCombineThreads), 0, stream,
+                           pacc, pml, lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                           plan.tokens_per_split, out, v_sign, ra);
+      else
+        hipLaunchKernelGGL((combine_kernel<64, false>), cgrid, dim3(kCombineThreads), 0, stream,
+                           pacc, pml, lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                           plan.tokens_per_split, out, v_sign, ra);
       break;
     case 128:
-      hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
-                         lengths, max_len, raw.lengths, n_q_heads, group, n_qtok, plan.splits,
-                         plan.tokens_per_split, out, v_sign);
+      if (raw.lengths)
+        hipLaunchKernelGGL((combine_kernel<128, true>), cgrid, dim3(kCombineThreads), 0, stream,
+                           pacc, pml, lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                           plan.tokens_per_split, out, v_sign, ra);
+      else
+        hipLaunchKernelGGL((combine_kernel<128, false>), cgrid, dim3(kCombineThreads), 0, stream,
+                           pacc, pml, lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                           plan.tokens_per_split, out, v_sign, ra);
       break;
     case 256:
-      hipLaunchKernelGGL(combine_kernel<256>, cgrid, dim3(kCombineThreads), 0, stream, pacc, pml,
-                         lengths, max_len, raw.lengths, n_q_heads, group, n_qtok, plan.splits,
-                         plan.tokens_per_split, out, v_sign);
+      if (raw.lengths)
+        hipLaunchKernelGGL((combine_kernel<256, true>), cgrid, dim3(kCombineThreads), 0, stream,
+                           pacc, pml, lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                           plan.tokens_per_split, out, v_sign, ra);
+      else
+        hipLaunchKernelGGL((combine_kernel<256, false>), cgrid, dim3(kCombineThreads), 0, stream,
+                           pacc, pml, lengths, max_len, n_q_heads, group, n_qtok, plan.splits,
+                           plan.tokens_per_split, out, v_sign, ra);
       break;
     default:
       return hipErrorInvalidValue;

@@ -145,8 +145,7 @@ size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int d
  *               h / (n_q_heads / n_kv_heads).
  *   workspace:  device buffer of at least tq_attend_workspace_bytes(...) bytes,
  *               256-byte aligned; its contents need not be initialised. It
- *               holds one partial per (sequence, query head, split) plus one
- *               slot for a raw segment (tq_decode_attend_mixed).
+ *               holds one partial per (sequence, query head, split).
  * Two kernels are enqueued: split attend (the query rotation runs in its
  * prologue) and combine + inverse rotation. Results agree with softmax attention over the dequantised cache
  * (computed in fp64) to about 1e-5 absolute for unit-scale inputs; fp32 sums
@@ -200,11 +199,12 @@ size_t tq_attend_multi_workspace_bytes(int batch, int n_query_tokens, int n_q_he
  *       contiguous, 16-byte aligned.
  *   raw_lengths: device int32[batch]; values are clamped to max_raw on the
  *       device; <= 0 means no raw rows for that sequence.
+ *   max_raw: 1 .. 4096 (TQ_ERR_UNSUPPORTED above).
  *   lengths[b] may be 0 (raw rows only); a sequence with no row at all gets
  *   a zero output row.
  * Every other argument is as for tq_decode_attend, with the same workspace
- * size (tq_attend_workspace_bytes). Three kernels are enqueued: split attend,
- * raw-segment attend, combine.
+ * size (tq_attend_workspace_bytes). The same two kernels are enqueued: the
+ * combine kernel also scores the raw rows and adds their part.
  */
 tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
                                  int batch, int n_q_heads, int n_kv_heads,

@@ -199,6 +199,7 @@ def test_decode_attend_mixed_validation():
                  rk, rv, max_raw, rlen, 0.125, FAKE, FAKE, ws_bytes, None)
 
     assert call(max_raw=0) == tq.TQ_ERR_INVALID_ARG
+    assert call(max_raw=4097) == tq.TQ_ERR_UNSUPPORTED        # raw scores are held in LDS
     assert call(rk=None) == tq.TQ_ERR_INVALID_ARG
     assert call(rlen=None) == tq.TQ_ERR_INVALID_ARG
     assert call(rv=FAKE + 8) == tq.TQ_ERR_INVALID_ARG           # raw rows 16-byte aligned
