@@ -225,12 +225,14 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
                         const uint8_t* v_codes, const float* v_norms, int max_ctx,
                         const int32_t* lengths, int max_len, float scale, float* out,
                         void* workspace, size_t workspace_bytes, const tq::RawSegment& raw,
-                        void* stream) {
-  if (!kc || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
-  if (kc->tabs.dim != vc->tabs.dim)
+                        void* stream, bool raw_k = false) {
+  // raw_k: k_codes holds fp16 key rows, there is no K codec and no key norm
+  if ((!kc && !raw_k) || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
+  if (kc && kc->tabs.dim != vc->tabs.dim)
     return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim,
                 vc->tabs.dim);
-  const int dim = kc->tabs.dim;
+  const int dim = vc->tabs.dim;
+  const int k_bits = raw_k ? 16 : kc->tabs.bits;
   if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_qtok <= 0)
     return fail(TQ_ERR_INVALID_ARG,
                 "%s: batch %d, query tokens %d, heads %d/%d must be positive", fn, batch,
@@ -246,7 +248,7 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
   if (max_len <= 0 || max_len > max_ctx)
     return fail(TQ_ERR_INVALID_ARG, "%s: need 1 <= max_len (%d) <= max_ctx (%d)", fn, max_len,
                 max_ctx);
-  if (!q_fp16 || !k_codes || !k_norms || !v_codes || !v_norms || !lengths || !out)
+  if (!q_fp16 || !k_codes || (!k_norms && !raw_k) || !v_codes || !v_norms || !lengths || !out)
     return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (((uintptr_t)k_codes & 15) || ((uintptr_t)v_codes & 15) || ((uintptr_t)k_norms & 3) ||
       ((uintptr_t)v_norms & 3) || ((uintptr_t)out & 3) || ((uintptr_t)lengths & 3) ||
@@ -254,10 +256,10 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
     return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale is NaN", fn);
   const int group = n_q_heads / n_kv_heads;
-  if (!tq::attend_supported(dim, kc->tabs.bits, vc->tabs.bits, group * n_qtok))
+  if (!tq::attend_supported(dim, k_bits, vc->tabs.bits, group * n_qtok))
     return fail(TQ_ERR_UNSUPPORTED,
                 "%s: no kernel for dim %d, K %d-bit, V %d-bit, %d heads per KV head", fn, dim,
-                kc->tabs.bits, vc->tabs.bits, group * n_qtok);
+                k_bits, vc->tabs.bits, group * n_qtok);
   const tq::AttendPlan plan =
       tq::plan_attend(batch, n_q_heads * n_qtok, n_kv_heads, dim, max_len);
   if ((long long)plan.splits > 0x7fffffffLL)
@@ -268,10 +270,17 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
   if ((uintptr_t)workspace & 255)
     return fail(TQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   tq::AttendTables tabs;
-  std::memcpy(tabs.k_centroids, kc->tabs.centroids, sizeof(tabs.k_centroids));
+  tq::SignArg ksign;
+  if (raw_k) {
+    std::memset(tabs.k_centroids, 0, sizeof(tabs.k_centroids));
+    std::memset(&ksign, 0, sizeof(ksign));
+  } else {
+    std::memcpy(tabs.k_centroids, kc->tabs.centroids, sizeof(tabs.k_centroids));
+    ksign = sign_arg(kc);
+  }
   std::memcpy(tabs.v_centroids, vc->tabs.centroids, sizeof(tabs.v_centroids));
-  hipError_t err = tq::launch_attend(dim, kc->tabs.bits, vc->tabs.bits, batch, n_qtok,
-                                     n_q_heads, n_kv_heads, q_fp16, sign_arg(kc), sign_arg(vc),
+  hipError_t err = tq::launch_attend(dim, k_bits, vc->tabs.bits, batch, n_qtok,
+                                     n_q_heads, n_kv_heads, q_fp16, ksign, sign_arg(vc),
                                      tabs, k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
                                      max_len, scale, out, workspace, plan, raw, g_split_before,
                                      g_split_after, (hipStream_t)stream);
@@ -312,6 +321,17 @@ tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const v
                        n_q_heads, n_kv_heads, k_codes, k_norms, v_codes, v_norms, max_ctx,
                        lengths, max_len, scale, out, workspace, workspace_bytes,
                        tq::RawSegment{}, stream);
+}
+
+tq_status tq_decode_attend_raw_k(const tq_codec* vc, const void* q_fp16, int batch,
+                                 int n_q_heads, int n_kv_heads, const void* k_fp16,
+                                 const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                 const int32_t* lengths, int max_len, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_attend("tq_decode_attend_raw_k", nullptr, vc, q_fp16, batch, 1, n_q_heads,
+                       n_kv_heads, (const uint8_t*)k_fp16, nullptr, v_codes, v_norms, max_ctx,
+                       lengths, max_len, scale, out, workspace, workspace_bytes,
+                       tq::RawSegment{}, stream, true);
 }
 
 tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,

@@ -145,7 +145,10 @@ template <int D_, int BK_, int BV_, int NHG_, int WAVES_>
 struct CfgBase {
   static constexpr int D = D_, BK = BK_, BV = BV_, NHG = NHG_, WAVES = WAVES_;
   static constexpr int E = D / 64;                     // coordinates per lane (rotation)
-  static constexpr bool KPAIR = BK <= 3;               // K looked up two coordinates at a time
+  // BK == 16: raw fp16 keys (PR #232's raw-K turbo0v* schemes), scored in the
+  // original basis with no lookup table and no key norm
+  static constexpr bool KRAW = BK == 16;
+  static constexpr bool KPAIR = !KRAW && BK <= 3;      // K looked up two coordinates at a time
   static constexpr bool VPAIR = BV <= 3 && D >= 128;   // V likewise
   static constexpr int KF = KPAIR ? 2 * BK : BK;       // bits per K lookup
   static constexpr int VF = VPAIR ? 2 * BV : BV;       // bits per V lookup
@@ -158,7 +161,7 @@ struct CfgBase {
   // field, which may reach from the dword before the row to the dword after
   // it (a neighbouring row or padding; those bits are masked off).
   static constexpr int VT_BYTES = (1 << VF) * 256;
-  static constexpr int KT_BYTES = (1 << KF) * 256;
+  static constexpr int KT_BYTES = KRAW ? 0 : (1 << KF) * 256;
   static constexpr int VS_BYTES = (kTile * RVW + 4) * 4;  // per wavefront
   static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights of a tile
   static constexpr int QS_BYTES = 4 * NHG * D * 4;      // rotated queries
@@ -331,7 +334,10 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         r.vw[i] = x.x; r.vw[i + 1] = x.y;
       }
     }
-    r.nk = knb[t];
+    if constexpr (C::KRAW)
+      r.nk = 1.f;
+    else
+      r.nk = knb[t];
     if constexpr (RKW % 4 == 0) {
 #pragma unroll
       for (int i = 0; i < RKW; i += 4) {
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     }
   };
   fill(vt, cen, C::BV, C::VPAIR);
-  fill(kt, cen + 256, C::BK, C::KPAIR);
+  if constexpr (!C::KRAW) fill(kt, cen + 256, C::BK, C::KPAIR);
 
   // ---- rotated queries: wavefront w rotates heads w, w + WAVES, ... into LDS
 #pragma unroll
@@ -424,10 +430,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       for (int e = 0; e < E; ++e) {
         const int j = E * lane + e;
         const float x = qf[r][e];
-        u[e] = ((sword >> (j & 31)) & 1u) ? -x : x;
+        u[e] = (!C::KRAW && ((sword >> (j & 31)) & 1u)) ? -x : x;
       }
+      // raw keys are scored in the original basis: no rotation
 #pragma unroll
-      for (int hs = 1; hs < E; hs <<= 1)
+      for (int hs = 1; hs < (C::KRAW ? 1 : E); hs <<= 1)
 #pragma unroll
         for (int e = 0; e < E; ++e)
           if ((e & hs) == 0) {
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
             u[e + hs] = a0 - a1;
           }
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
+      for (int m = 1; m < (C::KRAW ? 1 : 64); m <<= 1) {
         const bool upper = (lane & m) != 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -530,7 +537,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         constexpr int f = BI * kKBatch + II;
         constexpr int bit = C::KF * f;
         uint32_t addr;
-        if constexpr (C::KF == 8) {
+        if constexpr (C::KRAW) {
+          // coordinate f of the raw key row: half f % 2 of dword f / 2
+          dst[II] = __half2float(__builtin_bit_cast(__half, (uint16_t)(r.kw[f >> 1] >> (16 * (f & 1)))));
+          return;
+        } else if constexpr (C::KF == 8) {
           // whole byte: one byte permute builds (code << 8) | koff
           addr = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
                                        0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
@@ -981,7 +992,7 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(64, 4, 4, 1), TQ_SPLIT(64, 3, 3, 2), TQ_SPLIT(64, 3, 3, 1),
     TQ_SPLIT(64, 8, 3, 1), TQ_SPLIT(64, 2, 2, 1), TQ_SPLIT(64, 1, 1, 1),
     TQ_SPLIT(64, 5, 7, 1), TQ_SPLIT(64, 6, 6, 4), TQ_SPLIT(64, 4, 4, 2),
-    TQ_SPLIT(64, 8, 3, 2), TQ_SPLIT(64, 3, 3, 4),
+    TQ_SPLIT(64, 8, 3, 2), TQ_SPLIT(64, 3, 3, 4), TQ_SPLIT(64, 16, 4, 1), TQ_SPLIT(64, 16, 4, 2),
     // head_dim 128
     TQ_SPLIT(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
     TQ_SPLIT(128, 4, 4, 1), TQ_SPLIT(128, 4, 3, 1), TQ_SPLIT(128, 2, 2, 1),
@@ -990,6 +1001,8 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(128, 3, 3, 2), TQ_SPLIT(128, 4, 2, 2),
     // four query tokens of a group of 4 (multi-token decode)
     TQ_SPLIT(128, 8, 3, 4), TQ_SPLIT(128, 3, 3, 4),
+    // raw fp16 keys (turbo0v4, turbo0v2)
+    TQ_SPLIT(128, 16, 4, 1), TQ_SPLIT(128, 16, 2, 1), TQ_SPLIT(128, 16, 4, 2),
     // head_dim 256
     TQ_SPLIT(256, 4, 4, 1), TQ_SPLIT(256, 8, 3, 1), TQ_SPLIT(256, 3, 3, 1),
     TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2),
@@ -1046,7 +1059,8 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
   char* ws = (char*)workspace;
   float* pacc = (float*)ws;
   float* pml = (float*)(ws + plan.part_acc_bytes);
-  const float qscale = scale * kLog2e / (float)dim;
+  // rotated keys carry a factor d (H H = d I); raw keys are scored as they are
+  const float qscale = k_bits == 16 ? scale * kLog2e : scale * kLog2e / (float)dim;
   hipError_t err;
   err = ent->fn(plan, batch, n_kv_heads, group, n_qtok, q, k_codes, k_norms, v_codes, v_norms,
                 lengths, max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, ev_before, ev_after,

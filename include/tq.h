@@ -215,6 +215,24 @@ tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const v
                                  const int32_t* raw_lengths, float scale, float* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode attention with raw fp16 keys and packed values: PR #232's raw-K
+ * schemes (turbo0v4, turbo0v2: keys at FP16, only values compressed). Scores
+ * are taken from the fp16 key rows as they are; values are read through vc
+ * as in tq_decode_attend.
+ *   k_fp16: [batch][n_kv_heads][max_ctx][dim] fp16, contiguous, 16-byte
+ *           aligned.
+ *   v_codes / v_norms, lengths, max_len, scale, out, workspace: as for
+ *           tq_decode_attend (workspace size tq_attend_workspace_bytes).
+ * Kernels exist for dim 128 with 2- or 4-bit V (up to 8 query heads per KV
+ * head) and dim 64 with 4-bit V (up to 8); TQ_ERR_UNSUPPORTED otherwise.
+ */
+tq_status tq_decode_attend_raw_k(const tq_codec* vc, const void* q_fp16, int batch,
+                                 int n_q_heads, int n_kv_heads, const void* k_fp16,
+                                 const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                 const int32_t* lengths, int max_len, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement hook (per calling thread): while `before` and `after` are
  * non-NULL, each tq_decode_attend launches its split-attend kernel with the
  * hipEvent_t `before` and `after` bound to that dispatch (hipExtLaunchKernel

@@ -267,3 +267,29 @@ def attend_mixed(kc, vc, q, k_codes, k_norms, v_codes, v_norms, lengths, raw_k, 
             p = np.exp(s - s.max())
             out[b, h] = (p / p.sum()) @ vals
     return out
+
+
+def attend_raw_k(vc, q, k, v_codes, v_norms, lengths, scale=None):
+    """Raw fp16 keys with packed values (PR #232's raw-K turbo0v* schemes: keys
+    kept at FP16, values compressed): softmax over q . k_t for the raw key rows
+    k [B][Hkv][T][d], weighting the dequantised value rows. Written out
+    directly in fp64. q: [B][Hq][d]; returns [B][Hq][d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    k = np.asarray(k, dtype=np.float64)
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L = max(int(lengths[b]), 0)
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            v_hat = dequant(vc, v_codes[b, g, :L], v_norms[b, g, :L])
+            for h in range(g * G, (g + 1) * G):
+                s = scale * (k[b, g, :L] @ q[b, h])
+                p = np.exp(s - s.max())
+                out[b, h] = (p / p.sum()) @ v_hat
+    return out

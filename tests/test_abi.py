@@ -207,6 +207,22 @@ def test_decode_attend_mixed_validation():
     assert call(ws_bytes=16) == tq.TQ_ERR_WORKSPACE
 
 
+def test_decode_attend_raw_k_validation():
+    vc = tq.tq_codec_init(128, 4, 1)
+    v3 = tq.tq_codec_init(128, 3, 1)
+    f = tq._lib.tq_decode_attend_raw_k
+
+    def call(codec=vc, k=FAKE, Hq=32, ws_bytes=1 << 30):
+        return f(codec.handle if codec else None, FAKE, 1, Hq, 8, k, FAKE, FAKE, 256, FAKE, 256,
+                 0.125, FAKE, FAKE, ws_bytes, None)
+
+    assert call(codec=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(k=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(k=FAKE + 8) == tq.TQ_ERR_INVALID_ARG               # 16-byte aligned keys
+    assert call(codec=v3) == tq.TQ_ERR_UNSUPPORTED                 # no fp16-K / 3-bit V kernel
+    assert call(ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+
+
 def test_workspace_and_split_plan():
     assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
     assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0

@@ -567,3 +567,62 @@ def test_attend_mixed_workload_sink_prefix_full_size():
                                    np.array([L]), rk[0:1, g:g + 1], rv[0:1, g:g + 1],
                                    np.array([S]))
         assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
+
+
+# ------------------------------------------------------------------ raw fp16 keys
+
+def gpu_attend_raw_k(vc, q_np, k_dev, vcodes, vnorms, lengths_np, max_len=None):
+    B, Hq, d = q_np.shape
+    Hkv = vnorms.shape[1]
+    if max_len is None:
+        max_len = max(1, int(np.max(lengths_np)))
+    lengths = torch.from_numpy(np.asarray(lengths_np, dtype=np.int32)).to(DEV)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, max_len), dtype=torch.uint8,
+                     device=DEV)
+    tq.tq_decode_attend_raw_k(vc, to_dev(q_np), k_dev, vcodes, vnorms, lengths, max_len,
+                              1.0 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,vb,G", [(128, 4, 4), (128, 2, 3), (128, 4, 8), (64, 4, 2), (64, 4, 8)])
+def test_attend_raw_k_matches_oracle(d, vb, G):
+    """Raw fp16 keys with packed values (turbo0v4 / turbo0v2) over ragged lengths
+    spanning several tiles and splits, a length-1 and an empty sequence."""
+    announce(f"attend raw K d={d} vb={vb} G={G}")
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(d + 11 * vb + 13 * G)
+    B, Hkv, T = 4, 2, 2300
+    Hq = G * Hkv
+    lengths = np.array([T, 1100, 1, 0])
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    got = gpu_attend_raw_k(gv, q, to_dev(k), vcodes, vnorms, lengths)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    want = oracle.attend_raw_k(ov, q, k, ovc, ovn, lengths)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= ATOL
+    assert np.all(got[3] == 0.0)
+
+
+def test_attend_raw_k_llama8b_shape_32k_sampled():
+    """32K context, 32/8 heads, d=128, fp16 K and 4-bit V (turbo0v4), the 32K
+    workload's synthetic K/V: sampled KV heads against the oracle."""
+    wl = workloads.WORKLOADS["llama8b_32k_k8v3"]
+    announce("attend raw K 32K turbo0v4")
+    G = wl.n_q_heads // wl.n_kv_heads
+    gv, ov = codecs(wl.dim, 4, wl.codec_seed)
+    inp = workloads.generate(wl)
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(inp.v))
+    got = gpu_attend_raw_k(gv, inp.q, to_dev(inp.k), vcodes, vnorms, inp.lengths)
+    del vcodes, vnorms
+    rng = np.random.default_rng(4)
+    for g in rng.choice(wl.n_kv_heads, size=2, replace=False):
+        L = int(inp.lengths[0])
+        ovc, ovn, _ = oracle.encode(ov, inp.v[0:1, g:g + 1, :L])
+        want = oracle.attend_raw_k(ov, inp.q[0:1, g * G:(g + 1) * G], inp.k[0:1, g:g + 1, :L],
+                                   ovc, ovn, np.array([L]))
+        assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL

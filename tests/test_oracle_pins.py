@@ -494,3 +494,30 @@ def test_mixed_segments_reduce_to_known_attention(d, kb, vb, G):
     # neither: a zero row
     assert np.all(oracle.attend_mixed(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv,
                                       np.array([0, 0, 0]))[2] == 0.0)
+
+
+# ------------------------------------------------------------------ raw fp16 keys
+
+@pytest.mark.parametrize("d,vb,G", [(16, 4, 2), (8, 2, 1), (16, 3, 4)])
+def test_raw_keys_against_brute_force_and_special_cases(d, vb, G):
+    rng = np.random.default_rng(d * 17 + vb * 5 + G)
+    B, Hkv, T = 2, 2, 9
+    Hq = G * Hkv
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    vc = oracle.Codec(d, vb, 12)
+    vcodes, vnorms = _encode_cache(vc, v)
+    lengths = np.array([T, 4])
+    # explicit dequantisation of V and a dense softmax with the fp16 keys
+    r = _sylvester(d) * vc.signs[None, :].astype(np.float64) / math.sqrt(d)
+    idx = np.stack([oracle.unpack(cr, d, vb) for cr in vcodes.reshape(-1, vc.row_bytes)])
+    v_hat = (vnorms.reshape(-1, 1).astype(np.float64) *
+             (vc.centroids.astype(np.float64)[idx] @ r) / math.sqrt(d)).reshape(B, Hkv, T, d)
+    want = _brute_force_attention(q.astype(np.float64), k.astype(np.float64), v_hat, lengths, G,
+                                  1 / math.sqrt(d))
+    got = oracle.attend_raw_k(vc, q, k, vcodes, vnorms, lengths)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # one row: the output is that row's dequantised value
+    one = oracle.attend_raw_k(vc, q, k, vcodes, vnorms, np.array([1, 1]))
+    np.testing.assert_allclose(one[0, 0], v_hat[0, 0, 0], rtol=1e-13, atol=1e-13)
