@@ -432,6 +432,34 @@ def main():
                                              wl.k_bits, wl.v_bits) + B * Hkv * n_raw * 2 * d * 2
         mixed = {"raw_rows": n_raw, "attend_us": round(us, 3),
                  "GBps": round(mbytes / (us * 1e-6) / 1e9, 2)}
+
+    # ---- raw fp16 keys with 4-bit values (turbo0v4) over the same context
+    raw_k_line = None
+    if graph is not None:
+        try:
+            vc4 = tq.tq_codec_init(d, 4, wl.codec_seed)
+            vr4 = vc4.row_bytes
+            kcopies = max(2, math.ceil(args.cold_bytes / (B * Hkv * T * (2 * d + vr4 + 4))))
+            rk_copies = []
+            for i in range(kcopies):
+                v4c = torch.empty((B, Hkv, T, vr4), dtype=torch.uint8, device=dev)
+                v4n = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+                encode_into(vc4, v_dev, v4c, v4n, 0, T)
+                rk_copies.append((k_dev.clone(), v4c, v4n))
+            torch.cuda.synchronize()
+
+            def raw_k_only(i):
+                kr, v4c, v4n = rk_copies[i % kcopies]
+                tq.tq_decode_attend_raw_k(vc4, q_dev, kr, v4c, v4n, lengths, max_len, scale,
+                                          out_x, ws)
+
+            us = graph_us_per_call(raw_k_only, kcopies, max(2, args.steps // (4 * kcopies)))
+            kbytes = int(lengths_np.sum()) * Hkv * (2 * d + vr4 + 4)
+            raw_k_line = {"scheme": "fp16 K + 4-bit V", "cold_copies": kcopies,
+                          "attend_us": round(us, 3), "GBps": round(kbytes / (us * 1e-6) / 1e9, 2)}
+            del rk_copies
+        except tq.TQError as e:
+            raw_k_line = {"unsupported": str(e)}
     kcd, knd, vcd, vnd = copies[0]
     nbulk = 5
     eb0 = torch.cuda.Event(enable_timing=True)
@@ -496,6 +524,7 @@ def main():
         "phases": phases,
         "multi_token_decode": multi,
         "mixed_sink_decode": mixed,
+        "raw_k_decode": raw_k_line,
         "bulk_encode_kv": bulk,
     }
     if not args.no_cpu_baseline:
