@@ -521,3 +521,84 @@ def test_raw_keys_against_brute_force_and_special_cases(d, vb, G):
     # one row: the output is that row's dequantised value
     one = oracle.attend_raw_k(vc, q, k, vcodes, vnorms, np.array([1, 1]))
     np.testing.assert_allclose(one[0, 0], v_hat[0, 0, 0], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ TurboQuant-Prod keys
+
+@pytest.mark.parametrize("d,bits", [(16, 4), (64, 3), (128, 2), (32, 9)])
+def test_prod_residual_reconstructs_and_sketch_is_dense_product(d, bits):
+    rng = np.random.default_rng(d + bits)
+    x = (rng.standard_normal((40, d)) * rng.uniform(0.1, 5, (40, 1))).astype(np.float16)
+    pc = oracle.ProdCodec(d, bits, 21)
+    codes, sketch, norms, gam = oracle.encode_prod(pc, x)
+    _, _, n64, z = oracle.encode(pc.mse, x, want_z=True)
+    idx = np.stack([oracle.unpack(r, d, bits - 1) for r in codes])
+    rho = z - pc.mse.centroids.astype(np.float64)[idx]
+    # x = (N / d) sigma H (c[idx] + rho): the residual completes the MSE part
+    H = _sylvester(d)
+    rec = (n64[:, None] / d) * pc.mse.signs[None, :] * ((pc.mse.centroids.astype(np.float64)[idx] + rho) @ H)
+    np.testing.assert_allclose(rec, x.astype(np.float64), rtol=1e-12, atol=1e-12)
+    # gamma is |rho|, and N gamma / sqrt(d) the residual norm in the original basis
+    np.testing.assert_allclose(gam, np.linalg.norm(rho, axis=1), rtol=1e-6)
+    k_hat = oracle.dequant(pc.mse, codes, norms)
+    np.testing.assert_allclose(norms * gam / math.sqrt(d),
+                               np.linalg.norm(x.astype(np.float64) - k_hat, axis=1), rtol=1e-5)
+    # sketch bits: signs of the dense product H diag(sigma_S) rho
+    y = (rho * pc.sketch_signs[None, :]) @ H
+    bits_dense = np.packbits((y < 0).astype(np.uint8), axis=1, bitorder="little")
+    clear = np.abs(y) > 1e-9 * np.abs(y).max()
+    got = np.unpackbits(sketch, axis=1, bitorder="little")[:, :d]
+    want = np.unpackbits(bits_dense, axis=1, bitorder="little")[:, :d]
+    assert np.array_equal(got[clear], want[clear])
+
+
+def test_qjl_estimate_is_unbiased_over_sketch_draws():
+    """Average of the estimate over random sketch sign vectors approaches
+    <q~, rho>: a wrong sign or a missing sqrt(pi/2) fails it."""
+    rng = np.random.default_rng(7)
+    d = 64
+    rho = rng.standard_normal(d) * 0.3
+    qt = rng.standard_normal(d) * 2.0 + 0.8 * rho / np.linalg.norm(rho) * 6
+    H = _sylvester(d)
+    ests = []
+    for _ in range(4000):
+        ss = rng.choice([-1.0, 1.0], size=d)
+        y = H @ (ss * rho)
+        sketch = np.packbits((y < 0).astype(np.uint8), bitorder="little")
+        ests.append(oracle.qjl_estimate(np.linalg.norm(rho), sketch, H @ (ss * qt)))
+    ests = np.asarray(ests)
+    true = float(qt @ rho)
+    assert abs(ests.mean() - true) < 4 * ests.std() / math.sqrt(len(ests)) + 0.02 * abs(true)
+
+
+@pytest.mark.parametrize("d,bits,vb,G", [(16, 4, 3, 2), (8, 3, 2, 1)])
+def test_prod_attention_brute_force_tiny(d, bits, vb, G):
+    rng = np.random.default_rng(d * 7 + bits + vb)
+    B, Hkv, T = 1, 2, 7
+    Hq = G * Hkv
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    pc, vc = oracle.ProdCodec(d, bits, 3), oracle.Codec(d, vb, 4)
+    kcodes, ksk, knorms, krn = oracle.encode_prod(pc, k)
+    vcodes, vnorms = _encode_cache(vc, v)
+    lengths = np.array([T])
+    got = oracle.attend_prod(pc, vc, q, kcodes, ksk, knorms, krn, vcodes, vnorms, lengths)
+    # explicit: rotated query, sketch projection, estimate, dense softmax
+    H = _sylvester(d)
+    v_hat = oracle.dequant(vc, vcodes, vnorms)
+    want = np.zeros((B, Hq, d))
+    for h in range(Hq):
+        g = h // G
+        qt = H @ (pc.mse.signs * q[0, h].astype(np.float64))
+        u = H @ (pc.sketch_signs * qt)
+        s = []
+        for t in range(T):
+            idx = oracle.unpack(kcodes[0, g, t], d, bits - 1)
+            bitsj = np.unpackbits(ksk[0, g, t], bitorder="little")[:d]
+            est = math.sqrt(math.pi / 2) * float(krn[0, g, t]) / d * ((1 - 2.0 * bitsj) @ u)
+            s.append(float(knorms[0, g, t]) / d * (pc.mse.centroids[idx].astype(np.float64) @ qt + est) / math.sqrt(d))
+        s = np.asarray(s)
+        p = np.exp(s - s.max())
+        want[0, h] = (p / p.sum()) @ v_hat[0, g]
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
