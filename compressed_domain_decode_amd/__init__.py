@@ -31,7 +31,8 @@ TQ_ERR_NOMEM = -5
 EXPORTED = (
     "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
     "tq_encode", "tq_encode_kv", "tq_attend_workspace_bytes", "tq_decode_attend_multi",
-    "tq_attend_multi_workspace_bytes", "tq_decode_attend_mixed", "tq_decode_attend_raw_k", "tq_decode_attend", "tq_attend_num_splits",
+    "tq_attend_multi_workspace_bytes", "tq_decode_attend_mixed", "tq_decode_attend_raw_k",
+    "tq_codec_init_prod", "tq_encode_prod", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
 )
 
@@ -97,6 +98,11 @@ _lib.tq_decode_attend_mixed.restype = _I
 _lib.tq_decode_attend_raw_k.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
                                         ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_decode_attend_raw_k.restype = _I
+_lib.tq_codec_init_prod.argtypes = [_I, _I, ctypes.c_uint64, ctypes.POINTER(_P)]
+_lib.tq_codec_init_prod.restype = _I
+_lib.tq_encode_prod.argtypes = [_P, _P, _I, _I, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                _P, _I64, _I64, _P, _I64, _I64, _P]
+_lib.tq_encode_prod.restype = _I
 _lib.tq_attend_multi_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.tq_attend_multi_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_set_split_events.argtypes = [_P, _P]
@@ -180,15 +186,58 @@ def tq_codec_init(dim: int, bits: int, seed: int) -> Codec:
     return Codec(h.value, dim, bits, seed)
 
 
+class ProdCodec(Codec):
+    """A TurboQuant-Prod key codec: `bits` total, codes of bits - 1 bits plus a
+    dim-bit sketch and a residual norm per row."""
+
+    def __init__(self, handle: int, dim: int, bits: int, seed: int):
+        super().__init__(handle, dim, bits, seed)
+
+    @property
+    def row_bytes(self) -> int:
+        return self.dim * (self.bits - 1) // 8
+
+    @property
+    def sketch_bytes(self) -> int:
+        return self.dim // 8
+
+    def __repr__(self):
+        return f"ProdCodec(dim={self.dim}, bits={self.bits}, seed={self.seed})"
+
+
+def tq_codec_init_prod(dim: int, bits: int, seed: int) -> ProdCodec:
+    h = ctypes.c_void_p()
+    _check(_lib.tq_codec_init_prod(dim, bits, ctypes.c_uint64(seed), ctypes.byref(h)))
+    return ProdCodec(h.value, dim, bits, seed)
+
+
+def tq_encode_prod(codec: ProdCodec, x, codes, sketch, norms, rnorms, stream=None) -> None:
+    """Encode x[n_tok][n_head][dim] with a Prod codec into codes
+    [n_tok][n_head][row_bytes], sketch [n_tok][n_head][dim/8] (uint8), norms and
+    residual norms [n_tok][n_head] (fp32); any strides, last dims contiguous."""
+    j = _encode_views(codec, x, codes, norms)
+    n_tok, n_head = x.shape[0], x.shape[1]
+    if tuple(sketch.shape) != (n_tok, n_head, codec.sketch_bytes) or sketch.stride(2) != 1:
+        raise TQError(TQ_ERR_INVALID_ARG, "sketch must be [n_tok][n_head][dim/8], row contiguous")
+    if tuple(rnorms.shape) != (n_tok, n_head):
+        raise TQError(TQ_ERR_INVALID_ARG, "rnorms must be [n_tok][n_head]")
+    _check(_lib.tq_encode_prod(j.codec, j.x_fp16, n_tok, n_head, j.x_stride_tok,
+                               j.x_stride_head, j.codes, j.c_stride_tok, j.c_stride_head,
+                               _ptr(sketch), sketch.stride(0), sketch.stride(1), j.norms,
+                               j.n_stride_tok, j.n_stride_head, _ptr(rnorms), rnorms.stride(0),
+                               rnorms.stride(1), _stream_ptr(stream)))
+
+
 def tq_codec_destroy(codec: Codec) -> None:
     codec.close()
 
 
 def tq_codec_tables(codec: Codec):
     """(signs int8[dim], centroids float32[2^bits], boundaries float32[2^bits-1]) host copies."""
+    bits = codec.bits - 1 if isinstance(codec, ProdCodec) else codec.bits  # Lloyd-Max part
     s = np.zeros(codec.dim, np.int8)
-    c = np.zeros(1 << codec.bits, np.float32)
-    b = np.zeros((1 << codec.bits) - 1, np.float32)
+    c = np.zeros(1 << bits, np.float32)
+    b = np.zeros((1 << bits) - 1, np.float32)
     _check(_lib.tq_codec_tables(codec.handle, s.ctypes.data, c.ctypes.data, b.ctypes.data))
     return s, c, b
 

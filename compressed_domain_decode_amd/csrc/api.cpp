@@ -46,12 +46,25 @@ tq::SignArg sign_arg(const tq_codec* c) {
   return s;
 }
 
-// Validate the jobs of one encode call and launch them together.
+// Sketch and residual-norm outputs of a TurboQuant-Prod encode.
+struct ProdOut {
+  uint8_t* sketch;
+  int64_t s_stride_tok, s_stride_head;
+  float* rnorms;
+  int64_t r_stride_tok, r_stride_head;
+};
+
+// Validate the jobs of one encode call and launch them together. `prod`
+// (one entry per job, or NULL) carries the extra outputs of Prod codecs.
 tq_status encode_jobs(const char* fn, const tq_encode_job* jobs, int n_jobs, int n_tok,
-                      int n_head, void* stream) {
+                      int n_head, void* stream, const ProdOut* prod = nullptr) {
   for (int i = 0; i < n_jobs; ++i) {
     const tq_encode_job& j = jobs[i];
     if (!j.codec) return fail(TQ_ERR_INVALID_ARG, "%s: codec %d is NULL", fn, i);
+    if (j.codec->tabs.prod != (prod != nullptr))
+      return fail(TQ_ERR_INVALID_ARG, "%s: %s codec %d (use %s)", fn,
+                  j.codec->tabs.prod ? "TurboQuant-Prod" : "plain", i,
+                  j.codec->tabs.prod ? "tq_encode_prod" : "tq_encode or tq_encode_kv");
     if (j.codec->tabs.dim != jobs[0].codec->tabs.dim)
       return fail(TQ_ERR_INVALID_ARG, "%s: codecs of different dim (%d, %d)", fn,
                   jobs[0].codec->tabs.dim, j.codec->tabs.dim);
@@ -87,6 +100,22 @@ tq_status encode_jobs(const char* fn, const tq_encode_job* jobs, int n_jobs, int
     e.bits = j.codec->tabs.bits;
     e.sign = sign_arg(j.codec);
     std::memcpy(e.boundaries, j.codec->tabs.boundaries, sizeof(float) * ((1 << e.bits) - 1));
+    if (prod) {
+      const ProdOut& po = prod[i];
+      if (!po.sketch || !po.rnorms)
+        return fail(TQ_ERR_INVALID_ARG, "%s: NULL sketch or residual-norm pointer", fn);
+      if ((uintptr_t)po.rnorms & 3)
+        return fail(TQ_ERR_INVALID_ARG, "%s: misaligned residual-norm pointer", fn);
+      e.prod = 1;
+      std::memcpy(e.boundaries + 128, j.codec->tabs.centroids, sizeof(float) * (1 << e.bits));
+      e.sketch = po.sketch;
+      e.ss_tok = po.s_stride_tok;
+      e.ss_head = po.s_stride_head;
+      e.rnorms = po.rnorms;
+      e.rs_tok = po.r_stride_tok;
+      e.rs_head = po.r_stride_head;
+      std::memcpy(e.sketch_sign.bits, j.codec->tabs.sketch_sign_bits, sizeof(e.sketch_sign.bits));
+    }
   }
   const long long nvec = (long long)n_tok * n_head;
   if (nvec > 0x7fffffffLL - 64)
@@ -137,6 +166,23 @@ tq_status tq_codec_init(int dim, int bits, uint64_t seed, tq_codec** out) {
   return ok();
 }
 
+tq_status tq_codec_init_prod(int dim, int bits, uint64_t seed, tq_codec** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codec_init_prod: out is NULL");
+  *out = nullptr;
+  if (!dim_ok(dim))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_init_prod: dim %d not in {64, 128, 256}", dim);
+  if (bits < 2 || bits > 8)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_codec_init_prod: bits %d not in [2, 8]", bits);
+  tq_codec* c = new (std::nothrow) tq_codec;
+  if (!c) return fail(TQ_ERR_NOMEM, "tq_codec_init_prod: out of host memory");
+  if (!tq::build_prod_codec(dim, bits, seed, &c->tabs)) {
+    delete c;
+    return fail(TQ_ERR_INVALID_ARG, "tq_codec_init_prod: Lloyd-Max solve did not converge");
+  }
+  *out = c;
+  return ok();
+}
+
 void tq_codec_destroy(tq_codec* c) { delete c; }
 
 tq_status tq_codec_tables(const tq_codec* c, int8_t* signs, float* centroids,
@@ -167,6 +213,19 @@ tq_status tq_encode(const tq_codec* c, const void* x_fp16, int n_tok, int n_head
                              codes, c_stride_tok, c_stride_head, norms,
                              n_stride_tok, n_stride_head};
   return encode_jobs("tq_encode", &job, 1, n_tok, n_head, stream);
+}
+
+tq_status tq_encode_prod(const tq_codec* c, const void* x_fp16, int n_tok, int n_head,
+                         int64_t x_stride_tok, int64_t x_stride_head, uint8_t* codes,
+                         int64_t c_stride_tok, int64_t c_stride_head, uint8_t* sketch,
+                         int64_t s_stride_tok, int64_t s_stride_head, float* norms,
+                         int64_t n_stride_tok, int64_t n_stride_head, float* rnorms,
+                         int64_t r_stride_tok, int64_t r_stride_head, void* stream) {
+  const tq_encode_job job = {c,     x_fp16,       x_stride_tok, x_stride_head,
+                             codes, c_stride_tok, c_stride_head, norms,
+                             n_stride_tok, n_stride_head};
+  const ProdOut po = {sketch, s_stride_tok, s_stride_head, rnorms, r_stride_tok, r_stride_head};
+  return encode_jobs("tq_encode_prod", &job, 1, n_tok, n_head, stream, &po);
 }
 
 tq_status tq_encode_kv(const tq_encode_job* k, const tq_encode_job* v, int n_tok, int n_head,
@@ -228,6 +287,7 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
                         void* stream, bool raw_k = false) {
   // raw_k: k_codes holds fp16 key rows, there is no K codec and no key norm
   if ((!kc && !raw_k) || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
+  if (vc->tabs.prod) return fail(TQ_ERR_INVALID_ARG, "%s: V codec is a TurboQuant-Prod codec", fn);
   if (kc && kc->tabs.dim != vc->tabs.dim)
     return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim,
                 vc->tabs.dim);

@@ -138,4 +138,15 @@ bool build_codec(int dim, int bits, uint64_t seed, CodecTables* out) {
   return true;
 }
 
+bool build_prod_codec(int dim, int total_bits, uint64_t seed, CodecTables* out) {
+  if (!build_codec(dim, total_bits - 1, seed, out)) return false;
+  out->prod = true;
+  uint64_t state = seed + 1;
+  for (int j = 0; j < dim; ++j) {
+    const uint64_t z = splitmix64_next(&state);
+    if (z >> 63) out->sketch_sign_bits[j >> 5] |= 1u << (j & 31);
+  }
+  return true;
+}
+
 }  // namespace tq

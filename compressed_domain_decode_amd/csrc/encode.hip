@@ -129,38 +129,120 @@ __device__ __forceinline__ uint32_t count_below(double z, const EncodeJob& jb,
   }
 }
 
-// Quantise this lane's E coordinates and store its share of the packed row.
-template <int E, int BITS>
-__device__ __forceinline__ void quantize_store(const double (&u)[E], double nrm, int sub,
-                                               const EncodeJob& jb, const float* s_bnd,
-                                               uint8_t* row) {
-  constexpr int CH = E * BITS;                          // chunk bits per lane, <= 64
+// OR this lane's CH-bit chunk (stream bits CH*sub ..) into its byte-aligned
+// group of G = 8/gcd(CH, 8) lanes with a DPP tree; the group's first lane
+// stores the group's whole bytes at row + (sub / G) * NBY.
+template <int CH>
+__device__ __forceinline__ void pack_store(uint64_t chunk, int sub, uint8_t* row) {
   constexpr int G = CH % 8 == 0 ? 1 : 8 / gcd_c(CH, 8);  // lanes per byte-aligned group
   constexpr int NBY = G * CH / 8;                       // bytes a group stores
   static_assert(G * CH <= 64, "group chunk fits 64 bits");
-  uint64_t chunk = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const double z = (nrm == 0.0) ? 0.0 : u[e] / nrm;
-    chunk |= (uint64_t)count_below<BITS, (E <= 4)>(z, jb, s_bnd) << (BITS * e);
-  }
-  // OR-tree over the group: after the stage with mask m, every lane whose
-  // index is a multiple of 2m holds the chunks of its 2m lanes.
+  // after the stage with mask m, every lane whose index is a multiple of 2m
+  // holds the chunks of its 2m lanes
   if constexpr (G >= 2) chunk |= xor_lane64<1>(chunk) << CH;
   if constexpr (G >= 4) chunk |= xor_lane64<2>(chunk) << (2 * CH);
   if constexpr (G >= 8) chunk |= xor_lane64<4>(chunk) << (4 * CH);
-  if (sub % G != 0) return;
-  uint8_t* dst = row + (sub / G) * NBY;
-  if constexpr (NBY % 4 == 0) {
+  if (sub % G == 0) {
+    uint8_t* dst = row + (sub / G) * NBY;
+    if constexpr (NBY % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < NBY / 4; ++i) ((uint32_t*)dst)[i] = (uint32_t)(chunk >> (32 * i));
-  } else if constexpr (NBY % 2 == 0) {
+      for (int i = 0; i < NBY / 4; ++i) ((uint32_t*)dst)[i] = (uint32_t)(chunk >> (32 * i));
+    } else if constexpr (NBY % 2 == 0) {
 #pragma unroll
-    for (int i = 0; i < NBY / 2; ++i) ((uint16_t*)dst)[i] = (uint16_t)(chunk >> (16 * i));
-  } else {
+      for (int i = 0; i < NBY / 2; ++i) ((uint16_t*)dst)[i] = (uint16_t)(chunk >> (16 * i));
+    } else {
 #pragma unroll
-    for (int i = 0; i < NBY; ++i) dst[i] = (uint8_t)(chunk >> (8 * i));
+      for (int i = 0; i < NBY; ++i) dst[i] = (uint8_t)(chunk >> (8 * i));
+    }
   }
+}
+
+// Sum over the canonical pairwise tree of the vector's squares: in-lane levels,
+// then an xor butterfly with ascending lane masks (every lane gets the sum).
+template <int E, int L>
+__device__ __forceinline__ double tree_sum_sq(const double (&x)[E]) {
+  double sq[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sq[e] = x[e] * x[e];
+#pragma unroll
+  for (int w = 1; w < E; w <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; i += 2 * w) sq[i] = sq[i] + sq[i + w];
+  double s = sq[0];
+  if constexpr (L > 1) s = s + xor_lane_f64<1>(s);
+  if constexpr (L > 2) s = s + xor_lane_f64<2>(s);
+  if constexpr (L > 4) s = s + xor_lane_f64<4>(s);
+  if constexpr (L > 8) s = s + xor_lane_f64<8>(s);
+  if constexpr (L > 16) s = s + xor_lane_f64<16>(s);
+  if constexpr (L > 32) s = s + xor_lane_f64<32>(s);
+  return s;
+}
+
+// Walsh-Hadamard butterfly over the vector: in-lane stages, then cross-lane
+// stages, all in ascending order of the pair distance.
+template <int E, int L>
+__device__ __forceinline__ void wht_vector(double (&u)[E], int sub) {
+#pragma unroll
+  for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((e & hs) == 0) {
+        const double p = u[e], q = u[e + hs];
+        u[e] = p + q;
+        u[e + hs] = p - q;
+      }
+  auto cross = [&](auto mtag) __attribute__((always_inline)) {
+    constexpr int m = decltype(mtag)::value;
+    const bool upper = (sub & m) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double pv = xor_lane_f64<m>(u[e]);
+      u[e] = upper ? (pv - u[e]) : (u[e] + pv);
+    }
+  };
+  if constexpr (L > 1) cross(std::integral_constant<int, 1>{});
+  if constexpr (L > 2) cross(std::integral_constant<int, 2>{});
+  if constexpr (L > 4) cross(std::integral_constant<int, 4>{});
+  if constexpr (L > 8) cross(std::integral_constant<int, 8>{});
+  if constexpr (L > 16) cross(std::integral_constant<int, 16>{});
+  if constexpr (L > 32) cross(std::integral_constant<int, 32>{});
+}
+
+// Quantise this lane's E coordinates and store its share of the packed row.
+// For a TurboQuant-Prod job also the residual rho = z - c[idx]: its norm
+// (canonical tree) and the signs of H (sigma_S (.) rho), one bit per
+// coordinate, set for a negative value.
+template <int E, int L, int BITS>
+__device__ __forceinline__ void quantize_store(const double (&u)[E], double nrm, int sub,
+                                               const EncodeJob& jb, const float* s_bnd,
+                                               const float* s_cen, uint32_t ssgn, uint8_t* row,
+                                               uint8_t* sketch_row, float* rnorm) {
+  double z[E];
+  uint32_t idx[E];
+  uint64_t chunk = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    z[e] = (nrm == 0.0) ? 0.0 : u[e] / nrm;
+    idx[e] = count_below<BITS, (E <= 4)>(z[e], jb, s_bnd);
+    chunk |= (uint64_t)idx[e] << (BITS * e);
+  }
+  if constexpr (BITS <= 7) {
+    if (jb.prod) {  // block-uniform
+      double rho[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) rho[e] = z[e] - (double)s_cen[idx[e]];
+      const double gam = __builtin_sqrt(tree_sum_sq<E, L>(rho));
+#pragma unroll
+      for (int e = 0; e < E; ++e) rho[e] = ((ssgn >> e) & 1u) ? -rho[e] : rho[e];
+      wht_vector<E, L>(rho, sub);
+      uint64_t sk = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) sk |= (uint64_t)(rho[e] < 0.0 ? 1u : 0u) << e;
+      pack_store<E>(sk, sub, sketch_row);
+      if (sub == 0) *rnorm = (float)gam;
+    }
+  }
+  pack_store<E * BITS>(chunk, sub, row);
 }
 
 template <int D, int L>
@@ -169,6 +251,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   constexpr int VPW = 64 / L;  // vectors per wavefront
   static_assert(L >= 8 && L <= 64 && E >= 1 && E <= 8, "layout");
   __shared__ float s_bnd[256];
+  __shared__ float s_cen[128];
 
   const EncodeJob& jb = a.job[blockIdx.y];
   // The scalars the first vector load depends on come in one round of scalar
@@ -197,9 +280,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 #pragma unroll
   for (int w = 0; w < D / 32; ++w) words[w] = jb.sign.bits[w];
 
-  if (bits >= 5) {  // block-uniform: LDS copy of the boundaries for the count
+  const int prod = jb.prod;
+  if (bits >= 5 || prod) {  // block-uniform: LDS copies of the boundaries / centroids
     static_assert(64 * kWavesPerBlock >= 255, "one boundary per thread");
     if ((int)threadIdx.x < (1 << bits) - 1) s_bnd[threadIdx.x] = jb.boundaries[threadIdx.x];
+    if (prod && (int)threadIdx.x < (1 << bits))
+      s_cen[threadIdx.x] = jb.boundaries[128 + threadIdx.x];
     __syncthreads();
   }
   if (!live) return;
@@ -213,64 +299,39 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) xd[e] = (double)__half2float(xh[e]);
 
-  double u[E], sq[E];
+  double u[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    u[e] = ((sgn >> e) & 1u) ? -xd[e] : xd[e];
-    sq[e] = xd[e] * xd[e];
-  }
-  // squared norm: canonical pairwise tree, in-lane levels then cross-lane
-#pragma unroll
-  for (int w = 1; w < E; w <<= 1)
-#pragma unroll
-    for (int i = 0; i < E; i += 2 * w) sq[i] = sq[i] + sq[i + w];
-  double s = sq[0];
-  if constexpr (L > 1) s = s + xor_lane_f64<1>(s);
-  if constexpr (L > 2) s = s + xor_lane_f64<2>(s);
-  if constexpr (L > 4) s = s + xor_lane_f64<4>(s);
-  if constexpr (L > 8) s = s + xor_lane_f64<8>(s);
-  if constexpr (L > 16) s = s + xor_lane_f64<16>(s);
-  if constexpr (L > 32) s = s + xor_lane_f64<32>(s);
-  const double nrm = __builtin_sqrt(s);
-
-  // Walsh-Hadamard butterfly: in-lane stages, then cross-lane stages
-#pragma unroll
-  for (int hs = 1; hs < E; hs <<= 1)
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((e & hs) == 0) {
-        const double p = u[e], q = u[e + hs];
-        u[e] = p + q;
-        u[e + hs] = p - q;
-      }
-  auto cross = [&](auto mtag) __attribute__((always_inline)) {
-    constexpr int m = decltype(mtag)::value;
-    const bool upper = (sub & m) != 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const double pv = xor_lane_f64<m>(u[e]);
-      u[e] = upper ? (pv - u[e]) : (u[e] + pv);
-    }
-  };
-  if constexpr (L > 1) cross(std::integral_constant<int, 1>{});
-  if constexpr (L > 2) cross(std::integral_constant<int, 2>{});
-  if constexpr (L > 4) cross(std::integral_constant<int, 4>{});
-  if constexpr (L > 8) cross(std::integral_constant<int, 8>{});
-  if constexpr (L > 16) cross(std::integral_constant<int, 16>{});
-  if constexpr (L > 32) cross(std::integral_constant<int, 32>{});
+  for (int e = 0; e < E; ++e) u[e] = ((sgn >> e) & 1u) ? -xd[e] : xd[e];
+  // squared norm: canonical pairwise tree over x
+  const double nrm = __builtin_sqrt(tree_sum_sq<E, L>(xd));
+  // Walsh-Hadamard butterfly
+  wht_vector<E, L>(u, sub);
 
   if (sub == 0) jb.norms[(long long)t * jb.ns_tok + (long long)h * jb.ns_head] = (float)nrm;
   uint8_t* row = jb.codes + (long long)t * jb.cs_tok + (long long)h * jb.cs_head;
-  switch (bits) {
-    case 1: quantize_store<E, 1>(u, nrm, sub, jb, s_bnd, row); break;
-    case 2: quantize_store<E, 2>(u, nrm, sub, jb, s_bnd, row); break;
-    case 3: quantize_store<E, 3>(u, nrm, sub, jb, s_bnd, row); break;
-    case 4: quantize_store<E, 4>(u, nrm, sub, jb, s_bnd, row); break;
-    case 5: quantize_store<E, 5>(u, nrm, sub, jb, s_bnd, row); break;
-    case 6: quantize_store<E, 6>(u, nrm, sub, jb, s_bnd, row); break;
-    case 7: quantize_store<E, 7>(u, nrm, sub, jb, s_bnd, row); break;
-    default: quantize_store<E, 8>(u, nrm, sub, jb, s_bnd, row); break;
+  uint8_t* srow = nullptr;
+  float* rn = nullptr;
+  uint32_t ssgn = 0;
+  if (prod) {
+    srow = jb.sketch + (long long)t * jb.ss_tok + (long long)h * jb.ss_head;
+    rn = jb.rnorms + (long long)t * jb.rs_tok + (long long)h * jb.rs_head;
+    uint32_t sw2 = jb.sketch_sign.bits[0];
+#pragma unroll
+    for (int w = 1; w < D / 32; ++w) sw2 = ((E * sub) >> 5 == w) ? jb.sketch_sign.bits[w] : sw2;
+    ssgn = sw2 >> ((E * sub) & 31);
   }
+#define TQ_Q(B) quantize_store<E, L, B>(u, nrm, sub, jb, s_bnd, s_cen, ssgn, row, srow, rn)
+  switch (bits) {
+    case 1: TQ_Q(1); break;
+    case 2: TQ_Q(2); break;
+    case 3: TQ_Q(3); break;
+    case 4: TQ_Q(4); break;
+    case 5: TQ_Q(5); break;
+    case 6: TQ_Q(6); break;
+    case 7: TQ_Q(7); break;
+    default: TQ_Q(8); break;
+  }
+#undef TQ_Q
 }
 
 template <int D, int L>

@@ -20,9 +20,14 @@ struct EncodeJob {
   float* norms;                // norm (t, h) at element t*ns_tok + h*ns_head
   long long ns_tok, ns_head;
   int bits;
-  int pad_;
+  int prod;                    // TurboQuant-Prod keys: also the residual sketch and norm
   SignArg sign;
-  float boundaries[256];       // 2^bits - 1 used
+  float boundaries[256];       // 2^bits - 1 used; for prod, the centroids from [128]
+  uint8_t* sketch;             // prod: row (t, h) at byte t*ss_tok + h*ss_head, dim/8 bytes
+  long long ss_tok, ss_head;
+  float* rnorms;               // prod: residual norm (t, h) at element t*rs_tok + h*rs_head
+  long long rs_tok, rs_head;
+  SignArg sketch_sign;
 };
 constexpr int kMaxEncodeJobs = 2;
 struct EncodeArgs {

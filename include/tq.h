@@ -121,6 +121,32 @@ typedef struct {
 tq_status tq_encode_kv(const tq_encode_job* k, const tq_encode_job* v, int n_tok, int n_head,
                        void* stream);
 
+/*
+ * TurboQuant-Prod key codec (VeloxQuant "How I built", Stage 3 "QJL Residual
+ * Correction", and its TurboQuantProd method): bits - 1 bits of Lloyd-Max
+ * codes as above, plus a 1-bit sketch of the quantisation residual, so that
+ * scores can be corrected. In the rotated basis z = H(sigma x) / N the residual
+ * is rho = z - c[idx]; the codec stores its norm gamma = |rho| (fp32) and the
+ * signs of H(sigma_S (.) rho), sigma_S the SplitMix64 signs of seed + 1 (one bit
+ * per coordinate, LSB-first, set for a negative value). bits in [2, 8].
+ * Prod codecs encode with tq_encode_prod and attend as K codecs with
+ * tq_decode_attend_prod; the other calls reject them.
+ */
+tq_status tq_codec_init_prod(int dim, int bits, uint64_t seed, tq_codec** out);
+
+/* tq_encode for a Prod codec: codes (dim*(bits-1)/8 bytes per row, layout and
+ * alignment as tq_encode), sketch (dim/8 bytes per row at byte
+ * t*s_stride_tok + h*s_stride_head, any alignment), norms, and residual norms
+ * gamma (fp32, element t*r_stride_tok + h*r_stride_head, 4-byte aligned). Codes,
+ * sketch bits, norms and residual norms are bit-exact with the definition (fp64
+ * throughout, butterflies in ascending stage order, canonical pairwise trees). */
+tq_status tq_encode_prod(const tq_codec* c, const void* x_fp16, int n_tok, int n_head,
+                         int64_t x_stride_tok, int64_t x_stride_head, uint8_t* codes,
+                         int64_t c_stride_tok, int64_t c_stride_head, uint8_t* sketch,
+                         int64_t s_stride_tok, int64_t s_stride_head, float* norms,
+                         int64_t n_stride_tok, int64_t n_stride_head, float* rnorms,
+                         int64_t r_stride_tok, int64_t r_stride_head, void* stream);
+
 /* Workspace bytes tq_decode_attend needs for this shape (the per-split
  * partial results). A pure function of its arguments; 0 on invalid input. */
 size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int dim,

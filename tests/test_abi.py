@@ -223,6 +223,28 @@ def test_decode_attend_raw_k_validation():
     assert call(ws_bytes=16) == tq.TQ_ERR_WORKSPACE
 
 
+def test_prod_codec_and_encode_validation():
+    with pytest.raises(tq.TQError):
+        tq.tq_codec_init_prod(128, 1, 0)                  # needs at least 1 + 1 bits
+    with pytest.raises(tq.TQError):
+        tq.tq_codec_init_prod(128, 9, 0)
+    pc = tq.tq_codec_init_prod(128, 4, 7)
+    plain = tq.tq_codec_init(128, 3, 7)
+    # the MSE part is the plain 3-bit codec with the same seed
+    s1, c1, b1 = tq.tq_codec_tables(pc)
+    s2, c2, b2 = tq.tq_codec_tables(plain)
+    assert np.array_equal(s1, s2) and np.array_equal(c1, c2) and np.array_equal(b1, b2)
+    f = tq._lib.tq_encode_prod
+    args = [FAKE, 1, 1, 128, 128, FAKE, 48, 48, FAKE, 16, 16, FAKE, 1, 1, FAKE, 1, 1, None]
+    assert f(pc.handle, *args[:8], None, *args[9:]) == tq.TQ_ERR_INVALID_ARG      # no sketch
+    assert f(pc.handle, *args[:14], FAKE + 2, *args[15:]) == tq.TQ_ERR_INVALID_ARG  # rnorms align
+    assert f(plain.handle, *args) == tq.TQ_ERR_INVALID_ARG     # plain codec: tq_encode
+    assert "tq_encode" in tq.tq_last_error()
+    # and a Prod codec is refused by tq_encode
+    assert _lib.tq_encode(pc.handle, FAKE, 1, 1, 128, 128, FAKE, 48, 48, FAKE, 1, 1, None) == \
+        tq.TQ_ERR_INVALID_ARG
+
+
 def test_workspace_and_split_plan():
     assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
     assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0

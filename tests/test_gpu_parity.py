@@ -626,3 +626,40 @@ def test_attend_raw_k_llama8b_shape_32k_sampled():
         want = oracle.attend_raw_k(ov, inp.q[0:1, g * G:(g + 1) * G], inp.k[0:1, g:g + 1, :L],
                                    ovc, ovn, np.array([L]))
         assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
+
+
+# ------------------------------------------------------------------ TurboQuant-Prod keys
+
+@functools.lru_cache(maxsize=None)
+def prod_codecs(dim, bits, seed=42):
+    return tq.tq_codec_init_prod(dim, bits, seed), oracle.ProdCodec(dim, bits, seed)
+
+
+def gpu_encode_prod_rows(codec, x_np):
+    N, H, d = x_np.shape
+    x = to_dev(x_np)
+    codes = torch.full((N, H, codec.row_bytes), 0xA5, dtype=torch.uint8, device=DEV)
+    sketch = torch.full((N, H, codec.sketch_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+    norms = torch.full((N, H), -1.0, dtype=torch.float32, device=DEV)
+    rnorms = torch.full((N, H), -1.0, dtype=torch.float32, device=DEV)
+    tq.tq_encode_prod(codec, x, codes, sketch, norms, rnorms)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), sketch.cpu().numpy(), norms.cpu().numpy(), rnorms.cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("n", [384, None])
+def test_encode_prod_matches_oracle(d, bits, n):
+    """Codes, sketch bits, norms and residual norms bit-exact, in both encode
+    layouts (n = None: just past the switch to the bulk layout)."""
+    n = n or _bulk_layout_vectors(d) // 2 + 19
+    announce(f"encode prod d={d} bits={bits} n={n}")
+    g, o = prod_codecs(d, bits)
+    x = _encode_inputs(d, d * 1000 + bits, n=n)
+    codes, sketch, norms, rn = gpu_encode_prod_rows(g, x)
+    oc, osk, on, orn = oracle.encode_prod(o, x)
+    assert codes.tobytes() == oc.tobytes()
+    assert norms.tobytes() == on.tobytes()
+    assert rn.tobytes() == orn.tobytes()
+    assert sketch.tobytes() == osk.tobytes()
