@@ -32,7 +32,7 @@ EXPORTED = (
     "tq_codec_init", "tq_codec_destroy", "tq_codec_tables", "tq_codec_info", "tq_row_bytes",
     "tq_encode", "tq_encode_kv", "tq_attend_workspace_bytes", "tq_decode_attend_multi",
     "tq_attend_multi_workspace_bytes", "tq_decode_attend_mixed", "tq_decode_attend_raw_k",
-    "tq_codec_init_prod", "tq_encode_prod", "tq_decode_attend", "tq_attend_num_splits",
+    "tq_codec_init_prod", "tq_encode_prod", "tq_decode_attend_prod", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
 )
 
@@ -103,6 +103,9 @@ _lib.tq_codec_init_prod.restype = _I
 _lib.tq_encode_prod.argtypes = [_P, _P, _I, _I, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
                                 _P, _I64, _I64, _P, _I64, _I64, _P]
 _lib.tq_encode_prod.restype = _I
+_lib.tq_decode_attend_prod.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P,
+                                       _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_decode_attend_prod.restype = _I
 _lib.tq_attend_multi_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.tq_attend_multi_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_set_split_events.argtypes = [_P, _P]
@@ -407,6 +410,32 @@ def tq_decode_attend_raw_k(vc: Codec, q, k, v_codes, v_norms, lengths, max_len: 
                                        _ptr(v_norms), max_ctx, _ptr(lengths), int(max_len),
                                        float(scale), _ptr(out), _ptr(workspace), nbytes,
                                        _stream_ptr(stream)))
+
+
+def tq_decode_attend_prod(kc: ProdCodec, vc: Codec, q, k_codes, k_sketch, k_norms, k_rnorms,
+                          v_codes, v_norms, lengths, max_len: int, scale: float, out, workspace,
+                          stream=None) -> None:
+    """TurboQuant-Prod keys (codes, sketch [B][Hkv][T][d/8], norms, residual
+    norms) with packed values; the rest as tq_decode_attend."""
+    B, Hq, d = q.shape
+    Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
+    for name, t in (("q", q), ("k_codes", k_codes), ("k_sketch", k_sketch), ("k_norms", k_norms),
+                    ("k_rnorms", k_rnorms), ("v_codes", v_codes), ("v_norms", v_norms),
+                    ("lengths", lengths), ("out", out), ("workspace", workspace)):
+        if not t.is_contiguous():
+            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
+       tuple(k_sketch.shape) != (B, Hkv, max_ctx, kc.sketch_bytes) or \
+       tuple(k_rnorms.shape) != (B, Hkv, max_ctx) or \
+       tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
+       tuple(out.shape) != (B, Hq, d) or tuple(lengths.shape) != (B,):
+        raise TQError(TQ_ERR_INVALID_ARG, "cache / output shapes disagree")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tq_decode_attend_prod(kc.handle, vc.handle, _ptr(q), B, Hq, Hkv, _ptr(k_codes),
+                                      _ptr(k_sketch), _ptr(k_norms), _ptr(k_rnorms),
+                                      _ptr(v_codes), _ptr(v_norms), max_ctx, _ptr(lengths),
+                                      int(max_len), float(scale), _ptr(out), _ptr(workspace),
+                                      nbytes, _stream_ptr(stream)))
 
 
 def tq_set_split_events(before, after) -> None:

@@ -284,15 +284,20 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
                         const uint8_t* v_codes, const float* v_norms, int max_ctx,
                         const int32_t* lengths, int max_len, float scale, float* out,
                         void* workspace, size_t workspace_bytes, const tq::RawSegment& raw,
-                        void* stream, bool raw_k = false) {
+                        void* stream, bool raw_k = false,
+                        const tq::ProdKeys* prodk = nullptr) {
   // raw_k: k_codes holds fp16 key rows, there is no K codec and no key norm
   if ((!kc && !raw_k) || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
+  if (kc && kc->tabs.prod != (prodk != nullptr))
+    return fail(TQ_ERR_INVALID_ARG, "%s: %s K codec (use %s)", fn,
+                kc->tabs.prod ? "TurboQuant-Prod" : "plain",
+                kc->tabs.prod ? "tq_decode_attend_prod" : "a call without sketch arrays");
   if (vc->tabs.prod) return fail(TQ_ERR_INVALID_ARG, "%s: V codec is a TurboQuant-Prod codec", fn);
   if (kc && kc->tabs.dim != vc->tabs.dim)
     return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim,
                 vc->tabs.dim);
   const int dim = vc->tabs.dim;
-  const int k_bits = raw_k ? 16 : kc->tabs.bits;
+  const int k_bits = raw_k ? 16 : (prodk ? 32 + kc->tabs.bits : kc->tabs.bits);
   if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_qtok <= 0)
     return fail(TQ_ERR_INVALID_ARG,
                 "%s: batch %d, query tokens %d, heads %d/%d must be positive", fn, batch,
@@ -318,8 +323,9 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
   const int group = n_q_heads / n_kv_heads;
   if (!tq::attend_supported(dim, k_bits, vc->tabs.bits, group * n_qtok))
     return fail(TQ_ERR_UNSUPPORTED,
-                "%s: no kernel for dim %d, K %d-bit, V %d-bit, %d heads per KV head", fn, dim,
-                k_bits, vc->tabs.bits, group * n_qtok);
+                "%s: no kernel for dim %d, K %d-bit%s, V %d-bit, %d heads per KV head", fn, dim,
+                prodk ? kc->tabs.bits + 1 : k_bits, prodk ? " Prod" : "", vc->tabs.bits,
+                group * n_qtok);
   const tq::AttendPlan plan =
       tq::plan_attend(batch, n_q_heads * n_qtok, n_kv_heads, dim, max_len);
   if ((long long)plan.splits > 0x7fffffffLL)
@@ -342,7 +348,8 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
   hipError_t err = tq::launch_attend(dim, k_bits, vc->tabs.bits, batch, n_qtok,
                                      n_q_heads, n_kv_heads, q_fp16, ksign, sign_arg(vc),
                                      tabs, k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
-                                     max_len, scale, out, workspace, plan, raw, g_split_before,
+                                     max_len, scale, out, workspace, plan, raw,
+                                     prodk ? *prodk : tq::ProdKeys{}, g_split_before,
                                      g_split_after, (hipStream_t)stream);
   if (err != hipSuccess) return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return ok();
@@ -381,6 +388,28 @@ tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const v
                        n_q_heads, n_kv_heads, k_codes, k_norms, v_codes, v_norms, max_ctx,
                        lengths, max_len, scale, out, workspace, workspace_bytes,
                        tq::RawSegment{}, stream);
+}
+
+tq_status tq_decode_attend_prod(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                int batch, int n_q_heads, int n_kv_heads,
+                                const uint8_t* k_codes, const uint8_t* k_sketch,
+                                const float* k_norms, const float* k_rnorms,
+                                const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                const int32_t* lengths, int max_len, float scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_decode_attend_prod";
+  if (!kc || !kc->tabs.prod)
+    return fail(TQ_ERR_INVALID_ARG, "%s: K codec must be a TurboQuant-Prod codec", fn);
+  if (!k_sketch || !k_rnorms) return fail(TQ_ERR_INVALID_ARG, "%s: NULL sketch pointer", fn);
+  if (((uintptr_t)k_sketch & 15) || ((uintptr_t)k_rnorms & 3))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned sketch or residual-norm pointer", fn);
+  tq::ProdKeys pk;
+  pk.sketch = k_sketch;
+  pk.rnorms = k_rnorms;
+  std::memcpy(pk.sign.bits, kc->tabs.sketch_sign_bits, sizeof(pk.sign.bits));
+  return decode_attend(fn, kc, vc, q_fp16, batch, 1, n_q_heads, n_kv_heads, k_codes, k_norms,
+                       v_codes, v_norms, max_ctx, lengths, max_len, scale, out, workspace,
+                       workspace_bytes, tq::RawSegment{}, stream, false, &pk);
 }
 
 tq_status tq_decode_attend_raw_k(const tq_codec* vc, const void* q_fp16, int batch,

@@ -146,15 +146,19 @@ struct CfgBase {
   static constexpr int D = D_, BK = BK_, BV = BV_, NHG = NHG_, WAVES = WAVES_;
   static constexpr int E = D / 64;                     // coordinates per lane (rotation)
   // BK == 16: raw fp16 keys (PR #232's raw-K turbo0v* schemes), scored in the
-  // original basis with no lookup table and no key norm
+  // original basis with no lookup table and no key norm. BK == 32 + m:
+  // TurboQuant-Prod keys, m-bit codes plus a D-bit residual sketch and norm.
+  static constexpr bool PROD = BK > 32;
+  static constexpr int KBITS = PROD ? BK - 32 : BK;    // bits of the key codes
   static constexpr bool KRAW = BK == 16;
-  static constexpr bool KPAIR = !KRAW && BK <= 3;      // K looked up two coordinates at a time
+  static constexpr bool KPAIR = !KRAW && KBITS <= 3;   // K looked up two coordinates at a time
   static constexpr bool VPAIR = BV <= 3 && D >= 128;   // V likewise
-  static constexpr int KF = KPAIR ? 2 * BK : BK;       // bits per K lookup
+  static constexpr int KF = KPAIR ? 2 * KBITS : KBITS; // bits per K lookup
+  static constexpr int SKW = PROD ? D / 32 : 1;        // sketch dwords per K row
   static constexpr int VF = VPAIR ? 2 * BV : BV;       // bits per V lookup
   static constexpr int NKL = KPAIR ? D / 2 : D;        // K lookups per token
   static constexpr int NVS = VPAIR ? D / 128 : D / 64; // V lookups per lane per token
-  static constexpr int RKW = D * BK / 32;              // dwords per K row
+  static constexpr int RKW = D * KBITS / 32;           // dwords per K row
   static constexpr int RVW = D * BV / 32;              // dwords per V row
   // V rows of a tile staged contiguously in LDS (row t at dword 2 + t RVW,
   // 2 dwords of padding on each side): a lane reads the two dwords around its
@@ -164,7 +168,8 @@ struct CfgBase {
   static constexpr int KT_BYTES = KRAW ? 0 : (1 << KF) * 256;
   static constexpr int VS_BYTES = (kTile * RVW + 4) * 4;  // per wavefront
   static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights of a tile
-  static constexpr int QS_BYTES = 4 * NHG * D * 4;      // rotated queries
+  // rotated queries (and for Prod keys their sketch projections)
+  static constexpr int QS_BYTES = (PROD ? 2 : 1) * 4 * NHG * D * 4;
   static constexpr int CEN_BYTES = 2 * 256 * 4;         // plain centroid tables while filling
   static constexpr int GATE_BYTES = (WAVES * 4 + 15) / 16 * 16;  // first-tile arrival flags
   static constexpr int MAIN_BYTES =
@@ -191,7 +196,8 @@ constexpr int vgpr_estimate() {
   constexpr int base = B::NHG * B::D / 16 + 2 + B::NACC * B::NHG * 4 + B::NHG * 20 + 2 * B::NVS;
   constexpr int kphase = B::RKW + 2 * kKBatch * (B::KPAIR ? 2 : 1) + 16 * B::NHG;
   constexpr int vphase = 3 * kVBatch * B::NVS * 2 + 2 * kVBatch * B::NVS * (B::VPAIR ? 2 : 1);
-  return base + (kphase > vphase ? kphase : vphase);
+  constexpr int prod = B::PROD ? B::D / 32 + 1 + B::NHG * B::D / 16 + 16 * B::NHG : 0;
+  return base + prod + (kphase > vphase ? kphase : vphase);
 }
 
 // Wavefronts per workgroup: as many as the LDS and the register file allow
@@ -219,7 +225,19 @@ template <class C>
 struct TileRegs {
   uint32_t kw[C::RKW];
   uint32_t vw[C::RVW];
-  float nk, nv;
+  uint32_t sk[C::SKW];  // Prod keys: sketch bits
+  float nk, nv, rn;     // rn: Prod keys' residual norm
+};
+
+// TurboQuant-Prod keys: per-row sketch bits [.][Hkv][max_ctx][D/8] and residual
+// norms [.][Hkv][max_ctx], the sketch signs sigma_S, and the factor taking the
+// sketch projection H(sigma_S (.) H(sigma_K (.) q)) to score units
+// (scale log2(e) / d * sqrt(pi/2) / d).
+struct ProdArgs {
+  const uint8_t* sketch;
+  const float* rnorms;
+  SignArg sign;
+  float uscale;
 };
 
 // Rescale threshold of the online softmax (log2 units): the running maximum
@@ -277,7 +295,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     const float* __restrict__ k_norms, const uint8_t* __restrict__ v_codes,
     const float* __restrict__ v_norms, const int32_t* __restrict__ lengths, int n_kv_heads,
     int group, int n_qtok, int max_ctx, int max_len, int tokens_per_split, float qscale,
-    float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign) {
+    float* __restrict__ part_acc, float* __restrict__ part_ml, AttendTables tabs, SignArg ksign,
+    ProdArgs pa) {
   constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
   constexpr int RKW = C::RKW, RVW = C::RVW;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
@@ -309,6 +328,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   const uint32_t* __restrict__ vbase = (const uint32_t*)v_codes + kvrow0 * RVW;
   const float* __restrict__ knb = k_norms + kvrow0;
   const float* __restrict__ vnb = v_norms + kvrow0;
+  const uint32_t* __restrict__ skb = (const uint32_t*)pa.sketch + kvrow0 * C::SKW;
+  const float* __restrict__ rnb = pa.rnorms + kvrow0;
 
   // ---- tile registers: this lane's token rows and norms. Lanes past the
   //      range end load the range's last row instead (always in bounds); their
@@ -338,6 +359,16 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       r.nk = 1.f;
     else
       r.nk = knb[t];
+    if constexpr (C::PROD) {
+      r.rn = rnb[t];
+      const uint32_t* sr = skb + (long long)t * C::SKW;
+#pragma unroll
+      for (int i = 0; i < C::SKW; i += 2) {
+        const uint2 x = *(const uint2*)(sr + i);
+        r.sk[i] = x.x;
+        r.sk[i + 1] = x.y;
+      }
+    }
     if constexpr (RKW % 4 == 0) {
 #pragma unroll
       for (int i = 0; i < RKW; i += 4) {
@@ -418,7 +449,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     }
   };
   fill(vt, cen, C::BV, C::VPAIR);
-  if constexpr (!C::KRAW) fill(kt, cen + 256, C::BK, C::KPAIR);
+  if constexpr (!C::KRAW) fill(kt, cen + 256, C::KBITS, C::KPAIR);
 
   // ---- rotated queries: wavefront w rotates heads w, w + WAVES, ... into LDS
 #pragma unroll
@@ -453,17 +484,51 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) wq[h * D + E * lane + e] = u[e] * qscale;
+      if constexpr (C::PROD) {
+        // sketch projection H (sigma_S (.) q~) of the rotated query
+        uint32_t pw = pa.sign.bits[0];
+#pragma unroll
+        for (int w = 1; w < D / 32; ++w) pw = ((E * lane) >> 5 == w) ? pa.sign.bits[w] : pw;
+#pragma unroll
+        for (int e = 0; e < E; ++e) u[e] = ((pw >> ((E * lane + e) & 31)) & 1u) ? -u[e] : u[e];
+#pragma unroll
+        for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if ((e & hs) == 0) {
+              const float a0 = u[e], a1 = u[e + hs];
+              u[e] = a0 + a1;
+              u[e + hs] = a0 - a1;
+            }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const bool upper = (lane & m) != 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float p = __shfl_xor(u[e], m);
+            u[e] = upper ? (p - u[e]) : (u[e] + p);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) wq[4 * NHG * D + h * D + E * lane + e] = u[e] * pa.uscale;
+      }
     }
   }
   lds_barrier();  // tables, rotated queries and gate flags ready
 
   // broadcast layout: lane 4c + v of VGPR Q[hg][m] holds q^[4 hg + v][16 m + c]
   float Q[NHG][D / 16];
+  float U[C::PROD ? NHG : 1][C::PROD ? D / 16 : 1];  // Prod keys: sketch projections
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 4 * hg + (lane & 3);
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < GV ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
+    if constexpr (C::PROD) {
+#pragma unroll
+      for (int m = 0; m < D / 16; ++m)
+        U[hg][m] = h < GV ? wq[4 * NHG * D + h * D + 16 * m + (lane >> 2)] : 0.f;
+    }
   }
 
   // The gated wavefronts request their first tile once the first tile of
@@ -586,6 +651,26 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     v4f s0[NHG];
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) s0[hg] = (sc[0][hg] + sc[1][hg]) + (sc[2][hg] + sc[3][hg]);
+    if constexpr (C::PROD) {
+      // QJL correction: residual norm x sum_j sgn_j u^_j, sgn_j = -1 for a set
+      // sketch bit (the bit becomes the sign of 1.0 as the MFMA operand)
+      v4f kc4[4][NHG];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int hg = 0; hg < NHG; ++hg) kc4[a4][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+      sfor<D>([&](auto JI) {
+        constexpr int j = JI;
+        const float sg =
+            __builtin_bit_cast(float, 0x3f800000u | ((r.sk[j >> 5] << (31 - (j & 31))) & 0x80000000u));
+#pragma unroll
+        for (int hg = 0; hg < NHG; ++hg)
+          kc4[j % 4][hg] = mfma_bcast<j % 16>(U[hg][j / 16], sg, kc4[j % 4][hg]);
+      });
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg)
+        s0[hg] += r.rn * ((kc4[0][hg] + kc4[1][hg]) + (kc4[2][hg] + kc4[3][hg]));
+    }
 
     const float nv_cur = r.nv;
     const float nk_cur = r.nk;
@@ -957,19 +1042,19 @@ hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, int g
                         const uint8_t* vc,
                         const float* vn, const int32_t* lengths, int max_ctx, int max_len,
                         float qscale, float* pacc, float* pml, const AttendTables& tabs,
-                        const SignArg& ksign, hipEvent_t ev_start, hipEvent_t ev_stop,
-                        hipStream_t stream) {
+                        const SignArg& ksign, const ProdArgs& pa, hipEvent_t ev_start,
+                        hipEvent_t ev_stop, hipStream_t stream) {
   const dim3 grid(plan.splits, n_kv_heads, batch), block(64 * C::WAVES);
   if (ev_start) {
     // events bound to this dispatch: they time the kernel itself, not the queue
     hipExtLaunchKernelGGL((attend_split_kernel<C>), grid, block, 0, stream, ev_start, ev_stop, 0,
                           (const __half*)q, kc, kn, vc, vn, lengths, n_kv_heads, group, n_qtok,
                           max_ctx, max_len, plan.tokens_per_split, qscale, pacc, pml, tabs,
-                          ksign);
+                          ksign, pa);
   } else {
     hipLaunchKernelGGL((attend_split_kernel<C>), grid, block, 0, stream, (const __half*)q, kc, kn,
                        vc, vn, lengths, n_kv_heads, group, n_qtok, max_ctx, max_len,
-                       plan.tokens_per_split, qscale, pacc, pml, tabs, ksign);
+                       plan.tokens_per_split, qscale, pacc, pml, tabs, ksign, pa);
   }
   return hipGetLastError();
 }
@@ -977,7 +1062,7 @@ hipError_t launch_split(const AttendPlan& plan, int batch, int n_kv_heads, int g
 typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, int, int, const void*, const uint8_t*,
                               const float*, const uint8_t*, const float*, const int32_t*, int,
                               int, float, float*, float*, const AttendTables&, const SignArg&,
-                              hipEvent_t, hipEvent_t, hipStream_t);
+                              const ProdArgs&, hipEvent_t, hipEvent_t, hipStream_t);
 
 struct SplitEntry {
   int d, bk, bv, nhg;
@@ -993,6 +1078,7 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(64, 8, 3, 1), TQ_SPLIT(64, 2, 2, 1), TQ_SPLIT(64, 1, 1, 1),
     TQ_SPLIT(64, 5, 7, 1), TQ_SPLIT(64, 6, 6, 4), TQ_SPLIT(64, 4, 4, 2),
     TQ_SPLIT(64, 8, 3, 2), TQ_SPLIT(64, 3, 3, 4), TQ_SPLIT(64, 16, 4, 1), TQ_SPLIT(64, 16, 4, 2),
+    TQ_SPLIT(64, 35, 4, 1),
     // head_dim 128
     TQ_SPLIT(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
     TQ_SPLIT(128, 4, 4, 1), TQ_SPLIT(128, 4, 3, 1), TQ_SPLIT(128, 2, 2, 1),
@@ -1003,6 +1089,9 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(128, 8, 3, 4), TQ_SPLIT(128, 3, 3, 4),
     // raw fp16 keys (turbo0v4, turbo0v2)
     TQ_SPLIT(128, 16, 4, 1), TQ_SPLIT(128, 16, 2, 1), TQ_SPLIT(128, 16, 4, 2),
+    // TurboQuant-Prod keys (32 + code bits): 4-bit (3 + sketch) with 4-bit V,
+    // 3-bit (2 + sketch) with 3-bit V
+    TQ_SPLIT(128, 35, 4, 1), TQ_SPLIT(128, 35, 4, 2), TQ_SPLIT(128, 34, 3, 1),
     // head_dim 256
     TQ_SPLIT(256, 4, 4, 1), TQ_SPLIT(256, 8, 3, 1), TQ_SPLIT(256, 3, 3, 1),
     TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2),
@@ -1052,7 +1141,8 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
                          const uint8_t* v_codes, const float* v_norms, int max_ctx,
                          const int32_t* lengths, int max_len, float scale, float* out,
                          void* workspace, const AttendPlan& plan, const RawSegment& raw,
-                         hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream) {
+                         const ProdKeys& prodk, hipEvent_t ev_before, hipEvent_t ev_after,
+                         hipStream_t stream) {
   const int group = n_q_heads / n_kv_heads;
   const SplitEntry* ent = find_split(dim, k_bits, v_bits, group * n_qtok);
   if (!ent) return hipErrorInvalidValue;
@@ -1062,9 +1152,14 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
   // rotated keys carry a factor d (H H = d I); raw keys are scored as they are
   const float qscale = k_bits == 16 ? scale * kLog2e : scale * kLog2e / (float)dim;
   hipError_t err;
+  ProdArgs pa;
+  pa.sketch = prodk.sketch;
+  pa.rnorms = prodk.rnorms;
+  pa.sign = prodk.sign;
+  pa.uscale = qscale * 1.2533141373155003f / (float)dim;  // sqrt(pi/2) / d
   err = ent->fn(plan, batch, n_kv_heads, group, n_qtok, q, k_codes, k_norms, v_codes, v_norms,
-                lengths, max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, ev_before, ev_after,
-                stream);
+                lengths, max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, pa, ev_before,
+                ev_after, stream);
   if (err != hipSuccess) return err;
   if (raw.lengths && n_qtok != 1) return hipErrorInvalidValue;
   RawArgs ra;

@@ -54,6 +54,15 @@ struct AttendPlan {
 
 AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len);
 
+// TurboQuant-Prod keys' extra cache arrays (sketch == nullptr: plain keys):
+// sketch rows [batch][n_kv_heads][max_ctx][dim/8] (16-byte aligned) and
+// residual norms [batch][n_kv_heads][max_ctx]; sign: the sketch signs.
+struct ProdKeys {
+  const uint8_t* sketch = nullptr;
+  const float* rnorms = nullptr;
+  SignArg sign{};
+};
+
 // Raw fp16 rows attended together with the packed cache (lengths == nullptr:
 // none). k and v are [batch][n_kv_heads][max_raw][dim], 16-byte aligned.
 struct RawSegment {
@@ -71,6 +80,8 @@ hipError_t launch_encode(int dim, EncodeArgs& args, hipStream_t stream);
 
 bool attend_supported(int dim, int k_bits, int v_bits, int group);
 
+// k_bits: 1..8 plain codes, 16 raw fp16 keys, 32 + m TurboQuant-Prod keys with
+// m-bit codes (prodk then set).
 // n_qtok query tokens per sequence (q and out [batch][n_qtok][n_q_heads][dim]),
 // causal among themselves; plan sized for n_q_heads * n_qtok heads.
 hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok, int n_q_heads,
@@ -80,7 +91,8 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
                          const uint8_t* v_codes, const float* v_norms, int max_ctx,
                          const int32_t* lengths, int max_len, float scale, float* out,
                          void* workspace, const AttendPlan& plan, const RawSegment& raw,
-                         hipEvent_t ev_before, hipEvent_t ev_after, hipStream_t stream);
+                         const ProdKeys& prodk, hipEvent_t ev_before, hipEvent_t ev_after,
+                         hipStream_t stream);
 
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);

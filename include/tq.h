@@ -147,6 +147,28 @@ tq_status tq_encode_prod(const tq_codec* c, const void* x_fp16, int n_tok, int n
                          int64_t n_stride_tok, int64_t n_stride_head, float* rnorms,
                          int64_t r_stride_tok, int64_t r_stride_head, void* stream);
 
+/*
+ * Decode attention with TurboQuant-Prod keys (encoded by tq_encode_prod):
+ * scores use the QJL-corrected estimate of <q, k>,
+ *   <q, k_hat_MSE> + (N / d) sqrt(pi / 2) (gamma / d) sum_j sgn_j u_j,
+ * u = H(sigma_S (.) H(sigma_K (.) q)), sgn_j = -1 where sketch bit j is set
+ * (the asymmetric 1-bit JL estimate of the residual term of VeloxQuant "How I
+ * built", Stage 3). Values are read through vc as in tq_decode_attend.
+ *   k_codes: [batch][n_kv_heads][max_ctx][dim*(bits-1)/8], 16-byte aligned;
+ *   k_sketch: [batch][n_kv_heads][max_ctx][dim/8], 16-byte aligned;
+ *   k_norms, k_rnorms: [batch][n_kv_heads][max_ctx] fp32.
+ * Every other argument as for tq_decode_attend. Kernels exist for dim 128 with
+ * 4-bit Prod K and 4-bit V (group <= 8), 3-bit Prod K and 3-bit V (group <= 4),
+ * and dim 64 with 4-bit Prod K and 4-bit V (group <= 4).
+ */
+tq_status tq_decode_attend_prod(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                int batch, int n_q_heads, int n_kv_heads,
+                                const uint8_t* k_codes, const uint8_t* k_sketch,
+                                const float* k_norms, const float* k_rnorms,
+                                const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                const int32_t* lengths, int max_len, float scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes tq_decode_attend needs for this shape (the per-split
  * partial results). A pure function of its arguments; 0 on invalid input. */
 size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int dim,

@@ -245,6 +245,26 @@ def test_prod_codec_and_encode_validation():
         tq.TQ_ERR_INVALID_ARG
 
 
+def test_decode_attend_prod_validation():
+    pk = tq.tq_codec_init_prod(128, 4, 1)
+    plain = tq.tq_codec_init(128, 4, 1)
+    vc = tq.tq_codec_init(128, 4, 1)
+    f = tq._lib.tq_decode_attend_prod
+
+    def call(kc=pk, sk=FAKE, rn=FAKE, v=vc, ws_bytes=1 << 30):
+        return f(kc.handle, v.handle, FAKE, 1, 32, 8, FAKE, sk, FAKE, rn, FAKE, FAKE, 256, FAKE,
+                 256, 0.125, FAKE, FAKE, ws_bytes, None)
+
+    assert call(kc=plain) == tq.TQ_ERR_INVALID_ARG            # needs a Prod K codec
+    assert call(sk=None) == tq.TQ_ERR_INVALID_ARG
+    assert call(sk=FAKE + 8) == tq.TQ_ERR_INVALID_ARG
+    assert call(rn=FAKE + 2) == tq.TQ_ERR_INVALID_ARG
+    assert call(v=pk) == tq.TQ_ERR_INVALID_ARG                 # V cannot be a Prod codec
+    assert call(ws_bytes=16) == tq.TQ_ERR_WORKSPACE
+    # a Prod K codec is refused by the plain call
+    assert _attend_call(pk, vc) == tq.TQ_ERR_INVALID_ARG
+
+
 def test_workspace_and_split_plan():
     assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
     assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0

@@ -663,3 +663,51 @@ def test_encode_prod_matches_oracle(d, bits, n):
     assert norms.tobytes() == on.tobytes()
     assert rn.tobytes() == orn.tobytes()
     assert sketch.tobytes() == osk.tobytes()
+
+
+def gpu_encode_prod_cache(codec, x_dev):
+    B, H, T, d = x_dev.shape
+    codes = torch.empty((B, H, T, codec.row_bytes), dtype=torch.uint8, device=DEV)
+    sketch = torch.empty((B, H, T, codec.sketch_bytes), dtype=torch.uint8, device=DEV)
+    norms = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    rnorms = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    tm = lambda a, *row: a.view(B * H, T, *row).permute(1, 0, *range(2, 2 + len(row)))
+    tq.tq_encode_prod(codec, tm(x_dev, d), tm(codes, codec.row_bytes),
+                      tm(sketch, codec.sketch_bytes), tm(norms), tm(rnorms))
+    return codes, sketch, norms, rnorms
+
+
+@pytest.mark.parametrize("d,kb,vb,G", [(128, 4, 4, 4), (128, 4, 4, 8), (128, 3, 3, 4),
+                                       (64, 4, 4, 2)])
+def test_attend_prod_matches_oracle(d, kb, vb, G):
+    """Prod keys (codes + sketch + residual norms from the GPU encode, checked
+    bit-exact first) with packed values over ragged lengths, several splits, a
+    single-row and an empty sequence."""
+    announce(f"attend prod d={d} kb={kb} vb={vb} G={G}")
+    gk, ok = prod_codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(d + 3 * kb + 5 * vb + 7 * G)
+    B, Hkv, T = 4, 2, 2200
+    Hq = G * Hkv
+    lengths = np.array([T, 1300, 1, 0])
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    kcodes, ksk, knorms, krn = gpu_encode_prod_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    okc, osk, okn, okr = oracle.encode_prod(ok, k)
+    assert kcodes.cpu().numpy().tobytes() == okc.tobytes()
+    assert ksk.cpu().numpy().tobytes() == osk.tobytes()
+    assert krn.cpu().numpy().tobytes() == okr.tobytes()
+    ovc, ovn, _ = oracle.encode(ov, v)
+    lengths_d = torch.from_numpy(lengths.astype(np.int32)).to(DEV)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, T), dtype=torch.uint8, device=DEV)
+    tq.tq_decode_attend_prod(gk, gv, to_dev(q), kcodes, ksk, knorms, krn, vcodes, vnorms,
+                             lengths_d, T, 1.0 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.attend_prod(ok, ov, q, okc, osk, okn, okr, ovc, ovn, lengths)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= ATOL
+    assert np.all(got[3] == 0.0)
