@@ -460,6 +460,42 @@ def main():
             del rk_copies
         except tq.TQError as e:
             raw_k_line = {"unsupported": str(e)}
+    # ---- TurboQuant-Prod keys (3-bit codes + 1-bit sketch) with 4-bit values
+    prod_line = None
+    if graph is not None:
+        try:
+            pk = tq.tq_codec_init_prod(d, 4, wl.codec_seed)
+            vc4 = tq.tq_codec_init(d, 4, wl.codec_seed)
+            prow = pk.row_bytes + pk.sketch_bytes + 8 + vc4.row_bytes + 4
+            pcopies = max(2, math.ceil(args.cold_bytes / (B * Hkv * T * prow)))
+            tmv = lambda a, *row: a.view(B * Hkv, T, *row).permute(1, 0, *range(2, 2 + len(row)))
+            p_copies = []
+            for i in range(pcopies):
+                t = (torch.empty((B, Hkv, T, pk.row_bytes), dtype=torch.uint8, device=dev),
+                     torch.empty((B, Hkv, T, pk.sketch_bytes), dtype=torch.uint8, device=dev),
+                     torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+                     torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+                     torch.empty((B, Hkv, T, vc4.row_bytes), dtype=torch.uint8, device=dev),
+                     torch.empty((B, Hkv, T), dtype=torch.float32, device=dev))
+                tq.tq_encode_prod(pk, tmv(k_dev, d), tmv(t[0], pk.row_bytes),
+                                  tmv(t[1], pk.sketch_bytes), tmv(t[2]), tmv(t[3]))
+                encode_into(vc4, v_dev, t[4], t[5], 0, T)
+                p_copies.append(t)
+            torch.cuda.synchronize()
+
+            def prod_only(i):
+                c = p_copies[i % pcopies]
+                tq.tq_decode_attend_prod(pk, vc4, q_dev, c[0], c[1], c[2], c[3], c[4], c[5],
+                                         lengths, max_len, scale, out_x, ws)
+
+            us = graph_us_per_call(prod_only, pcopies, max(2, args.steps // (4 * pcopies)))
+            pbytes = int(lengths_np.sum()) * Hkv * prow
+            prod_line = {"scheme": "4-bit Prod K (3-bit codes + QJL sketch) + 4-bit V",
+                         "cold_copies": pcopies, "attend_us": round(us, 3),
+                         "GBps": round(pbytes / (us * 1e-6) / 1e9, 2)}
+            del p_copies
+        except tq.TQError as e:
+            prod_line = {"unsupported": str(e)}
     kcd, knd, vcd, vnd = copies[0]
     nbulk = 5
     eb0 = torch.cuda.Event(enable_timing=True)
@@ -525,6 +561,7 @@ def main():
         "multi_token_decode": multi,
         "mixed_sink_decode": mixed,
         "raw_k_decode": raw_k_line,
+        "prod_decode": prod_line,
         "bulk_encode_kv": bulk,
     }
     if not args.no_cpu_baseline:

@@ -711,3 +711,37 @@ def test_attend_prod_matches_oracle(d, kb, vb, G):
     assert np.all(np.isfinite(got))
     assert np.max(np.abs(got - want)) <= ATOL
     assert np.all(got[3] == 0.0)
+
+
+def test_attend_prod_llama8b_shape_32k_sampled():
+    """32K context, 32/8 heads, d=128, 4-bit Prod keys (3-bit codes + sketch)
+    and 4-bit values over the 32K workload's synthetic K/V: sampled KV heads
+    against the oracle, the Prod encode of those heads checked bit-exact."""
+    wl = workloads.WORKLOADS["llama8b_32k_k8v3"]
+    announce("attend prod 32K k4(prod) v4")
+    G = wl.n_q_heads // wl.n_kv_heads
+    gk, ok = prod_codecs(wl.dim, 4, wl.codec_seed)
+    gv, ov = codecs(wl.dim, 4, wl.codec_seed)
+    inp = workloads.generate(wl)
+    B, Hkv, T = inp.k.shape[:3]
+    kcodes, ksk, knorms, krn = gpu_encode_prod_cache(gk, to_dev(inp.k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(inp.v))
+    lengths_d = torch.from_numpy(inp.lengths.astype(np.int32)).to(DEV)
+    out = torch.empty((B, wl.n_q_heads, wl.dim), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, wl.n_q_heads, Hkv, wl.dim, T),
+                     dtype=torch.uint8, device=DEV)
+    tq.tq_decode_attend_prod(gk, gv, to_dev(inp.q), kcodes, ksk, knorms, krn, vcodes, vnorms,
+                             lengths_d, T, 1.0 / math.sqrt(wl.dim), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rng = np.random.default_rng(6)
+    for g in rng.choice(Hkv, size=2, replace=False):
+        L = int(inp.lengths[0])
+        okc, osk, okn, okr = oracle.encode_prod(ok, inp.k[0:1, g:g + 1, :L])
+        assert kcodes[0, g, :L].cpu().numpy().tobytes() == okc.tobytes()
+        assert ksk[0, g, :L].cpu().numpy().tobytes() == osk.tobytes()
+        assert krn[0, g, :L].cpu().numpy().tobytes() == okr.tobytes()
+        ovc, ovn, _ = oracle.encode(ov, inp.v[0:1, g:g + 1, :L])
+        want = oracle.attend_prod(ok, ov, inp.q[0:1, g * G:(g + 1) * G], okc, osk, okn, okr,
+                                  ovc, ovn, np.array([L]))
+        assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
