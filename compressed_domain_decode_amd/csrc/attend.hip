@@ -889,6 +889,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   __shared__ float s_acc[NG][D];
   __shared__ float s_racc[kRaw ? NG : 1][D];
   __shared__ float s_l[NG];
+  __shared__ float s_m[NG];
+  __shared__ float s_lr[kRaw ? NG : 1];
   __shared__ float s_raw[kRaw ? kMaxRawRows : 1];
   const int tid = threadIdx.x;
   // partial row: virtual head hx = g GV + vh of sequence b; output row: query
@@ -899,9 +901,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int g = hx / GV, vh = hx - g * GV, qi = vh / group;
   const long long orow =
       ((long long)b * n_qtok + qi) * n_q_heads + (long long)g * group + (vh - qi * group);
-  const int len = min(lengths[b], max_len);
-  const int ns = len > 0 ? min(splits, (len + tokens_per_split - 1) / tokens_per_split) : 0;
-  const int R = kRaw ? min(raw.lengths[b], raw.max_raw) : 0;
   const float* ml = part_ml + row * splits * 2;
   // sign word of coordinates E lane .. E lane + E - 1 (scalar loads, early)
   uint32_t sword = 0;
@@ -909,13 +908,52 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   for (int w = 0; w < D / 32; ++w)
     if ((E * (tid & 63)) >> 5 == w) sword = sign.bits[w];
 
-  // every wavefront takes the maximum over the valid splits itself
-  float M = -INFINITY;
-  for (int s = tid & 63; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M);
+  // rescaled sums: thread (group grp, coordinate j) over splits s = grp mod NG,
+  // U splits at a time, each group with its own running maximum. The loads
+  // are issued before the sequence length arrives: slots past the valid
+  // splits read in-bounds workspace and are dropped.
+  const int j = tid % D, grp = tid / D;
+  const float* pa = part_acc + row * splits * D + j;
+  const int len = min(lengths[b], max_len);
+  const int ns = len > 0 ? min(splits, (len + tokens_per_split - 1) / tokens_per_split) : 0;
+  const int R = kRaw ? min(raw.lengths[b], raw.max_raw) : 0;
+  float a = 0.f, L = 0.f, mg = -INFINITY;
+  for (int s0 = grp; s0 < splits; s0 += NG * U) {
+    float mv[U], lv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u * NG, splits - 1);
+      mv[u] = ml[2 * s];
+      lv[u] = ml[2 * s + 1];
+      av[u] = pa[(long long)s * D];
+    }
+    // a split where this head saw no row has maximum -inf and is dropped
+    bool ok[U];
+    float mnew = mg;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ok[u] = s0 + u * NG < ns && mv[u] != -INFINITY;
+      if (ok[u]) mnew = fmaxf(mnew, mv[u]);
+    }
+    if (mnew != mg) {  // mnew > mg: rescale (by 0 while mg is still -inf)
+      const float r = exp2f(mg - mnew);
+      a *= r;
+      L *= r;
+      mg = mnew;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) {
+        const float f = exp2f(mv[u] - mg);
+        a = fmaf(f, av[u], a);
+        L = fmaf(f, lv[u], L);
+      }
+  }
 
-  // raw rows: scores (RL lanes per row, 64 rows per pass) into LDS, then
-  // their maximum joins M
+  // raw rows: scores (RL lanes per row, 64 rows per pass) into LDS, their
+  // maximum mr, then weights and the V sum in the original basis, rows
+  // t = grp mod NG, U of them with their loads in flight together
+  float mr = -INFINITY, ar = 0.f, Lr = 0.f;
   if (kRaw && R > 0) {
     const long long kv0 = ((long long)b * raw.n_kv_heads + g) * raw.max_raw;
     const int part = tid % RL;
@@ -934,37 +972,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       if (part == 0 && t < R) s_raw[t] = sc;
     }
     __syncthreads();
-    float mr = -INFINITY;
     for (int t = tid & 63; t < R; t += 64) mr = fmaxf(mr, s_raw[t]);
-    M = fmaxf(M, wave_max(mr));
-  }
-
-  // rescaled sums: thread (group grp, coordinate j) over splits s = grp mod NG,
-  // U splits at a time with all their loads issued before any is used
-  const int j = tid % D, grp = tid / D;
-  const float* pa = part_acc + row * splits * D + j;
-  float a = 0.f, L = 0.f;
-  for (int s0 = grp; s0 < ns; s0 += NG * U) {
-    float mv[U], lv[U], av[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = min(s0 + u * NG, ns - 1);  // clamped: surplus slots get weight 0
-      mv[u] = ml[2 * s];
-      lv[u] = ml[2 * s + 1];
-      av[u] = pa[(long long)s * D];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // a split where this head saw no row has maximum -inf and weighs 0
-      const float f = s0 + u * NG < ns && mv[u] != -INFINITY ? exp2f(mv[u] - M) : 0.f;
-      a = fmaf(f, av[u], a);
-      L = fmaf(f, lv[u], L);
-    }
-  }
-  // raw rows: weights and V sum in the original basis, rows t = grp mod NG,
-  // U of them with their loads in flight together
-  float ar = 0.f;
-  if (kRaw && R > 0) {
+    mr = wave_max(mr);
     const __half* vcol =
         raw.v + ((long long)b * raw.n_kv_heads + g) * raw.max_raw * D + j;
     for (int t0 = grp; t0 < R; t0 += NG * 2 * U) {
@@ -973,37 +982,56 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       for (int u = 0; u < 2 * U; ++u) {
         const int t = min(t0 + u * NG, R - 1);
         vv[u] = __half2float(vcol[(long long)t * D]);
-        pp[u] = t0 + u * NG < R ? exp2f(s_raw[t] - M) : 0.f;
+        pp[u] = t0 + u * NG < R ? exp2f(s_raw[t] - mr) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 2 * U; ++u) {
         ar = fmaf(pp[u], vv[u], ar);
-        if (j == 0) L += pp[u];
+        Lr += pp[u];
       }
     }
   }
   s_acc[grp][j] = a;
   if constexpr (kRaw) s_racc[grp][j] = ar;
-  if (j == 0) s_l[grp] = L;
+  if (j == 0) {
+    s_m[grp] = mg;
+    s_l[grp] = L;
+    if constexpr (kRaw) s_lr[grp] = Lr;
+  }
   __syncthreads();
 
   if (tid < 64) {
     const int lane = tid;
     float u[E], ur[E];
+    // the groups (and the raw rows) meet at the overall maximum M
+    float M = mr;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) M = fmaxf(M, s_m[g2]);
+    float fg[NG];
     float Lt = 0.f;
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) Lt += s_l[g2];
+    for (int g2 = 0; g2 < NG; ++g2) {
+      fg[g2] = s_m[g2] == -INFINITY ? 0.f : exp2f(s_m[g2] - M);
+      Lt = fmaf(fg[g2], s_l[g2], Lt);
+    }
+    const float fr = kRaw && mr != -INFINITY ? exp2f(mr - M) : 0.f;
+    if constexpr (kRaw) {
+      float lr = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) lr += s_lr[g2];
+      Lt = fmaf(fr, lr, Lt);
+    }
     const float inv = Lt > 0.f ? 1.f / Lt : 0.f;  // no visible row: a zero output row
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float x = 0.f, xr = 0.f;
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
-        x += s_acc[g2][E * lane + e];
+        x = fmaf(fg[g2], s_acc[g2][E * lane + e], x);
         if constexpr (kRaw) xr += s_racc[g2][E * lane + e];
       }
       u[e] = Lt > 0.f ? x / Lt : 0.f;
-      ur[e] = xr * inv;
+      ur[e] = xr * fr * inv;
     }
     // inverse rotation: out = (1/d) sigma_V (.) H a
 #pragma unroll
