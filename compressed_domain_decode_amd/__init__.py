@@ -34,6 +34,8 @@ EXPORTED = (
     "tq_attend_multi_workspace_bytes", "tq_decode_attend_mixed", "tq_decode_attend_raw_k",
     "tq_codec_init_prod", "tq_encode_prod", "tq_decode_attend_prod", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
+    "tq_cache_init", "tq_cache_destroy", "tq_cache_state", "tq_cache_append",
+    "tq_cache_workspace_bytes", "tq_cache_attend",
 )
 
 
@@ -112,6 +114,27 @@ _lib.tq_set_split_events.argtypes = [_P, _P]
 _lib.tq_stream_read.restype = _I
 _lib.tq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.tq_set_split_events.restype = _I
+
+
+class _CacheDesc(ctypes.Structure):
+    """Mirror of tq_cache_desc."""
+    _fields_ = [("batch", _I), ("n_kv_heads", _I), ("max_ctx", _I), ("group_size", _I),
+                ("k_codes", _P), ("k_norms", _P), ("v_codes", _P), ("v_norms", _P),
+                ("pending_k", _P), ("pending_v", _P), ("packed_len", _P), ("pending_len", _P)]
+
+
+_lib.tq_cache_init.argtypes = [_P, _P, ctypes.POINTER(_CacheDesc), ctypes.POINTER(_P)]
+_lib.tq_cache_init.restype = _I
+_lib.tq_cache_destroy.argtypes = [_P]
+_lib.tq_cache_destroy.restype = None
+_lib.tq_cache_state.argtypes = [_P, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.tq_cache_state.restype = _I
+_lib.tq_cache_append.argtypes = [_P, _P, _P, _I, _P]
+_lib.tq_cache_append.restype = _I
+_lib.tq_cache_workspace_bytes.argtypes = [_P, _I]
+_lib.tq_cache_workspace_bytes.restype = ctypes.c_size_t
+_lib.tq_cache_attend.argtypes = [_P, _P, _I, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_cache_attend.restype = _I
 _lib.tq_status_string.argtypes = [_I]
 _lib.tq_status_string.restype = ctypes.c_char_p
 _lib.tq_last_error.argtypes = []
@@ -456,3 +479,97 @@ def tq_stream_read(buf, sink, stream=None) -> None:
 
 def library_path() -> str:
     return LIB_PATH
+
+
+# ------------------------------------------------------------ two-phase cache
+
+class Cache:
+    """Handle of a tq_cache. It keeps the caller's buffers referenced for as
+    long as the C object holds their pointers."""
+
+    def __init__(self, handle: int, kc: Codec, vc: Codec, buffers: tuple):
+        self._h = handle
+        self.kc, self.vc = kc, vc
+        self.buffers = buffers
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise TQError(TQ_ERR_INVALID_ARG, "cache already destroyed")
+        return self._h
+
+    def close(self):
+        if self._h:
+            _lib.tq_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tq_cache_init(kc: Codec, vc: Codec, k_codes, k_norms, v_codes, v_norms, pending_k,
+                  pending_v, packed_len, pending_len) -> Cache:
+    """Two-phase cache over caller-owned buffers: packed cache
+    [B][Hkv][max_ctx][row] / [B][Hkv][max_ctx], fp16 pending rows
+    [B][Hkv][group_size][d], device int32 length arrays [B]."""
+    B, Hkv, max_ctx = k_norms.shape
+    G = pending_k.shape[2]
+    for name, t in (("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
+                    ("v_norms", v_norms), ("pending_k", pending_k), ("pending_v", pending_v),
+                    ("packed_len", packed_len), ("pending_len", pending_len)):
+        if not t.is_contiguous():
+            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
+       tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
+       tuple(v_norms.shape) != (B, Hkv, max_ctx) or \
+       tuple(pending_k.shape) != (B, Hkv, G, kc.dim) or tuple(pending_v.shape) != (B, Hkv, G, kc.dim) or \
+       tuple(packed_len.shape) != (B,) or tuple(pending_len.shape) != (B,):
+        raise TQError(TQ_ERR_INVALID_ARG, "cache buffer shapes disagree")
+    desc = _CacheDesc(B, Hkv, max_ctx, G, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                      _ptr(v_norms), _ptr(pending_k), _ptr(pending_v), _ptr(packed_len),
+                      _ptr(pending_len))
+    h = _P()
+    _check(_lib.tq_cache_init(kc.handle, vc.handle, ctypes.byref(desc), ctypes.byref(h)))
+    return Cache(h.value, kc, vc, (k_codes, k_norms, v_codes, v_norms, pending_k, pending_v,
+                                   packed_len, pending_len))
+
+
+def tq_cache_destroy(cache: Cache) -> None:
+    cache.close()
+
+
+def tq_cache_state(cache: Cache):
+    """(rows packed, rows pending) per (sequence, KV head)."""
+    a, b = _I(), _I()
+    _check(_lib.tq_cache_state(cache.handle, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def tq_cache_append(cache: Cache, k, v, stream=None) -> None:
+    """Append k, v [B][Hkv][n][d] fp16 (contiguous) to the cache."""
+    if not k.is_contiguous() or not v.is_contiguous() or k.shape != v.shape:
+        raise TQError(TQ_ERR_INVALID_ARG, "k and v must be contiguous and of one shape")
+    B, Hkv, n, d = k.shape
+    pk = cache.buffers[4]
+    if (B, Hkv, d) != (pk.shape[0], pk.shape[1], pk.shape[3]):
+        raise TQError(TQ_ERR_INVALID_ARG, "rows do not match the cache's batch / heads / dim")
+    _check(_lib.tq_cache_append(cache.handle, _ptr(k), _ptr(v), n, _stream_ptr(stream)))
+
+
+def tq_cache_workspace_bytes(cache: Cache, n_q_heads: int) -> int:
+    return int(_lib.tq_cache_workspace_bytes(cache.handle, n_q_heads))
+
+
+def tq_cache_attend(cache: Cache, q, scale: float, out, workspace, stream=None) -> None:
+    """Decode attention of q [B][Hq][d] over the cache's packed and pending rows."""
+    if not q.is_contiguous() or not out.is_contiguous() or not workspace.is_contiguous():
+        raise TQError(TQ_ERR_INVALID_ARG, "q, out and workspace must be contiguous")
+    B, Hq, d = q.shape
+    if tuple(out.shape) != (B, Hq, d):
+        raise TQError(TQ_ERR_INVALID_ARG, "out shape disagrees with q")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tq_cache_attend(cache.handle, _ptr(q), Hq, float(scale), _ptr(out),
+                                _ptr(workspace), nbytes, _stream_ptr(stream)))

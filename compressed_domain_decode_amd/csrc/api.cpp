@@ -17,6 +17,15 @@ struct tq_codec {
   tq::CodecTables tabs;
 };
 
+// Host state of a two-phase cache: the caller's buffers and the two counts.
+struct tq_cache {
+  const tq_codec* kc;
+  const tq_codec* vc;
+  tq_cache_desc d;
+  int n_packed = 0, n_pending = 0;
+  bool lengths_published = false;  // the device length arrays hold the counts
+};
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -448,6 +457,181 @@ tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const v
   return decode_attend(fn, kc, vc, q_fp16, batch, 1, n_q_heads, n_kv_heads, k_codes, k_norms,
                        v_codes, v_norms, max_ctx, lengths, max_len, scale, out, workspace,
                        workspace_bytes, raw, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ two-phase cache
+
+namespace {
+
+// Rows [row0, row0 + n) of the fp16 array x ([heads][rows_per_head][dim]) as
+// an encode job writing packed positions [pos, pos + n).
+tq_encode_job cache_job(const tq_codec* c, const void* x, int rows_per_head, int row0,
+                        uint8_t* codes, float* norms, int max_ctx, int pos) {
+  const int dim = c->tabs.dim;
+  const int64_t rb = (int64_t)dim * c->tabs.bits / 8;
+  tq_encode_job j;
+  j.codec = c;
+  j.x_fp16 = (const uint16_t*)x + (int64_t)row0 * dim;
+  j.x_stride_tok = dim;
+  j.x_stride_head = (int64_t)rows_per_head * dim;
+  j.codes = codes + (int64_t)pos * rb;
+  j.c_stride_tok = rb;
+  j.c_stride_head = (int64_t)max_ctx * rb;
+  j.norms = norms + pos;
+  j.n_stride_tok = 1;
+  j.n_stride_head = max_ctx;
+  return j;
+}
+
+// One launch: K and V rows [row0, row0 + rows) of src ([heads][src_rows][dim])
+// to pending rows [dst_row0, ..) and the counts published to the length arrays.
+tq_status cache_move_rows(tq_cache* c, const char* fn, const void* src_k, const void* src_v,
+                          int src_rows, int row0, int dst_row0, int rows, void* stream) {
+  const int dim = c->kc->tabs.dim;
+  const int row16 = dim / 8;  // 16-byte words per fp16 row
+  tq::CopyRowsArgs a;
+  a.src_k = (const char*)src_k + (int64_t)row0 * dim * 2;
+  a.src_v = (const char*)src_v + (int64_t)row0 * dim * 2;
+  a.dst_k = (char*)c->d.pending_k + (int64_t)dst_row0 * dim * 2;
+  a.dst_v = (char*)c->d.pending_v + (int64_t)dst_row0 * dim * 2;
+  a.src_head = (long long)src_rows * row16;
+  a.dst_head = (long long)c->d.group_size * row16;
+  a.row16 = row16;
+  a.rows = rows;
+  a.heads = c->d.batch * c->d.n_kv_heads;
+  a.batch = c->d.batch;
+  a.n_packed = c->n_packed;
+  a.n_pending = c->n_pending;
+  a.packed_len = c->d.packed_len;
+  a.pending_len = c->d.pending_len;
+  hipError_t err = tq::launch_pending_rows(a, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+  c->lengths_published = true;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_cache_init(const tq_codec* kc, const tq_codec* vc, const tq_cache_desc* desc,
+                        tq_cache** out) {
+  const char* fn = "tq_cache_init";
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  *out = nullptr;
+  if (!kc || !vc || !desc) return fail(TQ_ERR_INVALID_ARG, "%s: NULL codec or descriptor", fn);
+  if (kc->tabs.prod || vc->tabs.prod)
+    return fail(TQ_ERR_INVALID_ARG, "%s: TurboQuant-Prod codecs are not cached here", fn);
+  if (kc->tabs.dim != vc->tabs.dim)
+    return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim, vc->tabs.dim);
+  const tq_cache_desc& d = *desc;
+  if (d.batch <= 0 || d.n_kv_heads <= 0 || d.max_ctx <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: batch %d, kv heads %d, max_ctx %d must be positive", fn,
+                d.batch, d.n_kv_heads, d.max_ctx);
+  if (d.batch > 65535 || d.n_kv_heads > 65535)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: batch or kv heads above 65535", fn);
+  if ((long long)d.batch * d.n_kv_heads > 0x7fffffffLL / 4096)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: too many (sequence, KV head) pairs", fn);
+  if (d.group_size < 1 || d.group_size > 4096)
+    return fail(TQ_ERR_INVALID_ARG, "%s: group_size %d outside 1..4096", fn, d.group_size);
+  if (!d.k_codes || !d.k_norms || !d.v_codes || !d.v_norms || !d.pending_k || !d.pending_v ||
+      !d.packed_len || !d.pending_len)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL buffer in the descriptor", fn);
+  if (((uintptr_t)d.k_codes & 15) || ((uintptr_t)d.v_codes & 15) || ((uintptr_t)d.k_norms & 3) ||
+      ((uintptr_t)d.v_norms & 3) || ((uintptr_t)d.pending_k & 15) ||
+      ((uintptr_t)d.pending_v & 15) || ((uintptr_t)d.packed_len & 3) ||
+      ((uintptr_t)d.pending_len & 3))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned buffer in the descriptor", fn);
+  tq_cache* c = new (std::nothrow) tq_cache;
+  if (!c) return fail(TQ_ERR_NOMEM, "%s: out of host memory", fn);
+  c->kc = kc;
+  c->vc = vc;
+  c->d = d;
+  *out = c;
+  return ok();
+}
+
+void tq_cache_destroy(tq_cache* c) { delete c; }
+
+tq_status tq_cache_state(const tq_cache* c, int* n_packed, int* n_pending) {
+  if (!c || !n_packed || !n_pending) return fail(TQ_ERR_INVALID_ARG, "tq_cache_state: NULL argument");
+  *n_packed = c->n_packed;
+  *n_pending = c->n_pending;
+  return ok();
+}
+
+tq_status tq_cache_append(tq_cache* c, const void* k_fp16, const void* v_fp16, int n_tok,
+                          void* stream) {
+  const char* fn = "tq_cache_append";
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  if (n_tok < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n_tok %d is negative", fn, n_tok);
+  if (n_tok == 0) return ok();
+  if (!k_fp16 || !v_fp16) return fail(TQ_ERR_INVALID_ARG, "%s: NULL rows", fn);
+  if (((uintptr_t)k_fp16 & 15) || ((uintptr_t)v_fp16 & 15))
+    return fail(TQ_ERR_INVALID_ARG, "%s: rows must be 16-byte aligned", fn);
+  const tq_cache_desc& d = c->d;
+  const long long G = d.group_size, P = c->n_pending;
+  const long long total = P + n_tok;
+  const long long groups = total / G;
+  const long long new_packed = c->n_packed + groups * G;
+  if (new_packed > d.max_ctx)
+    return fail(TQ_ERR_INVALID_ARG, "%s: %lld packed rows would exceed max_ctx %d", fn, new_packed,
+                d.max_ctx);
+  const int heads = d.batch * d.n_kv_heads;
+  tq_status st;
+  if (groups == 0) {
+    // the rows join the pending buffer
+    c->n_pending = (int)total;
+    return cache_move_rows(c, fn, k_fp16, v_fp16, n_tok, 0, (int)P, n_tok, stream) == TQ_OK
+               ? ok() : TQ_ERR_HIP;
+  }
+  // whole groups: the pending rows first, then the leading new rows
+  if (P > 0) {
+    const tq_encode_job kj = cache_job(c->kc, d.pending_k, d.group_size, 0, d.k_codes, d.k_norms,
+                                       d.max_ctx, c->n_packed);
+    const tq_encode_job vj = cache_job(c->vc, d.pending_v, d.group_size, 0, d.v_codes, d.v_norms,
+                                       d.max_ctx, c->n_packed);
+    tq_encode_job jobs[2] = {kj, vj};
+    if ((st = encode_jobs(fn, jobs, 2, (int)P, heads, stream)) != TQ_OK) return st;
+  }
+  const int from_new = (int)(groups * G - P);
+  {
+    const tq_encode_job kj = cache_job(c->kc, k_fp16, n_tok, 0, d.k_codes, d.k_norms, d.max_ctx,
+                                       c->n_packed + (int)P);
+    const tq_encode_job vj = cache_job(c->vc, v_fp16, n_tok, 0, d.v_codes, d.v_norms, d.max_ctx,
+                                       c->n_packed + (int)P);
+    tq_encode_job jobs[2] = {kj, vj};
+    if ((st = encode_jobs(fn, jobs, 2, from_new, heads, stream)) != TQ_OK) return st;
+  }
+  // the rest of the new rows start the next pending group
+  c->n_packed = (int)new_packed;
+  c->n_pending = n_tok - from_new;
+  return cache_move_rows(c, fn, k_fp16, v_fp16, n_tok, from_new, 0, c->n_pending, stream) == TQ_OK
+             ? ok() : TQ_ERR_HIP;
+}
+
+size_t tq_cache_workspace_bytes(const tq_cache* c, int n_q_heads) {
+  if (!c) return 0;
+  return tq_attend_workspace_bytes(c->d.batch, n_q_heads, c->d.n_kv_heads, c->kc->tabs.dim,
+                                   c->d.max_ctx);
+}
+
+tq_status tq_cache_attend(tq_cache* c, const void* q_fp16, int n_q_heads, float scale,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_cache_attend";
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  const tq_cache_desc& d = c->d;
+  if (!c->lengths_published) {
+    tq_status st = cache_move_rows(c, fn, d.pending_k, d.pending_v, d.group_size, 0, 0, 0, stream);
+    if (st != TQ_OK) return st;
+  }
+  return tq_decode_attend_mixed(c->kc, c->vc, q_fp16, d.batch, n_q_heads, d.n_kv_heads,
+                                d.k_codes, d.k_norms, d.v_codes, d.v_norms, d.max_ctx,
+                                d.packed_len, c->n_packed > 0 ? c->n_packed : 1, d.pending_k,
+                                d.pending_v, d.group_size, d.pending_len, scale, out, workspace,
+                                workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -94,6 +94,23 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
                          const ProdKeys& prodk, hipEvent_t ev_before, hipEvent_t ev_after,
                          hipStream_t stream);
 
+// Two-phase cache: rows [0, rows) of each of `heads` heads copied for K and V
+// (strides and row sizes in 16-byte words), and the lengths published.
+struct CopyRowsArgs {
+  const void* src_k;           // 16-byte aligned
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  long long src_head, dst_head;  // words between consecutive heads
+  int row16;                     // words per row
+  int rows, heads;               // rows may be 0 (lengths only)
+  int batch;
+  int n_packed, n_pending;
+  int32_t* packed_len;
+  int32_t* pending_len;
+};
+hipError_t launch_pending_rows(const CopyRowsArgs& a, hipStream_t stream);
+
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

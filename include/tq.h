@@ -281,6 +281,79 @@ tq_status tq_decode_attend_raw_k(const tq_codec* vc, const void* q_fp16, int bat
                                  const int32_t* lengths, int max_len, float scale, float* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Two-phase cache of one layer (PR #232, Design: keys and values stay fp16
+ * until they are batch-compressed; pending tokens are accumulated and
+ * encoded in batches, default 64). The cache holds packed rows [0, n_packed)
+ * of every (sequence, KV head) and fp16 pending rows that follow them; rows
+ * are compressed only in whole groups of group_size, so a long append (a
+ * prompt) is compressed in one batch and a decode step's row waits in the
+ * pending buffer until its group is full. Attention covers both parts.
+ * All sequences of the batch advance together (one length per cache).
+ *
+ * The caller allocates every buffer and keeps it alive until
+ * tq_cache_destroy; the cache object holds only host state (the two counts).
+ *   k_codes, k_norms, v_codes, v_norms: packed cache, as for
+ *       tq_decode_attend ([batch][n_kv_heads][max_ctx][row], 16-byte aligned).
+ *   pending_k, pending_v: fp16 [batch][n_kv_heads][group_size][dim], 16-byte
+ *       aligned.
+ *   packed_len, pending_len: device int32[batch]; the cache writes n_packed
+ *       and n_pending there (the lengths tq_decode_attend_mixed reads).
+ *   group_size: 1 .. 4096; max_ctx >= 1.
+ * Calls on one cache must be ordered by the caller (one stream, or events);
+ * they are not thread-safe.
+ */
+typedef struct tq_cache tq_cache;
+typedef struct {
+  int batch, n_kv_heads, max_ctx, group_size;
+  uint8_t* k_codes;
+  float* k_norms;
+  uint8_t* v_codes;
+  float* v_norms;
+  void* pending_k;
+  void* pending_v;
+  int32_t* packed_len;
+  int32_t* pending_len;
+} tq_cache_desc;
+
+/* Validate desc against the codecs (plain codecs of the same dim, a dim and
+ * bit widths tq_decode_attend_mixed covers) and create an empty cache. No
+ * device work is enqueued. */
+tq_status tq_cache_init(const tq_codec* kc, const tq_codec* vc, const tq_cache_desc* desc,
+                        tq_cache** out);
+void tq_cache_destroy(tq_cache* c);
+
+/* Current counts: rows compressed and rows pending, per (sequence, KV head). */
+tq_status tq_cache_state(const tq_cache* c, int* n_packed, int* n_pending);
+
+/*
+ * Append n_tok rows to every (sequence, KV head). k_fp16, v_fp16:
+ * [batch][n_kv_heads][n_tok][dim] fp16, contiguous, 16-byte aligned. Every
+ * whole group of group_size rows (pending rows first, then the new ones) is
+ * encoded into the packed cache at n_packed with tq_encode_kv's rules (bit-
+ * exact codes and norms); the remaining rows are copied to the pending
+ * buffer, and both length arrays are rewritten. Enqueues on `stream`: at most
+ * two encode launches, one copy and one length fill. Fails with
+ * TQ_ERR_INVALID_ARG before enqueueing anything when the packed rows would
+ * exceed max_ctx. n_tok == 0 does nothing.
+ */
+tq_status tq_cache_append(tq_cache* c, const void* k_fp16, const void* v_fp16, int n_tok,
+                          void* stream);
+
+/* Workspace bytes tq_cache_attend needs for n_q_heads query heads at any
+ * fill level (0 on invalid input). */
+size_t tq_cache_workspace_bytes(const tq_cache* c, int n_q_heads);
+
+/*
+ * Decode attention of q_fp16 [batch][n_q_heads][dim] over the packed and the
+ * pending rows (tq_decode_attend_mixed with the cache's buffers and lengths;
+ * the same result for any split of the rows between the two parts, up to
+ * rounding). An empty cache gives zero output rows. out, scale, workspace as
+ * for tq_decode_attend.
+ */
+tq_status tq_cache_attend(tq_cache* c, const void* q_fp16, int n_q_heads, float scale,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement hook (per calling thread): while `before` and `after` are
  * non-NULL, each tq_decode_attend launches its split-attend kernel with the
  * hipEvent_t `before` and `after` bound to that dispatch (hipExtLaunchKernel

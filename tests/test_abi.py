@@ -294,3 +294,54 @@ def test_stream_read_validation():
     assert lib.tq_stream_read(FAKE + 8, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG  # alignment
     assert lib.tq_stream_read(FAKE, 60, FAKE, None) == tq.TQ_ERR_INVALID_ARG      # size
     assert "tq_stream_read" in tq.tq_last_error()
+
+
+def _cache_desc(**kw):
+    d = dict(batch=2, n_kv_heads=2, max_ctx=256, group_size=64, k_codes=FAKE, k_norms=FAKE,
+             v_codes=FAKE, v_norms=FAKE, pending_k=FAKE, pending_v=FAKE, packed_len=FAKE,
+             pending_len=FAKE)
+    d.update(kw)
+    return tq._CacheDesc(**d)
+
+
+def _cache_init(kc, vc, desc):
+    h = ctypes.c_void_p()
+    st = tq._lib.tq_cache_init(kc.handle if kc else None, vc.handle if vc else None,
+                               ctypes.byref(desc) if desc is not None else None, ctypes.byref(h))
+    return st, h
+
+
+def test_cache_validation():
+    """Two-phase cache: descriptor checks at init, counts of an empty cache, and
+    appends refused (too many rows, bad rows) or empty, none of which launches."""
+    kc, vc = tq.tq_codec_init(128, 4, 42), tq.tq_codec_init(128, 2, 42)
+    other = tq.tq_codec_init(64, 2, 42)
+    prod = tq.tq_codec_init_prod(128, 4, 42)
+    E = tq.TQ_ERR_INVALID_ARG
+    assert _cache_init(None, vc, _cache_desc())[0] == E
+    assert _cache_init(kc, vc, None)[0] == E
+    assert _cache_init(kc, other, _cache_desc())[0] == E                    # dims differ
+    assert _cache_init(prod, vc, _cache_desc())[0] == E                     # Prod keys
+    for bad in (dict(batch=0), dict(n_kv_heads=-1), dict(max_ctx=0), dict(group_size=0),
+                dict(group_size=4097), dict(pending_k=None), dict(packed_len=None),
+                dict(k_codes=FAKE + 4), dict(pending_v=FAKE + 8), dict(pending_len=FAKE + 2)):
+        st, _ = _cache_init(kc, vc, _cache_desc(**bad))
+        assert st == E, bad
+    assert tq._lib.tq_cache_init(kc.handle, vc.handle, ctypes.byref(_cache_desc()), None) == E
+
+    st, h = _cache_init(kc, vc, _cache_desc(max_ctx=200, group_size=64))
+    assert st == tq.TQ_OK and h.value
+    cache = tq.Cache(h.value, kc, vc, ())
+    assert tq.tq_cache_state(cache) == (0, 0)
+    assert tq.tq_cache_workspace_bytes(cache, 4) == tq.tq_attend_workspace_bytes(2, 4, 2, 128, 200)
+    app = tq._lib.tq_cache_append
+    assert app(h, FAKE, FAKE, 0, None) == tq.TQ_OK                        # nothing to append
+    assert app(h, FAKE, FAKE, -1, None) == E
+    assert app(h, None, FAKE, 1, None) == E
+    assert app(h, FAKE + 8, FAKE, 1, None) == E                           # alignment
+    # 256 rows make four groups of 64: 256 packed rows > max_ctx 200
+    assert app(h, FAKE, FAKE, 256, None) == E
+    assert "max_ctx" in tq.tq_last_error()
+    assert tq.tq_cache_state(cache) == (0, 0)                             # nothing changed
+    assert app(None, FAKE, FAKE, 1, None) == E
+    cache.close()

@@ -745,3 +745,84 @@ def test_attend_prod_llama8b_shape_32k_sampled():
         want = oracle.attend_prod(ok, ov, inp.q[0:1, g * G:(g + 1) * G], okc, osk, okn, okr,
                                   ovc, ovn, np.array([L]))
         assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
+
+
+# ------------------------------------------------------------ two-phase cache
+
+@pytest.mark.parametrize("d,kb,vb,G,gsize,schedule", [
+    # a 200-row prompt (3 groups + 8 pending), decode steps up to one row short
+    # of a group, the flush, a long append that straddles the pending rows
+    (128, 4, 2, 3, 64, [200] + [1] * 55 + [1, 1, 130, 5]),
+    (64, 4, 4, 2, 16, [50] + [1] * 13 + [1, 37, 3]),
+])
+def test_cache_two_phase_matches_oracle(d, kb, vb, G, gsize, schedule):
+    """The two-phase cache against its definition: after every append the
+    first floor(rows / group) * group rows are packed exactly as the oracle
+    encodes them, the rest sit in the pending buffer as fp16, and attention
+    over the cache equals the oracle's attention over packed plus raw rows."""
+    announce(f"two-phase cache d={d} kb={kb} vb={vb} G={G} group={gsize}")
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(d + gsize)
+    B, Hkv, max_ctx = 2, 2, 512
+    Hq = G * Hkv
+    N = sum(schedule)
+    k_all = rng.standard_normal((B, Hkv, N, d)).astype(np.float16)
+    v_all = (rng.standard_normal((B, Hkv, N, d)) * 1.5).astype(np.float16)
+    kcodes = torch.zeros((B, Hkv, max_ctx, gk.row_bytes), dtype=torch.uint8, device=DEV)
+    vcodes = torch.zeros((B, Hkv, max_ctx, gv.row_bytes), dtype=torch.uint8, device=DEV)
+    knorms = torch.zeros((B, Hkv, max_ctx), dtype=torch.float32, device=DEV)
+    vnorms = torch.zeros((B, Hkv, max_ctx), dtype=torch.float32, device=DEV)
+    pk = torch.zeros((B, Hkv, gsize, d), dtype=torch.float16, device=DEV)
+    pv = torch.zeros((B, Hkv, gsize, d), dtype=torch.float16, device=DEV)
+    plen = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    rlen = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    cache = tq.tq_cache_init(gk, gv, kcodes, knorms, vcodes, vnorms, pk, pv, plen, rlen)
+    ws = torch.empty(tq.tq_cache_workspace_bytes(cache, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+
+    def attend_and_check(pos):
+        q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+        tq.tq_cache_attend(cache, to_dev(q), scale, out, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        n_packed = (pos // gsize) * gsize
+        P = pos - n_packed
+        assert plen.cpu().tolist() == [n_packed] * B and rlen.cpu().tolist() == [P] * B
+        if pos == 0:
+            assert np.all(got == 0.0)
+            return
+        npk = max(n_packed, 1)  # one row encoded, length 0, when nothing is packed
+        okc, okn, _ = oracle.encode(ok, k_all[:, :, :npk])
+        ovc, ovn, _ = oracle.encode(ov, v_all[:, :, :npk])
+        want = oracle.attend_mixed(ok, ov, q, okc, okn, ovc, ovn, np.full(B, n_packed),
+                                   k_all[:, :, n_packed:pos], v_all[:, :, n_packed:pos],
+                                   np.full(B, P), scale)
+        err = float(np.max(np.abs(got - want)))
+        assert err <= ATOL, (pos, err)
+
+    attend_and_check(0)                       # empty cache: zero rows
+    pos = 0
+    checks = {0, len(schedule) - 1, len(schedule) - 2, len(schedule) - 3, len(schedule) - 4,
+              len(schedule) // 2}
+    for i, n in enumerate(schedule):
+        tq.tq_cache_append(cache, to_dev(k_all[:, :, pos:pos + n]), to_dev(v_all[:, :, pos:pos + n]))
+        pos += n
+        n_packed = (pos // gsize) * gsize
+        assert tq.tq_cache_state(cache) == (n_packed, pos - n_packed)
+        if i in checks:
+            attend_and_check(pos)
+    torch.cuda.synchronize()
+    n_packed = (pos // gsize) * gsize
+    okc, okn, _ = oracle.encode(ok, k_all[:, :, :n_packed])
+    ovc, ovn, _ = oracle.encode(ov, v_all[:, :, :n_packed])
+    assert kcodes[:, :, :n_packed].cpu().numpy().tobytes() == okc.tobytes()
+    assert vcodes[:, :, :n_packed].cpu().numpy().tobytes() == ovc.tobytes()
+    assert knorms[:, :, :n_packed].cpu().numpy().tobytes() == okn.tobytes()
+    assert vnorms[:, :, :n_packed].cpu().numpy().tobytes() == ovn.tobytes()
+    assert np.all(kcodes[:, :, n_packed:].cpu().numpy() == 0)          # nothing past the packed rows
+    P = pos - n_packed
+    assert pk[:, :, :P].cpu().numpy().tobytes() == np.ascontiguousarray(k_all[:, :, n_packed:pos]).tobytes()
+    assert pv[:, :, :P].cpu().numpy().tobytes() == np.ascontiguousarray(v_all[:, :, n_packed:pos]).tobytes()
+    cache.close()
