@@ -826,3 +826,64 @@ def test_cache_two_phase_matches_oracle(d, kb, vb, G, gsize, schedule):
     assert pk[:, :, :P].cpu().numpy().tobytes() == np.ascontiguousarray(k_all[:, :, n_packed:pos]).tobytes()
     assert pv[:, :, :P].cpu().numpy().tobytes() == np.ascontiguousarray(v_all[:, :, n_packed:pos]).tobytes()
     cache.close()
+
+
+# ------------------------------------------------------------ graph replay
+
+def test_graph_replay_matches_eager():
+    """The timed step (append encode of K and V, then decode attention) captured
+    in a HIP graph: every replay, with eager work and synchronisations between
+    replays, gives the same bits as the eager calls, and those match the oracle."""
+    announce("graph replay of append + attend")
+    d, kb, vb, G = 128, 8, 3, 4
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(77)
+    B, Hkv, T, P = 2, 2, 3000, 64
+    Hq = G * Hkv
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    q = to_dev(rng.standard_normal((B, Hq, d)).astype(np.float16))
+    kd, vd = to_dev(k), to_dev(v)
+    kcodes, knorms = gpu_encode_cache(gk, kd[:, :, :T - P].contiguous())
+    vcodes, vnorms = gpu_encode_cache(gv, vd[:, :, :T - P].contiguous())
+    full = lambda c, n, row: (torch.cat([c, torch.zeros((B, Hkv, P) + row, dtype=c.dtype, device=DEV)], 2)
+                              .contiguous())
+    kcodes, vcodes = full(kcodes, None, (gk.row_bytes,)), full(vcodes, None, (gv.row_bytes,))
+    knorms, vnorms = full(knorms, None, ()), full(vnorms, None, ())
+    lengths = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, T), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    tm = lambda x, row: x.view(B * Hkv, T, *row).permute(1, 0, *range(2, 2 + len(row)))[T - P:T]
+
+    def step():
+        tq.tq_encode_kv(gk, tm(kd, (d,)), tm(kcodes, (gk.row_bytes,)), tm(knorms, ()),
+                        gv, tm(vd, (d,)), tm(vcodes, (gv.row_bytes,)), tm(vnorms, ()))
+        tq.tq_decode_attend(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths, T,
+                            1.0 / math.sqrt(d), out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        knorms[:, :, T - P:].fill_(-1.0)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == eager.tobytes(), f"replay {r}"
+    okc, okn, _ = oracle.encode(ok, k)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    assert kcodes.cpu().numpy().tobytes() == okc.tobytes()
+    assert knorms.cpu().numpy().tobytes() == okn.tobytes()
+    want = oracle.attend(ok, ov, q.cpu().numpy(), okc, okn, ovc, ovn, np.full(B, T, np.int32))
+    assert np.max(np.abs(eager - want)) <= ATOL
