@@ -540,6 +540,35 @@ def test_attend_mixed_no_rows_is_zero_and_raw_clamped():
     assert np.max(np.abs(got[1] - want[1])) <= ATOL
 
 
+def test_attend_mixed_raw_rows_past_length_unused():
+    """Raw rows at or past raw_lengths (and packed rows past lengths) hold NaN:
+    the result equals the one with clean buffers, bit for bit."""
+    announce("attend mixed: NaN past the raw and packed lengths")
+    d, kb, vb, G = 128, 4, 2, 3
+    gk, _ = codecs(d, kb)
+    gv, _ = codecs(d, vb)
+    rng = np.random.default_rng(11)
+    B, Hkv, T, R = 3, 2, 700, 96
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    rk = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    rv = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    q = rng.standard_normal((B, G * Hkv, d)).astype(np.float16)
+    lengths, rlen = np.array([700, 300, 0]), np.array([5, 70, 96])
+    kcodes, knorms = gpu_encode_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    clean = gpu_attend_mixed(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv, rlen)
+    rk2, rv2 = rk.copy(), rv.copy()
+    for b in range(B):
+        rk2[b, :, rlen[b]:] = np.nan
+        rv2[b, :, rlen[b]:] = np.nan
+        knorms[b, :, lengths[b]:] = float("nan")
+        vnorms[b, :, lengths[b]:] = float("nan")
+    poisoned = gpu_attend_mixed(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths, rk2, rv2, rlen)
+    assert np.all(np.isfinite(poisoned))
+    assert poisoned.tobytes() == clean.tobytes()
+
+
 def test_attend_mixed_workload_sink_prefix_full_size():
     """The 32K K8/V3 workload with its first 128 tokens kept as fp16 rows (the
     guide's --kv-min-tokens 128): sampled KV heads against the oracle."""
