@@ -437,7 +437,10 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   constexpr int kStride = WAVES * kTile;
   const int tile0 = t_begin + wave * kTile;
   TileRegs<C> ra;
-  if (wave < kGateDepth) load_tile(tile0, ra);  // in bounds even without tiles (rows clamped)
+  // a wavefront past the range end (short ranges) has no tile: it requests
+  // nothing and waits for no gate (the later ones have none either)
+  const bool has_tile = tile0 < t_end;
+  if (wave < kGateDepth && has_tile) load_tile(tile0, ra);
   auto fill = [&](unsigned char* tab, const float* c, int bits, bool pair) {
     const int rows = 1 << (pair ? 2 * bits : bits);
     const int mask = (1 << bits) - 1;
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   // wavefront w - kGateDepth has arrived. No workgroup barrier follows until
   // the merge: a wavefront may stall in issuing vector loads while the memory
   // pipeline is full, and each one runs its tiles independently.
-  if (wave >= kGateDepth) {
+  if (wave >= kGateDepth && has_tile) {
     const uint32_t ga = lds_addr(gate + (wave - kGateDepth));
     for (int i = 0; i < kGateSpins && flag_read(ga) == 0; ++i) __builtin_amdgcn_s_sleep(1);
     load_tile(tile0, ra);
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   // the first tile is peeled off the loop so that its register waits follow
   // the order its loads were issued in
-  if (tile0 < t_end) process(tile0, ra);
+  if (has_tile) process(tile0, ra);
   for (int tile = tile0 + kStride; tile < t_end; tile += kStride) process(tile, ra);
 
   // ---- merge the wavefronts of this workgroup and write the split partial
@@ -1139,11 +1142,12 @@ const SplitEntry* find_split(int d, int bk, int bv, int group) {
 
 AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
   AttendPlan p{};
-  // One workgroup per CU per round (256 CUs) and whole tiles for every
-  // wavefront of the largest (16-wavefront) workgroups.
+  // About one workgroup per CU (256 CUs), each range a whole number of
+  // 64-token tiles: short contexts get short ranges (some wavefronts of a
+  // workgroup then have no tile) rather than fewer workgroups than CUs.
   const long long units = (long long)batch * n_kv_heads;
   const long long target_wgs = 256;
-  const long long quantum = 16 * kTile;
+  const long long quantum = kTile;
   long long tps = ((long long)max_len * units + target_wgs - 1) / target_wgs;
   tps = ((tps + quantum - 1) / quantum) * quantum;
   if (tps < quantum) tps = quantum;
