@@ -260,6 +260,20 @@ def test_attend_ragged_edge_lengths(d, kb, vb, G):
     assert np.abs(got - want).max() <= ATOL
 
 
+def test_attend_many_splits_per_head():
+    """One KV head and a long context: the planner cuts 64-token-tile ranges
+    to fill the CUs, so a head has far more splits than the combine folds in
+    one pass (32), with a short last split."""
+    announce("attend many splits per head")
+    d, kb, vb, G, L = 128, 8, 3, 4, 20000
+    assert tq.tq_attend_num_splits(1, G, 1, d, L) > 64
+    got, want = _attend_case(d, kb, vb, G, lengths=[L], Hkv=1, seed=23)
+    assert np.abs(got - want).max() <= ATOL
+    # a batch of two with ragged lengths: the shorter sequence leaves splits empty
+    got, want = _attend_case(d, kb, vb, G, lengths=[L, 7001], Hkv=1, seed=24)
+    assert np.abs(got - want).max() <= ATOL
+
+
 def test_attend_zero_length_and_single_token():
     announce("attend zero length / single token")
     d, kb, vb, G = 128, 8, 3, 4
@@ -538,6 +552,30 @@ def test_attend_mixed_no_rows_is_zero_and_raw_clamped():
     ovc, ovn, _ = oracle.encode(ov, v)
     want = oracle.attend_mixed(ok, ov, q, okc, okn, ovc, ovn, lengths, rk, rv, np.array([0, R]))
     assert np.max(np.abs(got[1] - want[1])) <= ATOL
+
+
+def test_attend_mixed_maximum_raw_rows():
+    """The raw segment at its maximum, 4096 fp16 rows per (sequence, KV head),
+    with a packed part, against the oracle."""
+    announce("attend mixed: 4096 raw rows")
+    d, kb, vb, G = 128, 4, 2, 3
+    gk, ok = codecs(d, kb)
+    gv, ov = codecs(d, vb)
+    rng = np.random.default_rng(29)
+    B, Hkv, T, R = 1, 2, 1000, 4096
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    rk = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    rv = rng.standard_normal((B, Hkv, R, d)).astype(np.float16)
+    q = rng.standard_normal((B, G * Hkv, d)).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(gk, to_dev(k))
+    vcodes, vnorms = gpu_encode_cache(gv, to_dev(v))
+    lengths, rlen = np.array([T]), np.array([R])
+    got = gpu_attend_mixed(gk, gv, q, kcodes, knorms, vcodes, vnorms, lengths, rk, rv, rlen)
+    okc, okn, _ = oracle.encode(ok, k)
+    ovc, ovn, _ = oracle.encode(ov, v)
+    want = oracle.attend_mixed(ok, ov, q, okc, okn, ovc, ovn, lengths, rk, rv, rlen)
+    assert np.max(np.abs(got - want)) <= ATOL
 
 
 def test_attend_mixed_raw_rows_past_length_unused():
