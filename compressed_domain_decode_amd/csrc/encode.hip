@@ -191,13 +191,16 @@ __device__ __forceinline__ void wht_vector(double (&u)[E], int sub) {
         u[e] = p + q;
         u[e + hs] = p - q;
       }
+  // partner p, own value u: the lower lane keeps u + p, the upper p - u. Both
+  // are fma(u, s, p) with s = +-1: the product is exact, so the one rounding
+  // is that of the sum or difference (the same bits, signed zeros included).
   auto cross = [&](auto mtag) __attribute__((always_inline)) {
     constexpr int m = decltype(mtag)::value;
-    const bool upper = (sub & m) != 0;
+    const double s = (sub & m) != 0 ? -1.0 : 1.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const double pv = xor_lane_f64<m>(u[e]);
-      u[e] = upper ? (pv - u[e]) : (u[e] + pv);
+      u[e] = __builtin_fma(u[e], s, pv);
     }
   };
   if constexpr (L > 1) cross(std::integral_constant<int, 1>{});
