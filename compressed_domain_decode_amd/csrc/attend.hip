@@ -174,7 +174,7 @@ struct CfgBase {
   static constexpr int GATE_BYTES = (WAVES * 4 + 15) / 16 * 16;  // first-tile arrival flags
   static constexpr int MAIN_BYTES =
       VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + CEN_BYTES + GATE_BYTES;
-  static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * D) * 4;
+  static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * NHG * D) * 4;
   static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
 };
@@ -783,77 +783,61 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   if (has_tile) process(tile0, ra);
   for (int tile = tile0 + kStride; tile < t_end; tile += kStride) process(tile, ra);
 
-  // ---- merge the wavefronts of this workgroup and write the split partial
-  float lsum[NHG][4];
-#pragma unroll
-  for (int hg = 0; hg < NHG; ++hg)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) lsum[hg][v] = wave_sum(l_run[hg][v]);
+  // ---- merge the wavefronts of this workgroup and write the split partial:
+  //      every wavefront stores its maxima, sums and unscaled accumulators,
+  //      then thread (virtual head, coordinate) folds the wavefronts with the
+  //      factors 2^(m_w - M), M their maximum (a wavefront that saw no row
+  //      has the finite sentinel maximum, so it weighs 0 next to one that did)
   if constexpr (C::NVS == 1 && !C::VPAIR) {
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) acc[0][hg] += acc[1][hg];
   }
   __syncthreads();  // all wavefronts are done with tables and buffers
-  float* mbuf = (float*)lds;                    // [WAVES][4 NHG] maxima
-  float* abuf = mbuf + WAVES * 4 * NHG * 2;     // [WAVES][4][D] rescaled accumulators
-  if (lane == 0) {
-#pragma unroll
-    for (int hg = 0; hg < NHG; ++hg)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mbuf[wave * 4 * NHG + 4 * hg + v] = m_run[hg][v];
-  }
-  __syncthreads();
-  // this wavefront's factor 2^(m_w - M) per head, M the workgroup maximum
-  float fw[NHG][4];
+  constexpr int NV = 4 * NHG;                   // virtual-head slots per wavefront
+  float* mbuf = (float*)lds;                    // [WAVES][NV] maxima
+  float* lbuf = mbuf + WAVES * NV;              // [WAVES][NV] sums
+  float* abuf = lbuf + WAVES * NV;              // [WAVES][NV][D] accumulators
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float M = -INFINITY;
-      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[w * 4 * NHG + 4 * hg + v]);
-      // 0 for a wavefront that saw no row while another did (kNoRow - M)
-      fw[hg][v] = exp2f(m_run[hg][v] - M);
-      if (lane == 0) mbuf[WAVES * 4 * NHG + wave * 4 * NHG + 4 * hg + v] = fw[hg][v] * lsum[hg][v];
-    }
-  const int S = gridDim.x;
-  sfor<NHG>([&](auto HGI) {
-    constexpr int hg = HGI;
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float* dst = abuf + (wave * 4 + v) * D;
-      const float f = fw[hg][v];
+      const float lsum = wave_sum(l_run[hg][v]);
+      if (lane == 0) {
+        mbuf[wave * NV + 4 * hg + v] = m_run[hg][v];
+        lbuf[wave * NV + 4 * hg + v] = lsum;
+      }
+      float* dst = abuf + (wave * NV + 4 * hg + v) * D;
       if constexpr (C::VPAIR) {
 #pragma unroll
         for (int k = 0; k < C::NVS; ++k) {
-          dst[2 * (64 * k + lane)] = acc[2 * k][hg][v] * f;
-          dst[2 * (64 * k + lane) + 1] = acc[2 * k + 1][hg][v] * f;
+          dst[2 * (64 * k + lane)] = acc[2 * k][hg][v];
+          dst[2 * (64 * k + lane) + 1] = acc[2 * k + 1][hg][v];
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = acc[k][hg][v] * f;
+        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = acc[k][hg][v];
       }
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WAVES) {
-      const int v = idx / D, j = idx - v * D;
-      const int h = 4 * hg + v;
-      if (h >= GV) continue;
-      float a = 0.f;
-      for (int w = 0; w < WAVES; ++w) a += abuf[(w * 4 + v) * D + j];
-      const long long prow = (((long long)b * n_kv_heads + g) * GV + h) * S + split;
-      part_acc[prow * D + j] = a;
-      if (j == 0) {
-        float M = -INFINITY, L = 0.f;
-        for (int w = 0; w < WAVES; ++w) {
-          M = fmaxf(M, mbuf[w * 4 * NHG + h]);
-          L += mbuf[WAVES * 4 * NHG + w * 4 * NHG + h];
-        }
-        part_ml[prow * 2] = M;
-        part_ml[prow * 2 + 1] = L;
-      }
+  __syncthreads();
+  const int S = gridDim.x;
+  for (int idx = threadIdx.x; idx < NV * D; idx += 64 * WAVES) {
+    const int h = idx / D, j = idx - h * D;
+    if (h >= GV) continue;
+    float M = -INFINITY;
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[w * NV + h]);
+    float a = 0.f, L = 0.f;
+    for (int w = 0; w < WAVES; ++w) {
+      const float f = exp2f(mbuf[w * NV + h] - M);
+      a += f * abuf[(w * NV + h) * D + j];
+      L += f * lbuf[w * NV + h];
     }
-  });
+    const long long prow = (((long long)b * n_kv_heads + g) * GV + h) * S + split;
+    part_acc[prow * D + j] = a;
+    if (j == 0) {
+      part_ml[prow * 2] = M;
+      part_ml[prow * 2 + 1] = L;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- 2. combine
