@@ -104,27 +104,23 @@ def measured_traffic(workload):
 
 def read_calibration(nbytes, ncopies, warmup, steps):
     """A plain streaming read (tq_stream_read) of the same byte count, cold: cycled
-    through as many buffers as there are cache copies. The bandwidth a kernel
-    reading that much can reach on this device: the measured ceiling."""
+    through as many buffers as there are cache copies, back to back in a graph
+    replay as the timed steps run. The bandwidth a kernel reading that much can
+    reach on this device: the measured ceiling."""
     import torch
     import compressed_domain_decode_amd as tq
     n16 = max(1, nbytes // 16)
     bufs = [torch.ones(n16 * 4, dtype=torch.int32, device="cuda:0") for _ in range(ncopies)]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    for i in range(warmup):
+
+    def read(i):
         tq.tq_stream_read(bufs[i % ncopies], sink)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        tq.tq_stream_read(bufs[i % ncopies], sink)
-        b.record()
-    torch.cuda.synchronize()
-    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+    us = graph_us_per_call(read, ncopies, max(2, (steps + ncopies - 1) // ncopies))
     del bufs
     return {"kernel": "stream_read_kernel (tq_stream_read)", "bytes": n16 * 16,
-            "us_median": round(us, 3), "GBps": round(n16 * 16 / (us * 1e-6) / 1e9, 2)}
+            "timing": "graph replay, per call", "us": round(us, 3),
+            "GBps": round(n16 * 16 / (us * 1e-6) / 1e9, 2)}
 
 
 def graph_us_per_call(fn, ncalls, reps):
