@@ -689,8 +689,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float sv = tile + lane < vlim[hg][v] ? s[v] : -INFINITY;
-        const float mt = wave_max(sv);
-        if (mt > m_run[hg][v] + kRescaleSlack) {  // wavefront-uniform
+        // the tile maximum exceeds m_run + slack iff some lane's score does:
+        // one compare and a ballot decide it, and the maximum itself is only
+        // taken then (always on a wavefront's first tile, rarely after)
+        if (__ballot(sv > m_run[hg][v] + kRescaleSlack) != 0ull) {  // wavefront-uniform
+          const float mt = wave_max(sv);
           const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
           l_run[hg][v] *= alpha;
 #pragma unroll
