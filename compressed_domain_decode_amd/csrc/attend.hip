@@ -101,6 +101,22 @@ __device__ __forceinline__ float wave_max(float v) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+// Maximum over the wavefront of finite or -inf scores, returned in every lane:
+// the same DPP pattern on an order-preserving integer key (the bits, with the
+// magnitude bits flipped for negative values), so each step is one fused
+// v_max_i32_dpp with no NaN quieting, and the maximum is exact.
+__device__ __forceinline__ float wave_max_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  int k = b ^ ((b >> 31) & 0x7FFFFFFF);
+  constexpr int kLow = (int)0x80000000;  // identity of the max for the DPP's inactive sources
+  k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x140, 0xF, 0xF, false));  // row_mirror
+  const int r = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+                    max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+  return __builtin_bit_cast(float, r ^ ((r >> 31) & 0x7FFFFFFF));
+}
 // Sum over the wavefront, returned in every lane (same DPP pattern).
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);
@@ -693,7 +709,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         // one compare and a ballot decide it, and the maximum itself is only
         // taken then (always on a wavefront's first tile, rarely after)
         if (__ballot(sv > m_run[hg][v] + kRescaleSlack) != 0ull) {  // wavefront-uniform
-          const float mt = wave_max(sv);
+          const float mt = wave_max_key(sv);
           const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
           l_run[hg][v] *= alpha;
 #pragma unroll
