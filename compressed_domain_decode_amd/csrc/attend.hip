@@ -235,6 +235,14 @@ struct Cfg : CfgBase<D, BK, BV, NHG, cfg_waves<D, BK, BV, NHG>()> {
   static_assert(B::VT_BYTES < 65536, "K table base must fit a DS offset");
   static_assert(CfgBase<D, BK, BV, NHG, 4>::LDS_BYTES <= kLdsPerCU, "LDS budget");
 };
+// The same kernel with 4 wavefronts, for ranges of at most 4 tiles (short
+// contexts): a 16-wavefront workgroup would leave 12 or more without a tile
+// yet launch, synchronise and merge them all.
+template <int D, int BK, int BV, int NHG>
+struct CfgShort : CfgBase<D, BK, BV, NHG, 4> {
+  static_assert(Cfg<D, BK, BV, NHG>::WAVES >= 4, "a full configuration exists");
+};
+constexpr int kShortTiles = 4;  // ranges up to this many tiles use the short workgroup
 
 // One tile's worth of this lane's token: packed K and V rows and the norms.
 template <class C>
@@ -1101,20 +1109,26 @@ typedef hipError_t (*SplitFn)(const AttendPlan&, int, int, int, int, const void*
 struct SplitEntry {
   int d, bk, bv, nhg;
   SplitFn fn;
+  SplitFn short_fn;  // 4-wavefront workgroups for ranges of <= kShortTiles tiles, or null
 };
 
 // Instantiated (head_dim, K bits, V bits, groups of 4 query heads). A group
 // size G is served by the entry with the smallest nhg such that G <= 4 * nhg.
-#define TQ_SPLIT(D, BK, BV, NHG) {D, BK, BV, NHG, &launch_split<Cfg<D, BK, BV, NHG>>}
+// TQ_SPLIT_S entries also have the short-range variant (the small-context
+// workloads' configurations).
+#define TQ_SPLIT(D, BK, BV, NHG) {D, BK, BV, NHG, &launch_split<Cfg<D, BK, BV, NHG>>, nullptr}
+#define TQ_SPLIT_S(D, BK, BV, NHG)                                      \
+  {D, BK, BV, NHG, &launch_split<Cfg<D, BK, BV, NHG>>,                  \
+   &launch_split<CfgShort<D, BK, BV, NHG>>}
 const SplitEntry kSplitTable[] = {
     // head_dim 64
-    TQ_SPLIT(64, 4, 4, 1), TQ_SPLIT(64, 3, 3, 2), TQ_SPLIT(64, 3, 3, 1),
+    TQ_SPLIT_S(64, 4, 4, 1), TQ_SPLIT(64, 3, 3, 2), TQ_SPLIT(64, 3, 3, 1),
     TQ_SPLIT(64, 8, 3, 1), TQ_SPLIT(64, 2, 2, 1), TQ_SPLIT(64, 1, 1, 1),
     TQ_SPLIT(64, 5, 7, 1), TQ_SPLIT(64, 6, 6, 4), TQ_SPLIT(64, 4, 4, 2),
     TQ_SPLIT(64, 8, 3, 2), TQ_SPLIT(64, 3, 3, 4), TQ_SPLIT(64, 16, 4, 1), TQ_SPLIT(64, 16, 4, 2),
     TQ_SPLIT(64, 35, 4, 1),
     // head_dim 128
-    TQ_SPLIT(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
+    TQ_SPLIT_S(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
     TQ_SPLIT(128, 4, 4, 1), TQ_SPLIT(128, 4, 3, 1), TQ_SPLIT(128, 2, 2, 1),
     TQ_SPLIT(128, 8, 4, 1), TQ_SPLIT(128, 4, 4, 2), TQ_SPLIT(128, 8, 3, 2),
     TQ_SPLIT(128, 1, 1, 1), TQ_SPLIT(128, 7, 5, 2),
@@ -1131,6 +1145,7 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2),
 };
 #undef TQ_SPLIT
+#undef TQ_SPLIT_S
 
 const SplitEntry* find_split(int d, int bk, int bv, int group) {
   const SplitEntry* best = nullptr;
@@ -1192,9 +1207,10 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
   pa.rnorms = prodk.rnorms;
   pa.sign = prodk.sign;
   pa.uscale = qscale * 1.2533141373155003f / (float)dim;  // sqrt(pi/2) / d
-  err = ent->fn(plan, batch, n_kv_heads, group, n_qtok, q, k_codes, k_norms, v_codes, v_norms,
-                lengths, max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, pa, ev_before,
-                ev_after, stream);
+  const SplitFn fn =
+      ent->short_fn && plan.tokens_per_split <= kShortTiles * kTile ? ent->short_fn : ent->fn;
+  err = fn(plan, batch, n_kv_heads, group, n_qtok, q, k_codes, k_norms, v_codes, v_norms, lengths,
+           max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, pa, ev_before, ev_after, stream);
   if (err != hipSuccess) return err;
   if (raw.lengths && n_qtok != 1) return hipErrorInvalidValue;
   RawArgs ra;
