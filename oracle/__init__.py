@@ -63,7 +63,12 @@ def _load():
             att = [I, I, I, P, P, P, P, P, I, I, I, P, P, P, P, I, P, ctypes.c_double, P, I, P]
             lib.orc_attend.argtypes = att
             lib.orc_attend_rotated.argtypes = att
-            for f in ("orc_signs", "orc_encode", "orc_dequant", "orc_attend", "orc_attend_rotated"):
+            lib.orc_encode_dense.argtypes = [I, I, P, P, P, I64, I64, P, P, P, P]
+            lib.orc_dequant_dense.argtypes = [I, I, P, P, P, P, I64, P]
+            lib.orc_tree_sum.argtypes = [P, I]
+            lib.orc_tree_sum.restype = ctypes.c_double
+            for f in ("orc_signs", "orc_encode", "orc_dequant", "orc_attend", "orc_attend_rotated",
+                      "orc_encode_dense", "orc_dequant_dense"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -290,6 +295,91 @@ def attend_raw_k(vc, q, k, v_codes, v_norms, lengths, scale=None):
             v_hat = dequant(vc, v_codes[b, g, :L], v_norms[b, g, :L])
             for h in range(g * G, (g + 1) * G):
                 s = scale * (k[b, g, :L] @ q[b, h])
+                p = np.exp(s - s.max())
+                out[b, h] = (p / p.sum()) @ v_hat
+    return out
+
+
+# ------------------------------------------------------------------ dense rotation
+
+class DenseCodec:
+    """A codec whose rotation is a dense matrix given by the caller (head dims
+    that are not a power of two; PR #232, Known limitations: dense rotation
+    otherwise). m is d x d with m / sqrt(d) orthogonal: z = m x / |x|.
+    Lloyd-Max tables as for the Walsh-Hadamard codec."""
+
+    def __init__(self, m: np.ndarray, bits: int):
+        m = np.ascontiguousarray(m, dtype=np.float64)
+        assert m.ndim == 2 and m.shape[0] == m.shape[1]
+        self.dim, self.bits, self.m = m.shape[0], bits, m
+        c, b = codebook.tables(bits)
+        self.centroids = np.ascontiguousarray(c, dtype=np.float32)
+        self.boundaries = np.ascontiguousarray(b, dtype=np.float32)
+
+    @property
+    def row_bytes(self) -> int:
+        return self.dim * self.bits // 8
+
+
+def tree_sum(v: np.ndarray) -> float:
+    """The any-count pairwise tree the dense codec sums squares over."""
+    v = np.ascontiguousarray(v, dtype=np.float64).reshape(-1)
+    return float(_load().orc_tree_sum(_p(v), v.size))
+
+
+def encode_dense(codec: DenseCodec, x: np.ndarray, want_z: bool = False):
+    """encode() with the dense rotation: returns (codes, norms, norms64, [z])."""
+    x = np.asarray(x)
+    lead = x.shape[:-1]
+    d = x.shape[-1]
+    assert d == codec.dim
+    xd = np.ascontiguousarray(x.reshape(-1, d), dtype=np.float64)
+    n = xd.shape[0]
+    codes = np.zeros((n, codec.row_bytes), dtype=np.uint8)
+    norms = np.zeros(n, dtype=np.float32)
+    norms64 = np.zeros(n, dtype=np.float64)
+    z = np.zeros((n, d), dtype=np.float64) if want_z else None
+    _check(_load().orc_encode_dense(d, codec.bits, _p(codec.m), _p(codec.boundaries), _p(xd),
+                                    n, d, _p(codes), _p(norms), _p(norms64),
+                                    _p(z) if want_z else None), "encode_dense")
+    out = (codes.reshape(*lead, codec.row_bytes), norms.reshape(lead), norms64.reshape(lead))
+    if want_z:
+        out = out + (z.reshape(*lead, d),)
+    return out
+
+
+def dequant_dense(codec: DenseCodec, codes: np.ndarray, norms: np.ndarray) -> np.ndarray:
+    lead = np.asarray(norms).shape
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, codec.row_bytes)
+    nr = np.ascontiguousarray(norms, dtype=np.float32).reshape(-1)
+    out = np.zeros((nr.size, codec.dim), dtype=np.float64)
+    _check(_load().orc_dequant_dense(codec.dim, codec.bits, _p(codec.m), _p(codec.centroids),
+                                     _p(c), _p(nr), nr.size, _p(out)), "dequant_dense")
+    return out.reshape(*lead, codec.dim)
+
+
+def attend_dense(kc: DenseCodec, vc: DenseCodec, q, k_codes, k_norms, v_codes, v_norms,
+                 lengths, scale=None):
+    """Softmax attention over the dequantised cache of dense-rotation codecs,
+    written out directly in fp64 (the fused kernel's output equals the
+    expand-then-attend path: turboquant-mlx KV-cache guide). q: [B][Hq][d];
+    codes [B][Hkv][T][row]; norms [B][Hkv][T]. Returns [B][Hq][d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = np.asarray(k_norms).shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L = max(int(lengths[b]), 0)
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            k_hat = dequant_dense(kc, k_codes[b, g, :L], k_norms[b, g, :L])
+            v_hat = dequant_dense(vc, v_codes[b, g, :L], v_norms[b, g, :L])
+            for h in range(g * G, (g + 1) * G):
+                s = scale * (k_hat @ q[b, h])
                 p = np.exp(s - s.max())
                 out[b, h] = (p / p.sum()) @ v_hat
     return out

@@ -376,3 +376,96 @@ int orc_attend_rotated(int d, int k_bits, int v_bits,
   free(h); free(u); free(qt); free(a); free(y); free(idx); free(s);
   return ORC_OK;
 }
+
+/* ---------------------------------------------------------------- dense rotation
+ * Head dims that are not a power of two have no Walsh-Hadamard transform; the
+ * pages' fallback is a dense rotation (PR #232, Known limitations: dense
+ * rotation otherwise; VeloxQuant "How I built", Stage 1: the original method
+ * draws the rotation as the Q factor of a Gaussian matrix). Here the rotation
+ * is an input: m is d x d, row-major, equal to sqrt(d) times an orthogonal
+ * matrix, so that z = m x / |x| is N(0,1)-scaled like H(sigma x) / |x|, and
+ * m = H diag(sigma) reproduces the Walsh-Hadamard codec exactly.
+ */
+
+/* Pairwise tree for any count: each level adds neighbouring pairs in index
+ * order and carries an odd last element up unchanged (for d = 2^k this is the
+ * canonical tree above). */
+static double pairwise_tree_sum_any(const double* v, int d, double* scratch) {
+  memcpy(scratch, v, sizeof(double) * (size_t)d);
+  for (int w = d; w > 1; w = (w + 1) / 2) {
+    for (int i = 0; i < w / 2; ++i) scratch[i] = scratch[2 * i] + scratch[2 * i + 1];
+    if (w & 1) scratch[w / 2] = scratch[w - 1];
+  }
+  return scratch[0];
+}
+
+/* y = m x: products and sums in index order, no fused multiply-add. */
+static void matvec(const double* m, int d, const double* x, double* y) {
+  for (int i = 0; i < d; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j) acc += m[(size_t)i * d + j] * x[j];
+    y[i] = acc;
+  }
+}
+
+/* Exposed for tests: the any-count pairwise tree. */
+double orc_tree_sum(const double* v, int d) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+  if (!s) return NAN;
+  double r = d > 0 ? pairwise_tree_sum_any(v, d, s) : 0.0;
+  free(s);
+  return r;
+}
+
+int orc_encode_dense(int d, int bits, const double* m, const float* boundaries,
+                     const double* x, int64_t n, int64_t x_stride, uint8_t* codes,
+                     float* norms, double* norms64, double* z_out) {
+  if (d < 1 || bits < 1 || bits > 8 || (d * bits) % 8) return ORC_BAD;
+  int nb = (1 << bits) - 1;
+  int row_bytes = d * bits / 8;
+  double* w = (double*)malloc(sizeof(double) * (size_t)d);
+  double* sq = (double*)malloc(sizeof(double) * (size_t)d);
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)d);
+  if (!w || !sq || !tmp || !idx) {
+    free(w); free(sq); free(tmp); free(idx);
+    return ORC_NOMEM;
+  }
+  for (int64_t v = 0; v < n; ++v) {
+    const double* xv = x + v * x_stride;
+    for (int j = 0; j < d; ++j) sq[j] = xv[j] * xv[j];
+    double nrm = sqrt(pairwise_tree_sum_any(sq, d, tmp));
+    matvec(m, d, xv, w);
+    for (int i = 0; i < d; ++i) {
+      double z = (nrm == 0.0) ? 0.0 : w[i] / nrm;
+      if (z_out) z_out[v * d + i] = z;
+      idx[i] = bucketize(z, boundaries, nb);
+    }
+    orc_pack(d, bits, idx, codes + v * row_bytes);
+    norms[v] = (float)nrm;
+    if (norms64) norms64[v] = nrm;
+  }
+  free(w); free(sq); free(tmp); free(idx);
+  return ORC_OK;
+}
+
+/* x_hat = (norm / d) m^T c[idx]: the inverse of z = m x / |x| when m / sqrt(d)
+ * is orthogonal. */
+int orc_dequant_dense(int d, int bits, const double* m, const float* centroids,
+                      const uint8_t* codes, const float* norms, int64_t n, double* out) {
+  if (d < 1 || bits < 1 || bits > 8 || (d * bits) % 8) return ORC_BAD;
+  int row_bytes = d * bits / 8;
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)d);
+  if (!idx) return ORC_NOMEM;
+  for (int64_t v = 0; v < n; ++v) {
+    orc_unpack(d, bits, codes + v * row_bytes, idx);
+    double s = (double)norms[v] / (double)d;
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += m[(size_t)i * d + j] * (double)centroids[idx[i]];
+      out[v * d + j] = s * acc;
+    }
+  }
+  free(idx);
+  return ORC_OK;
+}

@@ -132,6 +132,19 @@ def small_case(seed: int, batch: int, n_q_heads: int, n_kv_heads: int, dim: int,
     return lengths, k, v, q
 
 
+def rotation_matrix(dim: int, seed: int) -> np.ndarray:
+    """A Haar-random rotation for head dims with no Walsh-Hadamard transform,
+    scaled by sqrt(dim): the Q factor of a standard Gaussian matrix with the
+    signs of R's diagonal moved into it (Mezzadri 2007), drawn from
+    numpy.random.default_rng(seed). It is a random input of the method, drawn
+    here once and handed to both sides as the same fp64 matrix."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((dim, dim))
+    qm, r = np.linalg.qr(g)
+    qm = qm * np.sign(np.diag(r))
+    return np.ascontiguousarray(qm * math.sqrt(dim), dtype=np.float64)
+
+
 def algorithmic_bytes(lengths, n_kv_heads: int, dim: int, k_bits: int, v_bits: int) -> int:
     """Bytes the decode-attend must read: packed K and V codes plus fp32 norms."""
     per_tok = (dim * k_bits // 8 + 4) + (dim * v_bits // 8 + 4)
