@@ -35,7 +35,7 @@ EXPORTED = (
     "tq_codec_init_prod", "tq_encode_prod", "tq_decode_attend_prod", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
     "tq_cache_init", "tq_cache_destroy", "tq_cache_state", "tq_cache_append",
-    "tq_cache_workspace_bytes", "tq_cache_attend",
+    "tq_cache_workspace_bytes", "tq_cache_attend", "tq_codec_init_dense",
 )
 
 
@@ -62,6 +62,8 @@ _I = ctypes.c_int
 _I64 = ctypes.c_int64
 _lib.tq_codec_init.argtypes = [_I, _I, ctypes.c_uint64, ctypes.POINTER(_P)]
 _lib.tq_codec_init.restype = _I
+_lib.tq_codec_init_dense.argtypes = [_I, _I, _P, ctypes.POINTER(_P)]
+_lib.tq_codec_init_dense.restype = _I
 _lib.tq_codec_destroy.argtypes = [_P]
 _lib.tq_codec_destroy.restype = None
 _lib.tq_codec_tables.argtypes = [_P, _P, _P, _P]
@@ -210,6 +212,26 @@ def tq_codec_init(dim: int, bits: int, seed: int) -> Codec:
     h = ctypes.c_void_p()
     _check(_lib.tq_codec_init(dim, bits, ctypes.c_uint64(seed), ctypes.byref(h)))
     return Codec(h.value, dim, bits, seed)
+
+
+class DenseCodec(Codec):
+    """A dense-rotation codec (head dims with no Walsh-Hadamard transform)."""
+
+    def __repr__(self):
+        return f"DenseCodec(dim={self.dim}, bits={self.bits})"
+
+
+def tq_codec_init_dense(dim: int, bits: int, rotation) -> DenseCodec:
+    """rotation: dim x dim fp64 array (sqrt(dim) times an orthogonal matrix),
+    copied by the library."""
+    import numpy as _np
+    m = _np.ascontiguousarray(rotation, dtype=_np.float64)
+    if m.shape != (dim, dim):
+        raise ValueError(f"rotation must be {dim} x {dim}, got {m.shape}")
+    h = ctypes.c_void_p()
+    _check(_lib.tq_codec_init_dense(dim, bits, m.ctypes.data_as(ctypes.c_void_p),
+                                    ctypes.byref(h)))
+    return DenseCodec(h.value, dim, bits, 0)
 
 
 class ProdCodec(Codec):

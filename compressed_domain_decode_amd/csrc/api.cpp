@@ -15,6 +15,10 @@
 
 struct tq_codec {
   tq::CodecTables tabs;
+  // dense-rotation codecs: the rotation and its transpose on the device
+  bool dense = false;
+  double* m_dev = nullptr;
+  double* mt_dev = nullptr;
 };
 
 // Host state of a two-phase cache: the caller's buffers and the two counts.
@@ -48,6 +52,7 @@ tq_status ok() {
 }
 
 bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool dense_dim_ok(int d) { return d >= 32 && d <= tq::kMaxDim && d % 32 == 0; }
 
 tq::SignArg sign_arg(const tq_codec* c) {
   tq::SignArg s;
@@ -77,6 +82,8 @@ tq_status encode_jobs(const char* fn, const tq_encode_job* jobs, int n_jobs, int
     if (j.codec->tabs.dim != jobs[0].codec->tabs.dim)
       return fail(TQ_ERR_INVALID_ARG, "%s: codecs of different dim (%d, %d)", fn,
                   jobs[0].codec->tabs.dim, j.codec->tabs.dim);
+    if (j.codec->dense != jobs[0].codec->dense)
+      return fail(TQ_ERR_INVALID_ARG, "%s: dense-rotation and Walsh-Hadamard codecs mixed", fn);
   }
   if (n_tok < 0 || n_head < 0)
     return fail(TQ_ERR_INVALID_ARG, "%s: negative count (n_tok %d, n_head %d)", fn, n_tok,
@@ -129,6 +136,33 @@ tq_status encode_jobs(const char* fn, const tq_encode_job* jobs, int n_jobs, int
   const long long nvec = (long long)n_tok * n_head;
   if (nvec > 0x7fffffffLL - 64)
     return fail(TQ_ERR_UNSUPPORTED, "%s: more than 2^31 - 65 vectors", fn);
+  if (jobs[0].codec->dense) {  // one launch per job
+    for (int i = 0; i < n_jobs; ++i) {
+      const tq_codec* c = jobs[i].codec;
+      const tq::EncodeJob& e = args.job[i];
+      tq::DenseEncodeArgs da;
+      std::memset(&da, 0, sizeof(da));
+      da.x = e.x;
+      da.xs_tok = e.xs_tok;
+      da.xs_head = e.xs_head;
+      da.codes = e.codes;
+      da.cs_tok = e.cs_tok;
+      da.cs_head = e.cs_head;
+      da.norms = e.norms;
+      da.ns_tok = e.ns_tok;
+      da.ns_head = e.ns_head;
+      da.mt = c->mt_dev;
+      da.dim = c->tabs.dim;
+      da.bits = c->tabs.bits;
+      da.n_tok = n_tok;
+      da.n_head = n_head;
+      std::memcpy(da.boundaries, c->tabs.boundaries, sizeof(float) * ((1 << da.bits) - 1));
+      const hipError_t err = tq::launch_encode_dense(da, (hipStream_t)stream);
+      if (err != hipSuccess)
+        return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    }
+    return ok();
+  }
   hipError_t err = tq::launch_encode(jobs[0].codec->tabs.dim, args, (hipStream_t)stream);
   if (err != hipSuccess)
     return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
@@ -192,7 +226,56 @@ tq_status tq_codec_init_prod(int dim, int bits, uint64_t seed, tq_codec** out) {
   return ok();
 }
 
-void tq_codec_destroy(tq_codec* c) { delete c; }
+tq_status tq_codec_init_dense(int dim, int bits, const double* rotation, tq_codec** out) {
+  const char* fn = "tq_codec_init_dense";
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  *out = nullptr;
+  if (!rotation) return fail(TQ_ERR_INVALID_ARG, "%s: rotation is NULL", fn);
+  if (!dense_dim_ok(dim))
+    return fail(TQ_ERR_UNSUPPORTED, "%s: dim %d not a multiple of 32 in [32, 256]", fn, dim);
+  if (bits < 1 || bits > 8) return fail(TQ_ERR_UNSUPPORTED, "%s: bits %d not in [1, 8]", fn, bits);
+  const size_t n = (size_t)dim * dim;
+  for (size_t i = 0; i < n; ++i)
+    if (!(rotation[i] - rotation[i] == 0.0))
+      return fail(TQ_ERR_INVALID_ARG, "%s: rotation entry %zu is not finite", fn, i);
+  tq_codec* c = new (std::nothrow) tq_codec;
+  if (!c) return fail(TQ_ERR_NOMEM, "%s: out of host memory", fn);
+  if (!tq::build_codec(dim, bits, 0, &c->tabs)) {
+    delete c;
+    return fail(TQ_ERR_INVALID_ARG, "%s: Lloyd-Max solve did not converge", fn);
+  }
+  std::memset(c->tabs.sign_bits, 0, sizeof(c->tabs.sign_bits));  // no sign vector
+  c->dense = true;
+  std::string err_text;
+  double* mt = new (std::nothrow) double[n];
+  if (!mt) {
+    delete c;
+    return fail(TQ_ERR_NOMEM, "%s: out of host memory", fn);
+  }
+  for (int i = 0; i < dim; ++i)
+    for (int j = 0; j < dim; ++j) mt[(size_t)j * dim + i] = rotation[(size_t)i * dim + j];
+  hipError_t e = hipMalloc((void**)&c->m_dev, n * sizeof(double));
+  if (e == hipSuccess) e = hipMalloc((void**)&c->mt_dev, n * sizeof(double));
+  if (e == hipSuccess) e = hipMemcpy(c->m_dev, rotation, n * sizeof(double), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->mt_dev, mt, n * sizeof(double), hipMemcpyHostToDevice);
+  delete[] mt;
+  if (e != hipSuccess) {
+    if (c->m_dev) (void)hipFree(c->m_dev);
+    if (c->mt_dev) (void)hipFree(c->mt_dev);
+    delete c;
+    return fail(TQ_ERR_HIP, "%s: device copy of the rotation failed: %s", fn,
+                hipGetErrorString(e));
+  }
+  *out = c;
+  return ok();
+}
+
+void tq_codec_destroy(tq_codec* c) {
+  if (!c) return;
+  if (c->m_dev) (void)hipFree(c->m_dev);
+  if (c->mt_dev) (void)hipFree(c->mt_dev);
+  delete c;
+}
 
 tq_status tq_codec_tables(const tq_codec* c, int8_t* signs, float* centroids,
                           float* boundaries) {
@@ -266,7 +349,7 @@ tq_status tq_stream_read(const void* buf, size_t bytes, void* sink, void* stream
 
 static bool attend_shape_ok(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
   return batch > 0 && n_kv_heads > 0 && n_q_heads > 0 && n_q_heads % n_kv_heads == 0 &&
-         n_q_heads / n_kv_heads <= 16 && dim_ok(dim) && max_len > 0 && batch <= 65535 &&
+         n_q_heads / n_kv_heads <= 16 && dense_dim_ok(dim) && max_len > 0 && batch <= 65535 &&
          n_kv_heads <= 65535;
 }
 
@@ -306,6 +389,12 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
     return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim,
                 vc->tabs.dim);
   const int dim = vc->tabs.dim;
+  const bool dense = vc->dense || (kc && kc->dense);
+  if (dense && (!kc || !kc->dense || !vc->dense || n_qtok != 1 || raw.lengths))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "%s: dense-rotation codecs are attended only by tq_decode_attend with dense "
+                "K and V codecs",
+                fn);
   const int k_bits = raw_k ? 16 : (prodk ? 32 + kc->tabs.bits : kc->tabs.bits);
   if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_qtok <= 0)
     return fail(TQ_ERR_INVALID_ARG,
@@ -330,6 +419,43 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
     return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale is NaN", fn);
   const int group = n_q_heads / n_kv_heads;
+  if (dense) {
+    const tq::AttendPlan dplan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
+    if (!workspace || workspace_bytes < dplan.total_bytes)
+      return fail(TQ_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
+                  workspace ? workspace_bytes : (size_t)0, dplan.total_bytes);
+    if ((uintptr_t)workspace & 255)
+      return fail(TQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    tq::DenseAttendArgs da;
+    std::memset(&da, 0, sizeof(da));
+    da.q = q_fp16;
+    da.mt_k = kc->mt_dev;
+    da.m_v = vc->m_dev;
+    da.k_codes = k_codes;
+    da.k_norms = k_norms;
+    da.v_codes = v_codes;
+    da.v_norms = v_norms;
+    da.lengths = lengths;
+    da.pacc = (float*)workspace;
+    da.pml = (float*)((char*)workspace + dplan.part_acc_bytes);
+    da.out = out;
+    da.dim = dim;
+    da.k_bits = kc->tabs.bits;
+    da.v_bits = vc->tabs.bits;
+    da.n_q_heads = n_q_heads;
+    da.n_kv_heads = n_kv_heads;
+    da.group = group;
+    da.max_ctx = max_ctx;
+    da.splits = dplan.splits;
+    da.tokens_per_split = dplan.tokens_per_split;
+    da.qscale = tq::dense_qscale(scale, dim);
+    std::memcpy(da.k_centroids, kc->tabs.centroids, sizeof(float) * (1 << da.k_bits));
+    std::memcpy(da.v_centroids, vc->tabs.centroids, sizeof(float) * (1 << da.v_bits));
+    const hipError_t err = tq::launch_attend_dense(da, batch, (hipStream_t)stream);
+    if (err != hipSuccess)
+      return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return ok();
+  }
   if (!tq::attend_supported(dim, k_bits, vc->tabs.bits, group * n_qtok))
     return fail(TQ_ERR_UNSUPPORTED,
                 "%s: no kernel for dim %d, K %d-bit%s, V %d-bit, %d heads per KV head", fn, dim,
@@ -524,6 +650,8 @@ tq_status tq_cache_init(const tq_codec* kc, const tq_codec* vc, const tq_cache_d
   if (!kc || !vc || !desc) return fail(TQ_ERR_INVALID_ARG, "%s: NULL codec or descriptor", fn);
   if (kc->tabs.prod || vc->tabs.prod)
     return fail(TQ_ERR_INVALID_ARG, "%s: TurboQuant-Prod codecs are not cached here", fn);
+  if (kc->dense || vc->dense)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: dense-rotation codecs are not cached here", fn);
   if (kc->tabs.dim != vc->tabs.dim)
     return fail(TQ_ERR_INVALID_ARG, "%s: K dim %d != V dim %d", fn, kc->tabs.dim, vc->tabs.dim);
   const tq_cache_desc& d = *desc;

@@ -1,0 +1,325 @@
+// dense.hip -- codecs whose rotation is a dense matrix, for head dims with no
+// Walsh-Hadamard transform (PR #232, Known limitations: power-of-2 head dims
+// use the WHT, others fall back to a dense rotation; VeloxQuant "How I built",
+// Stage 1: the original method's rotation is the Q factor of a Gaussian matrix).
+//
+// The caller supplies m (d x d, m / sqrt(d) orthogonal, d a multiple of 32 up
+// to 256). With m = H diag(sigma) this is exactly the Walsh-Hadamard codec.
+//
+// Encode, per fp16 vector x (one wavefront per vector):
+//   N = sqrt(sum_j x_j^2)  fp64; pairwise tree in index order, an odd last
+//                          element carried up to the next level
+//   w = m x                fp64; products and sums in index order, no fused
+//                          multiply-add (m is read transposed, so a lane's
+//                          coordinate i walks a coalesced column)
+//   z = w / N (0 when N = 0), index = #{boundaries < z}, packed LSB-first.
+//
+// Attend (the same split / combine shape as the Walsh-Hadamard path, without
+// its matrix-core scoring): q_hat = scale log2(e) / d * m_K q per query head;
+// per 64-token tile a lane scores one token, s = n_t q_hat . c_K[idx_t];
+// online softmax in base 2; a lane then owns coordinates and accumulates
+// p_t n^V_t c_V[idx^V_t] over the tile's tokens; the combine merges the
+// splits and applies the inverse rotation out = m_V^T a / d.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "codec.hpp"
+#include "kernels.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int kDW = 4;           // wavefronts per workgroup
+constexpr int kDTile = 64;       // tokens per wavefront tile
+constexpr int kDMaxG = 16;       // query heads per KV head
+constexpr float kDLog2e = 1.4426950408889634f;
+constexpr float kDNoRow = -1e30f;  // running maximum before any row (finite)
+
+__device__ __forceinline__ void dwave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ float dwave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float dwave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// The b-bit field of coordinate j in a packed row of dwords (the field never
+// reaches past the row's last dword).
+__device__ __forceinline__ uint32_t dfield(const uint32_t* r, int j, int b) {
+  const int p = j * b, wi = p >> 5, sh = p & 31;
+  uint32_t f = r[wi] >> sh;
+  if (sh + b > 32) f |= r[wi + 1] << (32 - sh);
+  return f & ((1u << b) - 1u);
+}
+
+// ---------------------------------------------------------------- encode
+
+__global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
+#pragma clang fp contract(off)
+  __shared__ float s_bnd[256];
+  __shared__ double s_x[kDW][kMaxDim];
+  __shared__ double s_t[kDW][2][kMaxDim];
+  __shared__ uint8_t s_idx[kDW][kMaxDim];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = (1 << a.bits) - 1;
+  s_bnd[threadIdx.x] = (int)threadIdx.x < nb ? a.boundaries[threadIdx.x] : 0.f;
+  __syncthreads();
+  const long long nvec = (long long)a.n_tok * a.n_head;
+  const long long v = (long long)blockIdx.x * kDW + wave;
+  if (v >= nvec) return;  // whole wavefront
+  const long long t = v / a.n_head, h = v - t * a.n_head;
+  const int d = a.dim;
+  const __half* x = (const __half*)a.x + t * a.xs_tok + h * a.xs_head;
+  double* xs = s_x[wave];
+  double* cur = s_t[wave][0];
+  double* nxt = s_t[wave][1];
+  for (int j = lane; j < d; j += 64) {
+    const double xv = (double)__half2float(x[j]);
+    xs[j] = xv;
+    cur[j] = xv * xv;  // exact
+  }
+  dwave_sync();
+  for (int w = d; w > 1; w = (w + 1) >> 1) {
+    for (int i = lane; i < (w >> 1); i += 64) nxt[i] = cur[2 * i] + cur[2 * i + 1];
+    if ((w & 1) && lane == 0) nxt[w >> 1] = cur[w - 1];
+    dwave_sync();
+    double* tmp = cur;
+    cur = nxt;
+    nxt = tmp;
+  }
+  const double nrm = __builtin_sqrt(cur[0]);
+  double acc[kMaxDim / 64];
+#pragma unroll
+  for (int e = 0; e < kMaxDim / 64; ++e) acc[e] = 0.0;
+  for (int j = 0; j < d; ++j) {
+    const double xj = xs[j];
+    const double* col = a.mt + (size_t)j * d;
+#pragma unroll
+    for (int e = 0; e < kMaxDim / 64; ++e) {
+      const int i = lane + 64 * e;
+      if (i < d) acc[e] = acc[e] + col[i] * xj;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kMaxDim / 64; ++e) {
+    const int i = lane + 64 * e;
+    if (i < d) {
+      const double z = nrm == 0.0 ? 0.0 : acc[e] / nrm;
+      int c = 0;
+      for (int s = (nb + 1) >> 1; s >= 1; s >>= 1)
+        if ((double)s_bnd[c + s - 1] < z) c += s;
+      s_idx[wave][i] = (uint8_t)c;
+    }
+  }
+  dwave_sync();
+  uint32_t* row = (uint32_t*)(a.codes + t * a.cs_tok + h * a.cs_head);
+  const int b = a.bits, words = d * b / 32;
+  for (int k = lane; k < words; k += 64) {
+    uint32_t word = 0;
+    for (int p = 0; p < 32; ++p) {
+      const int bit = 32 * k + p, j = bit / b, r = bit - j * b;
+      word |= (uint32_t)((s_idx[wave][j] >> r) & 1) << p;
+    }
+    row[k] = word;
+  }
+  if (lane == 0) a.norms[t * a.ns_tok + h * a.ns_head] = (float)nrm;
+}
+
+// ---------------------------------------------------------------- attend
+
+// Grid (splits, n_kv_heads, batch); 4 wavefronts take the range's 64-token
+// tiles in turn and merge at the end; one partial (m, l, acc[d]) per query
+// head and split, in base-2 units.
+__global__ __launch_bounds__(256) void dense_split_kernel(DenseAttendArgs a) {
+  __shared__ float s_q[kDMaxG][kMaxDim];
+  __shared__ float s_ck[256], s_cv[256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_rows[kDW][kDTile * kMaxDim / 4];
+  __shared__ float s_w[kDW][kDTile][kDMaxG];
+  __shared__ float s_ml[kDW][2][kDMaxG];
+  static_assert(sizeof(s_rows) >= sizeof(float) * kDW * kDMaxG * kMaxDim, "merge fits");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int d = a.dim, G = a.group, kb = a.k_bits, vb = a.v_bits;
+  s_ck[tid] = a.k_centroids[tid];
+  s_cv[tid] = a.v_centroids[tid];
+  // rotated queries of this KV head's group: q_hat_i = sum_j m_ij q_j
+  const __half* qg = (const __half*)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * d;
+  for (int idx = tid; idx < G * d; idx += 256) {
+    const int h = idx / d, i = idx - h * d;
+    const __half* qh = qg + (size_t)h * d;
+    double acc = 0.0;
+    for (int j = 0; j < d; ++j) acc += a.mt_k[(size_t)j * d + i] * (double)__half2float(qh[j]);
+    s_q[h][i] = (float)(acc * (double)a.qscale);
+  }
+  __syncthreads();
+
+  const int len = a.lengths[b];
+  const long long t_begin = (long long)s * a.tokens_per_split;
+  const long long t_stop = t_begin + a.tokens_per_split;
+  const int t_end = (int)(t_stop < len ? t_stop : (len > 0 ? len : 0));
+  const int kw = d * kb / 32, vw = d * vb / 32;  // dwords per row
+  const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_ctx;
+  const uint32_t* kbase = (const uint32_t*)a.k_codes + row0 * kw;
+  const uint32_t* vbase = (const uint32_t*)a.v_codes + row0 * vw;
+  uint32_t* rows = s_rows[wave];
+
+  float m_run[kDMaxG], l_run[kDMaxG], acc[kDMaxG][kMaxDim / 64];
+#pragma unroll
+  for (int h = 0; h < kDMaxG; ++h) {
+    m_run[h] = kDNoRow;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kMaxDim / 64; ++e) acc[h][e] = 0.f;
+  }
+  for (long long t0 = t_begin + (long long)kDTile * wave; t0 < t_end;
+       t0 += (long long)kDTile * kDW) {
+    const int cnt = (int)(t_end - t0 < kDTile ? t_end - t0 : kDTile);
+    const bool valid = lane < cnt;
+    // K rows t0 .. t0 + cnt - 1 are contiguous
+    const uint32_t* ksrc = kbase + (size_t)t0 * kw;
+    for (int k = lane; k < cnt * kw; k += 64) rows[k] = ksrc[k];
+    const float nk = valid ? a.k_norms[row0 + t0 + lane] : 0.f;
+    const float nv = valid ? a.v_norms[row0 + t0 + lane] : 0.f;
+    dwave_sync();
+    float sc[kDMaxG];
+#pragma unroll
+    for (int h = 0; h < kDMaxG; ++h) sc[h] = 0.f;
+    if (valid) {
+      const uint32_t* r = rows + lane * kw;
+      for (int j = 0; j < d; ++j) {
+        const float c = s_ck[dfield(r, j, kb)];
+#pragma unroll
+        for (int h = 0; h < kDMaxG; ++h)
+          if (h < G) sc[h] += s_q[h][j] * c;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kDMaxG; ++h) {
+      if (h < G) {
+        const float sv = valid ? sc[h] * nk : -INFINITY;
+        const float mn = fmaxf(m_run[h], dwave_max(sv));
+        const float alpha = exp2f(m_run[h] - mn);
+        const float p = exp2f(sv - mn);
+        l_run[h] = l_run[h] * alpha + dwave_sum(p);
+#pragma unroll
+        for (int e = 0; e < kMaxDim / 64; ++e) acc[h][e] *= alpha;
+        m_run[h] = mn;
+        s_w[wave][lane][h] = p * nv;
+      }
+    }
+    dwave_sync();  // K rows read, weights written
+    const uint32_t* vsrc = vbase + (size_t)t0 * vw;
+    for (int k = lane; k < cnt * vw; k += 64) rows[k] = vsrc[k];
+    dwave_sync();
+    for (int t = 0; t < cnt; ++t) {
+      const uint32_t* r = rows + t * vw;
+#pragma unroll
+      for (int e = 0; e < kMaxDim / 64; ++e) {
+        const int j = lane + 64 * e;
+        if (j < d) {
+          const float c = s_cv[dfield(r, j, vb)];
+#pragma unroll
+          for (int h = 0; h < kDMaxG; ++h)
+            if (h < G) acc[h][e] += s_w[wave][t][h] * c;
+        }
+      }
+    }
+    dwave_sync();  // V rows and weights read before the next tile
+  }
+
+  __syncthreads();  // every wavefront is done with its rows: reuse them for the merge
+  float* macc = (float*)&s_rows[0][0];  // [kDW][kDMaxG][kMaxDim]
+#pragma unroll
+  for (int h = 0; h < kDMaxG; ++h) {
+    if (h < G) {
+#pragma unroll
+      for (int e = 0; e < kMaxDim / 64; ++e) {
+        const int j = lane + 64 * e;
+        if (j < d) macc[(wave * kDMaxG + h) * kMaxDim + j] = acc[h][e];
+      }
+      if (lane == 0) {
+        s_ml[wave][0][h] = m_run[h];
+        s_ml[wave][1][h] = l_run[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * d; idx += 256) {
+    const int h = idx / d, j = idx - h * d;
+    float mx = s_ml[0][0][h];
+#pragma unroll
+    for (int w = 1; w < kDW; ++w) mx = fmaxf(mx, s_ml[w][0][h]);
+    float A = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDW; ++w) {
+      const float f = exp2f(s_ml[w][0][h] - mx);
+      A += macc[(w * kDMaxG + h) * kMaxDim + j] * f;
+      L += s_ml[w][1][h] * f;
+    }
+    const size_t slot = ((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.splits + s;
+    a.pacc[slot * d + j] = A;
+    if (j == 0) {
+      a.pml[slot * 2] = mx;
+      a.pml[slot * 2 + 1] = L;
+    }
+  }
+}
+
+// Grid (n_q_heads, batch): merge the splits by log-sum-exp, then
+// out_i = sum_j m_V[j][i] a_j / d (fp64 sums).
+__global__ __launch_bounds__(256) void dense_combine_kernel(DenseAttendArgs a) {
+  __shared__ float s_a[kMaxDim];
+  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y, d = a.dim;
+  const size_t slot0 = ((size_t)b * a.n_q_heads + h) * a.splits;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.pml[(slot0 + s) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < a.splits; ++s)
+    L += a.pml[(slot0 + s) * 2 + 1] * exp2f(a.pml[(slot0 + s) * 2] - mx);
+  for (int j = tid; j < d; j += 256) {
+    float A = 0.f;
+    for (int s = 0; s < a.splits; ++s)
+      A += a.pacc[(slot0 + s) * d + j] * exp2f(a.pml[(slot0 + s) * 2] - mx);
+    s_a[j] = L > 0.f ? A / L : 0.f;  // no visible row: a zero output
+  }
+  __syncthreads();
+  for (int i = tid; i < d; i += 256) {
+    double o = 0.0;
+    for (int j = 0; j < d; ++j) o += a.m_v[(size_t)j * d + i] * (double)s_a[j];
+    a.out[((size_t)b * a.n_q_heads + h) * d + i] = (float)(o / d);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
+  const long long nvec = (long long)a.n_tok * a.n_head;
+  if (nvec <= 0) return hipSuccess;
+  const long long blocks = (nvec + kDW - 1) / kDW;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dense_encode_kernel, dim3((unsigned)blocks), dim3(64 * kDW), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream) {
+  if (a.group < 1 || a.group > kDMaxG || a.dim % 32 || a.dim > kMaxDim) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dense_split_kernel, dim3(a.splits, a.n_kv_heads, batch), dim3(64 * kDW), 0,
+                     stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dense_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+float dense_qscale(float scale, int dim) { return scale * kDLog2e / (float)dim; }
+
+}  // namespace tq

@@ -111,6 +111,40 @@ struct CopyRowsArgs {
 };
 hipError_t launch_pending_rows(const CopyRowsArgs& a, hipStream_t stream);
 
+// Dense-rotation codecs (head dims with no Walsh-Hadamard transform).
+struct DenseEncodeArgs {
+  const void* x;               // fp16; vector (t, h) at element t*xs_tok + h*xs_head
+  long long xs_tok, xs_head;
+  uint8_t* codes;              // row (t, h) at byte t*cs_tok + h*cs_head (4-byte aligned)
+  long long cs_tok, cs_head;
+  float* norms;
+  long long ns_tok, ns_head;
+  const double* mt;            // transposed rotation, mt[j*dim + i] = m[i][j] (device)
+  int dim, bits, n_tok, n_head;
+  float boundaries[256];       // 2^bits - 1 used
+};
+hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream);
+
+struct DenseAttendArgs {
+  const void* q;               // fp16 [batch][n_q_heads][dim]
+  const double* mt_k;          // transposed K rotation (device)
+  const double* m_v;           // V rotation, row-major (device)
+  const uint8_t* k_codes;      // [batch][n_kv_heads][max_ctx][dim*k_bits/8], 4-byte aligned
+  const float* k_norms;
+  const uint8_t* v_codes;
+  const float* v_norms;
+  const int32_t* lengths;
+  float* pacc;                 // workspace: [batch][n_q_heads][splits][dim]
+  float* pml;                  //            [batch][n_q_heads][splits][2]
+  float* out;                  // [batch][n_q_heads][dim]
+  int dim, k_bits, v_bits, n_q_heads, n_kv_heads, group, max_ctx, splits, tokens_per_split;
+  float qscale;                // scale * log2(e) / dim
+  float k_centroids[256];      // unused entries zero
+  float v_centroids[256];
+};
+hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream);
+float dense_qscale(float scale, int dim);
+
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

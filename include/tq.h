@@ -134,6 +134,30 @@ tq_status tq_encode_kv(const tq_encode_job* k, const tq_encode_job* v, int n_tok
  */
 tq_status tq_codec_init_prod(int dim, int bits, uint64_t seed, tq_codec** out);
 
+/*
+ * Dense-rotation codec for head dims with no Walsh-Hadamard transform (PR #232,
+ * Known limitations: power-of-2 head dims use the WHT, others a dense
+ * rotation; VeloxQuant "How I built", Stage 1: the original method rotates by
+ * the Q factor of a Gaussian matrix). rotation: host array, dim x dim fp64,
+ * row-major, equal to sqrt(dim) times an orthogonal matrix (the caller draws
+ * it; only finiteness is checked). It is copied to the current device, with
+ * its transpose (16 dim^2 bytes); the codec owns both until tq_codec_destroy.
+ * Encode (tq_encode, tq_encode_kv with two dense codecs of one dim):
+ * N = |x| summed in fp64 over a pairwise tree in index order (an odd last
+ * element is carried up a level), w = rotation . x in fp64 with products and
+ * sums in index order and no fused multiply-add, z = w / N, then the
+ * Lloyd-Max indices and packing of tq_encode. With rotation = H diag(sigma)
+ * the codes and norms equal those of tq_codec_init's codec with that sigma.
+ * Attend: tq_decode_attend with dense K and V codecs (the same arguments and
+ * workspace as for the Walsh-Hadamard codecs); the other attend calls and the
+ * two-phase cache return TQ_ERR_UNSUPPORTED for dense codecs.
+ * dim: a multiple of 32 in [32, 256] (so rows are whole dwords), else
+ * TQ_ERR_UNSUPPORTED; bits in [1, 8]. TQ_ERR_INVALID_ARG for a NULL rotation
+ * or a non-finite entry, TQ_ERR_HIP if the device copy fails. tq_codec_tables
+ * reports signs of +1 and tq_codec_info a seed of 0 for a dense codec.
+ */
+tq_status tq_codec_init_dense(int dim, int bits, const double* rotation, tq_codec** out);
+
 /* tq_encode for a Prod codec: codes (dim*(bits-1)/8 bytes per row, layout and
  * alignment as tq_encode), sketch (dim/8 bytes per row at byte
  * t*s_stride_tok + h*s_stride_head, any alignment), norms, and residual norms

@@ -75,6 +75,39 @@ def test_codec_init_rejects_unsupported(dim, bits):
     assert "tq_codec_init" in tq.tq_last_error()
 
 
+@pytest.mark.parametrize("dim,bits", [(80, 4), (288, 4), (0, 4), (16, 4), (96, 0), (96, 9)])
+def test_codec_init_dense_rejects_unsupported(dim, bits):
+    m = np.eye(max(dim, 1)) * np.sqrt(max(dim, 1))
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    lib.tq_codec_init_dense.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_void_p)]
+    h = ctypes.c_void_p(1)
+    assert lib.tq_codec_init_dense(dim, bits, m.ctypes.data, ctypes.byref(h)) == \
+        tq.TQ_ERR_UNSUPPORTED
+    assert h.value is None
+    assert "tq_codec_init_dense" in tq.tq_last_error()
+
+
+def test_codec_init_dense_invalid_arguments():
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    lib.tq_codec_init_dense.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    m = np.eye(96) * np.sqrt(96)
+    h = ctypes.c_void_p()
+    assert lib.tq_codec_init_dense(96, 4, m.ctypes.data, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_codec_init_dense(96, 4, None, ctypes.addressof(h)) == tq.TQ_ERR_INVALID_ARG
+    bad = m.copy()
+    bad[3, 7] = np.nan
+    assert lib.tq_codec_init_dense(96, 4, bad.ctypes.data, ctypes.addressof(h)) == \
+        tq.TQ_ERR_INVALID_ARG
+    bad[3, 7] = np.inf
+    assert lib.tq_codec_init_dense(96, 4, bad.ctypes.data, ctypes.addressof(h)) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert "not finite" in tq.tq_last_error()
+    with pytest.raises(ValueError):
+        tq.tq_codec_init_dense(96, 4, np.eye(64))
+
+
 def test_codec_init_null_out():
     lib = ctypes.CDLL(tq.LIB_PATH)
     lib.tq_codec_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p]
@@ -267,7 +300,9 @@ def test_decode_attend_prod_validation():
 
 def test_workspace_and_split_plan():
     assert tq.tq_attend_workspace_bytes(1, 4, 3, 64, 10) == 0
-    assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) == 0
+    assert tq.tq_attend_workspace_bytes(1, 4, 2, 96, 10) > 0     # dense-rotation dims
+    assert tq.tq_attend_workspace_bytes(1, 4, 2, 80, 10) == 0     # not a multiple of 32
+    assert tq.tq_attend_workspace_bytes(1, 4, 2, 288, 10) == 0
     for (B, Hq, Hkv, d, L) in [(1, 4, 2, 64, 256), (1, 32, 8, 128, 32768), (16, 32, 8, 128, 8192),
                                (1, 64, 8, 64, 131072), (1, 24, 8, 128, 4096)]:
         S = tq.tq_attend_num_splits(B, Hq, Hkv, d, L)
