@@ -464,6 +464,58 @@ def main():
             del rk_copies
         except tq.TQError as e:
             raw_k_line = {"unsupported": str(e)}
+    # ---- dense-rotation codecs: a Phi-3-mini-shaped layer (32 query and 32 KV
+    # heads, head dim 96: no Walsh-Hadamard transform) at 32K context, K4/V3
+    dense_line = None
+    if graph is not None:
+        try:
+            dd, dH, dT = 96, 32, 32768
+            dkc = tq.tq_codec_init_dense(dd, 4, workloads.rotation_matrix(dd, 1))
+            dvc = tq.tq_codec_init_dense(dd, 3, workloads.rotation_matrix(dd, 2))
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(96)
+            dk = torch.randn((1, dH, dT, dd), generator=gen, device=dev).half()
+            dv = torch.randn((1, dH, dT, dd), generator=gen, device=dev).half()
+            dq = torch.randn((1, dH, dd), generator=gen, device=dev).half()
+            drow = dkc.row_bytes + 4 + dvc.row_bytes + 4
+            dcopies = max(2, math.ceil(args.cold_bytes / (dH * dT * drow)))
+            tmaj = lambda a, *row: a.view(dH, dT, *row).permute(1, 0, *range(2, 2 + len(row)))
+            d_copies = []
+            for i in range(dcopies):
+                t = (torch.empty((1, dH, dT, dkc.row_bytes), dtype=torch.uint8, device=dev),
+                     torch.empty((1, dH, dT), dtype=torch.float32, device=dev),
+                     torch.empty((1, dH, dT, dvc.row_bytes), dtype=torch.uint8, device=dev),
+                     torch.empty((1, dH, dT), dtype=torch.float32, device=dev))
+                tq.tq_encode(dkc, tmaj(dk, dd), tmaj(t[0], dkc.row_bytes), tmaj(t[1]))
+                tq.tq_encode(dvc, tmaj(dv, dd), tmaj(t[2], dvc.row_bytes), tmaj(t[3]))
+                d_copies.append(t)
+            dlen = torch.full((1,), dT, dtype=torch.int32, device=dev)
+            dout = torch.empty((1, dH, dd), dtype=torch.float32, device=dev)
+            dws = torch.empty(tq.tq_attend_workspace_bytes(1, dH, dH, dd, dT), dtype=torch.uint8,
+                              device=dev)
+            torch.cuda.synchronize()
+
+            def dense_only(i):
+                c = d_copies[i % dcopies]
+                tq.tq_decode_attend(dkc, dvc, dq, c[0], c[1], c[2], c[3], dlen, dT,
+                                    1.0 / math.sqrt(dd), dout, dws)
+
+            us = graph_us_per_call(dense_only, dcopies, max(2, args.steps // (4 * dcopies)))
+            dbytes = dH * dT * drow
+            c0 = d_copies[0]
+
+            def dense_encode(i):
+                tq.tq_encode(dkc, tmaj(dk, dd), tmaj(c0[0], dkc.row_bytes), tmaj(c0[1]))
+
+            enc_us = graph_us_per_call(dense_encode, 2, 3)
+            dense_line = {"shape": "1 x 32/32 heads, head dim 96, 32768 tokens, K4/V3",
+                          "cold_copies": dcopies, "attend_us": round(us, 3),
+                          "GBps": round(dbytes / (us * 1e-6) / 1e9, 2),
+                          "encode_k_cache_us": round(enc_us, 2),
+                          "encode_vectors_per_s": round(dH * dT / (enc_us * 1e-6), 1)}
+            del d_copies, dk, dv
+        except tq.TQError as e:
+            dense_line = {"unsupported": str(e)}
     # ---- TurboQuant-Prod keys (3-bit codes + 1-bit sketch) with 4-bit values
     prod_line = None
     if graph is not None:
@@ -618,6 +670,7 @@ def main():
         "mixed_sink_decode": mixed,
         "raw_k_decode": raw_k_line,
         "prod_decode": prod_line,
+        "dense_rotation_decode": dense_line,
         "two_phase_cache_decode": cache_line,
         "bulk_encode_kv": bulk,
     }

@@ -31,7 +31,7 @@
 namespace tq {
 namespace {
 
-constexpr int kDW = 4;           // wavefronts per workgroup
+constexpr int kDW = 4;           // wavefronts per encode workgroup
 constexpr int kDTile = 64;       // tokens per wavefront tile
 constexpr int kDMaxG = 16;       // query heads per KV head
 constexpr float kDLog2e = 1.4426950408889634f;
@@ -136,29 +136,41 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
 
 // ---------------------------------------------------------------- attend
 
-// Grid (splits, n_kv_heads, batch); 4 wavefronts take the range's 64-token
-// tiles in turn and merge at the end; one partial (m, l, acc[d]) per query
-// head and split, in base-2 units.
-__global__ __launch_bounds__(256) void dense_split_kernel(DenseAttendArgs a) {
-  __shared__ float s_q[kDMaxG][kMaxDim];
-  __shared__ float s_ck[256], s_cv[256];
-  __shared__ __attribute__((aligned(16))) uint32_t s_rows[kDW][kDTile * kMaxDim / 4];
-  __shared__ float s_w[kDW][kDTile][kDMaxG];
-  __shared__ float s_ml[kDW][2][kDMaxG];
-  static_assert(sizeof(s_rows) >= sizeof(float) * kDW * kDMaxG * kMaxDim, "merge fits");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Grid (splits, n_kv_heads, batch); nw = blockDim.x / 64 wavefronts take the
+// range's 64-token tiles in turn and merge at the end; one partial
+// (m, l, acc[d]) per query head and split, in base-2 units. GM and EM bound
+// the query heads per KV head and the coordinates per lane (d / 64, rounded
+// up) so that the per-lane arrays stay in registers. LDS (sized at launch):
+// rotated queries [G][d], the two centroid tables, running (m, l) per
+// wavefront, and per wavefront a region of a.wave_stride floats holding the
+// tile's staged rows (a.rows_words dwords) and weights [64][G], reused for its
+// accumulators [G][d] at the merge.
+template <int GM, int EM>
+__global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(DenseAttendArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float dlds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int d = a.dim, G = a.group, kb = a.k_bits, vb = a.v_bits;
-  s_ck[tid] = a.k_centroids[tid];
-  s_cv[tid] = a.v_centroids[tid];
+  float* s_q = dlds;
+  float* s_ck = s_q + G * d;
+  float* s_cv = s_ck + 256;
+  float* s_ml = s_cv + 256;                       // [nw][2][G]
+  float* s_wave = s_ml + ((nw * 2 * G + 3) & ~3);
+  float* mine = s_wave + (size_t)wave * a.wave_stride;
+  uint32_t* rows = (uint32_t*)mine;
+  float* s_w = mine + a.rows_words;               // [64][G]
+  for (int k = tid; k < 256; k += blockDim.x) {
+    s_ck[k] = a.k_centroids[k];
+    s_cv[k] = a.v_centroids[k];
+  }
   // rotated queries of this KV head's group: q_hat_i = sum_j m_ij q_j
   const __half* qg = (const __half*)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * d;
-  for (int idx = tid; idx < G * d; idx += 256) {
+  for (int idx = tid; idx < G * d; idx += blockDim.x) {
     const int h = idx / d, i = idx - h * d;
     const __half* qh = qg + (size_t)h * d;
     double acc = 0.0;
     for (int j = 0; j < d; ++j) acc += a.mt_k[(size_t)j * d + i] * (double)__half2float(qh[j]);
-    s_q[h][i] = (float)(acc * (double)a.qscale);
+    s_q[h * d + i] = (float)(acc * (double)a.qscale);
   }
   __syncthreads();
 
@@ -170,18 +182,17 @@ __global__ __launch_bounds__(256) void dense_split_kernel(DenseAttendArgs a) {
   const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_ctx;
   const uint32_t* kbase = (const uint32_t*)a.k_codes + row0 * kw;
   const uint32_t* vbase = (const uint32_t*)a.v_codes + row0 * vw;
-  uint32_t* rows = s_rows[wave];
 
-  float m_run[kDMaxG], l_run[kDMaxG], acc[kDMaxG][kMaxDim / 64];
+  float m_run[GM], l_run[GM], acc[GM][EM];
 #pragma unroll
-  for (int h = 0; h < kDMaxG; ++h) {
+  for (int h = 0; h < GM; ++h) {
     m_run[h] = kDNoRow;
     l_run[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < kMaxDim / 64; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < EM; ++e) acc[h][e] = 0.f;
   }
   for (long long t0 = t_begin + (long long)kDTile * wave; t0 < t_end;
-       t0 += (long long)kDTile * kDW) {
+       t0 += (long long)kDTile * nw) {
     const int cnt = (int)(t_end - t0 < kDTile ? t_end - t0 : kDTile);
     const bool valid = lane < cnt;
     // K rows t0 .. t0 + cnt - 1 are contiguous
@@ -190,20 +201,20 @@ __global__ __launch_bounds__(256) void dense_split_kernel(DenseAttendArgs a) {
     const float nk = valid ? a.k_norms[row0 + t0 + lane] : 0.f;
     const float nv = valid ? a.v_norms[row0 + t0 + lane] : 0.f;
     dwave_sync();
-    float sc[kDMaxG];
+    float sc[GM];
 #pragma unroll
-    for (int h = 0; h < kDMaxG; ++h) sc[h] = 0.f;
+    for (int h = 0; h < GM; ++h) sc[h] = 0.f;
     if (valid) {
       const uint32_t* r = rows + lane * kw;
       for (int j = 0; j < d; ++j) {
         const float c = s_ck[dfield(r, j, kb)];
 #pragma unroll
-        for (int h = 0; h < kDMaxG; ++h)
-          if (h < G) sc[h] += s_q[h][j] * c;
+        for (int h = 0; h < GM; ++h)
+          if (h < G) sc[h] += s_q[h * d + j] * c;
       }
     }
 #pragma unroll
-    for (int h = 0; h < kDMaxG; ++h) {
+    for (int h = 0; h < GM; ++h) {
       if (h < G) {
         const float sv = valid ? sc[h] * nk : -INFINITY;
         const float mn = fmaxf(m_run[h], dwave_max(sv));
@@ -211,9 +222,9 @@ __global__ __launch_bounds__(256) void dense_split_kernel(DenseAttendArgs a) {
         const float p = exp2f(sv - mn);
         l_run[h] = l_run[h] * alpha + dwave_sum(p);
 #pragma unroll
-        for (int e = 0; e < kMaxDim / 64; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < EM; ++e) acc[h][e] *= alpha;
         m_run[h] = mn;
-        s_w[wave][lane][h] = p * nv;
+        s_w[lane * G + h] = p * nv;
       }
     }
     dwave_sync();  // K rows read, weights written
@@ -223,47 +234,44 @@ __global__ __launch_bounds__(256) void dense_split_kernel(DenseAttendArgs a) {
     for (int t = 0; t < cnt; ++t) {
       const uint32_t* r = rows + t * vw;
 #pragma unroll
-      for (int e = 0; e < kMaxDim / 64; ++e) {
+      for (int e = 0; e < EM; ++e) {
         const int j = lane + 64 * e;
         if (j < d) {
           const float c = s_cv[dfield(r, j, vb)];
 #pragma unroll
-          for (int h = 0; h < kDMaxG; ++h)
-            if (h < G) acc[h][e] += s_w[wave][t][h] * c;
+          for (int h = 0; h < GM; ++h)
+            if (h < G) acc[h][e] += s_w[t * G + h] * c;
         }
       }
     }
     dwave_sync();  // V rows and weights read before the next tile
   }
 
-  __syncthreads();  // every wavefront is done with its rows: reuse them for the merge
-  float* macc = (float*)&s_rows[0][0];  // [kDW][kDMaxG][kMaxDim]
+  // merge: each wavefront's accumulators go to its own region
 #pragma unroll
-  for (int h = 0; h < kDMaxG; ++h) {
+  for (int h = 0; h < GM; ++h) {
     if (h < G) {
 #pragma unroll
-      for (int e = 0; e < kMaxDim / 64; ++e) {
+      for (int e = 0; e < EM; ++e) {
         const int j = lane + 64 * e;
-        if (j < d) macc[(wave * kDMaxG + h) * kMaxDim + j] = acc[h][e];
+        if (j < d) mine[h * d + j] = acc[h][e];
       }
       if (lane == 0) {
-        s_ml[wave][0][h] = m_run[h];
-        s_ml[wave][1][h] = l_run[h];
+        s_ml[(wave * 2) * G + h] = m_run[h];
+        s_ml[(wave * 2 + 1) * G + h] = l_run[h];
       }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * d; idx += 256) {
+  for (int idx = tid; idx < G * d; idx += blockDim.x) {
     const int h = idx / d, j = idx - h * d;
-    float mx = s_ml[0][0][h];
-#pragma unroll
-    for (int w = 1; w < kDW; ++w) mx = fmaxf(mx, s_ml[w][0][h]);
+    float mx = s_ml[h];
+    for (int w = 1; w < nw; ++w) mx = fmaxf(mx, s_ml[(w * 2) * G + h]);
     float A = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDW; ++w) {
-      const float f = exp2f(s_ml[w][0][h] - mx);
-      A += macc[(w * kDMaxG + h) * kMaxDim + j] * f;
-      L += s_ml[w][1][h] * f;
+    for (int w = 0; w < nw; ++w) {
+      const float f = exp2f(s_ml[(w * 2) * G + h] - mx);
+      A += s_wave[(size_t)w * a.wave_stride + h * d + j] * f;
+      L += s_ml[(w * 2 + 1) * G + h] * f;
     }
     const size_t slot = ((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.splits + s;
     a.pacc[slot * d + j] = A;
@@ -310,11 +318,46 @@ hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int GM, int EM>
+hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) {
+  constexpr int kMaxWaves = GM * EM > 8 ? 8 : 16;
+  constexpr size_t kLdsLimit = 160 * 1024;
+  const int G = a.group, d = a.dim;
+  const int kw = d * a.k_bits / 32, vw = d * a.v_bits / 32;
+  a.rows_words = kDTile * (kw > vw ? kw : vw);
+  int stride = a.rows_words + kDTile * G;
+  if (stride < G * d) stride = G * d;
+  a.wave_stride = (stride + 3) & ~3;
+  auto bytes = [&](int nw) {
+    return sizeof(float) * ((size_t)G * d + 512 + ((nw * 2 * G + 3) & ~3) +
+                            (size_t)nw * a.wave_stride);
+  };
+  int nw = kMaxWaves;
+  while (nw > 1 && bytes(nw) > kLdsLimit) nw >>= 1;
+  const size_t lds = bytes(nw);
+  if (lds > kLdsLimit) return hipErrorInvalidValue;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)&dense_split_kernel<GM, EM>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kLdsLimit);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((dense_split_kernel<GM, EM>), dim3(a.splits, a.n_kv_heads, batch),
+                     dim3(64 * nw), lds, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream) {
   if (a.group < 1 || a.group > kDMaxG || a.dim % 32 || a.dim > kMaxDim) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dense_split_kernel, dim3(a.splits, a.n_kv_heads, batch), dim3(64 * kDW), 0,
-                     stream, a);
-  hipError_t err = hipGetLastError();
+  hipError_t err;
+  if (a.group <= 4)
+    err = a.dim <= 128 ? launch_dense_split<4, 2>(a, batch, stream)
+                       : launch_dense_split<4, 4>(a, batch, stream);
+  else
+    err = a.dim <= 128 ? launch_dense_split<16, 2>(a, batch, stream)
+                       : launch_dense_split<16, 4>(a, batch, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dense_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, stream, a);
   return hipGetLastError();
