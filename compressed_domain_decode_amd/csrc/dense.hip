@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
   __shared__ float s_bnd[256];
   __shared__ double s_x[kDW][kMaxDim];
   __shared__ double s_t[kDW][2][kMaxDim];
-  __shared__ uint8_t s_idx[kDW][kMaxDim];
+  __shared__ uint32_t s_row[kDW][kMaxDim * 8 / 32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb = (1 << a.bits) - 1;
   s_bnd[threadIdx.x] = (int)threadIdx.x < nb ? a.boundaries[threadIdx.x] : 0.f;
@@ -97,10 +97,15 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
     nxt = tmp;
   }
   const double nrm = __builtin_sqrt(cur[0]);
+  const int b = a.bits, words = d * b / 32;
+  uint32_t* srow = s_row[wave];
+  for (int k = lane; k < words; k += 64) srow[k] = 0u;
+  dwave_sync();
   double acc[kMaxDim / 64];
 #pragma unroll
   for (int e = 0; e < kMaxDim / 64; ++e) acc[e] = 0.0;
-  for (int j = 0; j < d; ++j) {
+#pragma unroll 8
+  for (int j = 0; j < d; ++j) {  // d is a multiple of 32
     const double xj = xs[j];
     const double* col = a.mt + (size_t)j * d;
 #pragma unroll
@@ -117,20 +122,15 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
       int c = 0;
       for (int s = (nb + 1) >> 1; s >= 1; s >>= 1)
         if ((double)s_bnd[c + s - 1] < z) c += s;
-      s_idx[wave][i] = (uint8_t)c;
+      // LSB-first: the code occupies stream bits i*b .. i*b + b - 1
+      const int p = i * b, wi = p >> 5, sh = p & 31;
+      atomicOr(&srow[wi], (uint32_t)c << sh);
+      if (sh + b > 32) atomicOr(&srow[wi + 1], (uint32_t)c >> (32 - sh));
     }
   }
   dwave_sync();
   uint32_t* row = (uint32_t*)(a.codes + t * a.cs_tok + h * a.cs_head);
-  const int b = a.bits, words = d * b / 32;
-  for (int k = lane; k < words; k += 64) {
-    uint32_t word = 0;
-    for (int p = 0; p < 32; ++p) {
-      const int bit = 32 * k + p, j = bit / b, r = bit - j * b;
-      word |= (uint32_t)((s_idx[wave][j] >> r) & 1) << p;
-    }
-    row[k] = word;
-  }
+  for (int k = lane; k < words; k += 64) row[k] = srow[k];
   if (lane == 0) a.norms[t * a.ns_tok + h * a.ns_head] = (float)nrm;
 }
 
@@ -169,6 +169,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     const int h = idx / d, i = idx - h * d;
     const __half* qh = qg + (size_t)h * d;
     double acc = 0.0;
+#pragma unroll 8
     for (int j = 0; j < d; ++j) acc += a.mt_k[(size_t)j * d + i] * (double)__half2float(qh[j]);
     s_q[h * d + i] = (float)(acc * (double)a.qscale);
   }
@@ -206,6 +207,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     for (int h = 0; h < GM; ++h) sc[h] = 0.f;
     if (valid) {
       const uint32_t* r = rows + lane * kw;
+#pragma unroll 4
       for (int j = 0; j < d; ++j) {
         const float c = s_ck[dfield(r, j, kb)];
 #pragma unroll
@@ -231,6 +233,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     const uint32_t* vsrc = vbase + (size_t)t0 * vw;
     for (int k = lane; k < cnt * vw; k += 64) rows[k] = vsrc[k];
     dwave_sync();
+#pragma unroll 2
     for (int t = 0; t < cnt; ++t) {
       const uint32_t* r = rows + t * vw;
 #pragma unroll
@@ -302,6 +305,7 @@ __global__ __launch_bounds__(256) void dense_combine_kernel(DenseAttendArgs a) {
   __syncthreads();
   for (int i = tid; i < d; i += 256) {
     double o = 0.0;
+#pragma unroll 8
     for (int j = 0; j < d; ++j) o += a.m_v[(size_t)j * d + i] * (double)s_a[j];
     a.out[((size_t)b * a.n_q_heads + h) * d + i] = (float)(o / d);
   }
