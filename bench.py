@@ -146,6 +146,23 @@ def graph_us_per_call(fn, ncalls, reps):
     return e0.elapsed_time(e1) * 1e3 / (reps * ncalls)
 
 
+def eager_us_per_call(fn, ncalls, reps):
+    """Average time of one fn(i) call launched eagerly, ncalls per rep."""
+    import torch
+    for i in range(ncalls):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for i in range(ncalls):
+            fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * ncalls)
+
+
 class Hip:
     """hipEvent helpers through the HIP runtime (events on an explicit stream)."""
 
@@ -467,7 +484,8 @@ def main():
     # ---- dense-rotation codecs: a Phi-3-mini-shaped layer (32 query and 32 KV
     # heads, head dim 96: no Walsh-Hadamard transform) at 32K context, K4/V3
     dense_line = None
-    if graph is not None:
+    per_call = graph_us_per_call if graph is not None else eager_us_per_call
+    if True:
         try:
             dd, dH, dT = 96, 32, 32768
             dkc = tq.tq_codec_init_dense(dd, 4, workloads.rotation_matrix(dd, 1))
@@ -500,15 +518,16 @@ def main():
                 tq.tq_decode_attend(dkc, dvc, dq, c[0], c[1], c[2], c[3], dlen, dT,
                                     1.0 / math.sqrt(dd), dout, dws)
 
-            us = graph_us_per_call(dense_only, dcopies, max(2, args.steps // (4 * dcopies)))
+            us = per_call(dense_only, dcopies, max(2, args.steps // (4 * dcopies)))
             dbytes = dH * dT * drow
             c0 = d_copies[0]
 
             def dense_encode(i):
                 tq.tq_encode(dkc, tmaj(dk, dd), tmaj(c0[0], dkc.row_bytes), tmaj(c0[1]))
 
-            enc_us = graph_us_per_call(dense_encode, 2, 3)
+            enc_us = per_call(dense_encode, 2, 3)
             dense_line = {"shape": "1 x 32/32 heads, head dim 96, 32768 tokens, K4/V3",
+                          "timing": "graph replay" if graph is not None else "eager",
                           "cold_copies": dcopies, "attend_us": round(us, 3),
                           "GBps": round(dbytes / (us * 1e-6) / 1e9, 2),
                           "encode_k_cache_us": round(enc_us, 2),
