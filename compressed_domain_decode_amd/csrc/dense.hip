@@ -61,6 +61,31 @@ __device__ __forceinline__ uint32_t dfield(const uint32_t* r, int j, int b) {
   return f & ((1u << b) - 1u);
 }
 
+// Scores of one token (this lane's K row r) against the G rotated queries,
+// for KB-bit codes: 32 coordinates at a time, the row's KB dwords for them in
+// registers and every field at a compile-time offset, so the 32 centroid
+// lookups are independent.
+template <int GM, int KB>
+__device__ __forceinline__ void dense_scores(const uint32_t* r, int d, int G, const float* s_q,
+                                             const float* s_ck, float (&sc)[GM]) {
+  for (int j0 = 0; j0 < d; j0 += 32) {
+    uint32_t w[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) w[k] = r[(j0 >> 5) * KB + k];
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {
+      constexpr uint32_t mask = (1u << KB) - 1u;
+      const int off = jj * KB, wi = off >> 5, sh = off & 31;
+      uint32_t f = w[wi] >> sh;
+      if (sh + KB > 32) f |= w[wi + 1] << (32 - sh);
+      const float c = s_ck[f & mask];
+#pragma unroll
+      for (int h = 0; h < GM; ++h)
+        if (h < G) sc[h] += s_q[h * d + j0 + jj] * c;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- encode
 
 __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
@@ -207,12 +232,15 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     for (int h = 0; h < GM; ++h) sc[h] = 0.f;
     if (valid) {
       const uint32_t* r = rows + lane * kw;
-#pragma unroll 4
-      for (int j = 0; j < d; ++j) {
-        const float c = s_ck[dfield(r, j, kb)];
-#pragma unroll
-        for (int h = 0; h < GM; ++h)
-          if (h < G) sc[h] += s_q[h * d + j] * c;
+      switch (kb) {
+        case 1: dense_scores<GM, 1>(r, d, G, s_q, s_ck, sc); break;
+        case 2: dense_scores<GM, 2>(r, d, G, s_q, s_ck, sc); break;
+        case 3: dense_scores<GM, 3>(r, d, G, s_q, s_ck, sc); break;
+        case 4: dense_scores<GM, 4>(r, d, G, s_q, s_ck, sc); break;
+        case 5: dense_scores<GM, 5>(r, d, G, s_q, s_ck, sc); break;
+        case 6: dense_scores<GM, 6>(r, d, G, s_q, s_ck, sc); break;
+        case 7: dense_scores<GM, 7>(r, d, G, s_q, s_ck, sc); break;
+        default: dense_scores<GM, 8>(r, d, G, s_q, s_ck, sc); break;
       }
     }
 #pragma unroll
@@ -233,7 +261,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     const uint32_t* vsrc = vbase + (size_t)t0 * vw;
     for (int k = lane; k < cnt * vw; k += 64) rows[k] = vsrc[k];
     dwave_sync();
-#pragma unroll 2
+#pragma unroll 4
     for (int t = 0; t < cnt; ++t) {
       const uint32_t* r = rows + t * vw;
 #pragma unroll
