@@ -52,13 +52,23 @@ __device__ __forceinline__ float dwave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-// The b-bit field of coordinate j in a packed row of dwords (the field never
-// reaches past the row's last dword).
-__device__ __forceinline__ uint32_t dfield(const uint32_t* r, int j, int b) {
-  const int p = j * b, wi = p >> 5, sh = p & 31;
-  uint32_t f = r[wi] >> sh;
-  if (sh + b > 32) f |= r[wi + 1] << (32 - sh);
-  return f & ((1u << b) - 1u);
+// Copy n dwords src -> dst (LDS) with up to 16 loads per lane in flight
+// before the first store (a load-store pair per iteration would wait out one
+// memory round trip per dword).
+__device__ __forceinline__ void stage_rows(uint32_t* dst, const uint32_t* src, int n, int lane) {
+  for (int k0 = 0; k0 < n; k0 += 64 * 16) {
+    uint32_t tmp[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + lane + 64 * u;
+      tmp[u] = k < n ? src[k] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + lane + 64 * u;
+      if (k < n) dst[k] = tmp[u];
+    }
+  }
 }
 
 // Scores of one token (this lane's K row r) against the G rotated queries,
@@ -209,6 +219,15 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
   const uint32_t* kbase = (const uint32_t*)a.k_codes + row0 * kw;
   const uint32_t* vbase = (const uint32_t*)a.v_codes + row0 * vw;
 
+  // this lane's value coordinates lane + 64 e: field positions in a V row
+  int v_wi[EM], v_sh[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    const int p = (lane + 64 * e) * vb;
+    v_wi[e] = p >> 5;
+    v_sh[e] = p & 31;
+  }
+  const uint32_t v_mask = (1u << vb) - 1u;
   float m_run[GM], l_run[GM], acc[GM][EM];
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
@@ -223,7 +242,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     const bool valid = lane < cnt;
     // K rows t0 .. t0 + cnt - 1 are contiguous
     const uint32_t* ksrc = kbase + (size_t)t0 * kw;
-    for (int k = lane; k < cnt * kw; k += 64) rows[k] = ksrc[k];
+    stage_rows(rows, ksrc, cnt * kw, lane);
     const float nk = valid ? a.k_norms[row0 + t0 + lane] : 0.f;
     const float nv = valid ? a.v_norms[row0 + t0 + lane] : 0.f;
     dwave_sync();
@@ -259,16 +278,17 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     }
     dwave_sync();  // K rows read, weights written
     const uint32_t* vsrc = vbase + (size_t)t0 * vw;
-    for (int k = lane; k < cnt * vw; k += 64) rows[k] = vsrc[k];
+    stage_rows(rows, vsrc, cnt * vw, lane);
     dwave_sync();
 #pragma unroll 4
     for (int t = 0; t < cnt; ++t) {
       const uint32_t* r = rows + t * vw;
 #pragma unroll
       for (int e = 0; e < EM; ++e) {
-        const int j = lane + 64 * e;
-        if (j < d) {
-          const float c = s_cv[dfield(r, j, vb)];
+        if (lane + 64 * e < d) {
+          uint32_t f = r[v_wi[e]] >> v_sh[e];
+          if (v_sh[e] + vb > 32) f |= r[v_wi[e] + 1] << (32 - v_sh[e]);
+          const float c = s_cv[f & v_mask];
 #pragma unroll
           for (int h = 0; h < GM; ++h)
             if (h < G) acc[h][e] += s_w[t * G + h] * c;
