@@ -175,17 +175,18 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
 // range's 64-token tiles in turn and merge at the end; one partial
 // (m, l, acc[d]) per query head and split, in base-2 units. GM and EM bound
 // the query heads per KV head and the coordinates per lane (d / 64, rounded
-// up) so that the per-lane arrays stay in registers. LDS (sized at launch):
+// up) so that the per-lane arrays stay in registers; with EX the group size
+// is exactly GM and the per-head loops have no run-time guard. LDS (sized at launch):
 // rotated queries [G][d], the two centroid tables, running (m, l) per
 // wavefront, and per wavefront a region of a.wave_stride floats holding the
 // tile's staged rows (a.rows_words dwords) and weights [64][G], reused for its
 // accumulators [G][d] at the merge.
-template <int GM, int EM>
+template <int GM, int EM, bool EX>
 __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(DenseAttendArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dlds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int d = a.dim, G = a.group, kb = a.k_bits, vb = a.v_bits;
+  const int d = a.dim, G = EX ? GM : a.group, kb = a.k_bits, vb = a.v_bits;
   float* s_q = dlds;
   float* s_ck = s_q + G * d;
   float* s_cv = s_ck + 256;
@@ -370,7 +371,7 @@ hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int GM, int EM>
+template <int GM, int EM, bool EX>
 hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) {
   constexpr int kMaxWaves = GM * EM > 8 ? 8 : 16;
   constexpr size_t kLdsLimit = 160 * 1024;
@@ -390,13 +391,13 @@ hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) 
   if (lds > kLdsLimit) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)&dense_split_kernel<GM, EM>,
+    const hipError_t e = hipFuncSetAttribute((const void*)&dense_split_kernel<GM, EM, EX>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)kLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((dense_split_kernel<GM, EM>), dim3(a.splits, a.n_kv_heads, batch),
+  hipLaunchKernelGGL((dense_split_kernel<GM, EM, EX>), dim3(a.splits, a.n_kv_heads, batch),
                      dim3(64 * nw), lds, stream, a);
   return hipGetLastError();
 }
@@ -404,12 +405,19 @@ hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) 
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream) {
   if (a.group < 1 || a.group > kDMaxG || a.dim % 32 || a.dim > kMaxDim) return hipErrorInvalidValue;
   hipError_t err;
-  if (a.group <= 4)
-    err = a.dim <= 128 ? launch_dense_split<4, 2>(a, batch, stream)
-                       : launch_dense_split<4, 4>(a, batch, stream);
+  const bool wide = a.dim > 128;
+  if (a.group == 1)  // exact group sizes: the head loops fold away
+    err = wide ? launch_dense_split<1, 4, true>(a, batch, stream)
+               : launch_dense_split<1, 2, true>(a, batch, stream);
+  else if (a.group == 4)
+    err = wide ? launch_dense_split<4, 4, true>(a, batch, stream)
+               : launch_dense_split<4, 2, true>(a, batch, stream);
+  else if (a.group < 4)
+    err = wide ? launch_dense_split<4, 4, false>(a, batch, stream)
+               : launch_dense_split<4, 2, false>(a, batch, stream);
   else
-    err = a.dim <= 128 ? launch_dense_split<16, 2>(a, batch, stream)
-                       : launch_dense_split<16, 4>(a, batch, stream);
+    err = wide ? launch_dense_split<16, 4, false>(a, batch, stream)
+               : launch_dense_split<16, 2, false>(a, batch, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dense_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, stream, a);
   return hipGetLastError();

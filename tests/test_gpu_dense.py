@@ -120,6 +120,8 @@ def _attend_case(d, kb, vb, G, Hkv, lengths, T, seed):
     (192, 4, 4, 4, 2, [777, 129], 777),
     (32, 1, 8, 16, 1, [5000], 5000),             # 16 query heads per KV head, many splits
     (224, 2, 5, 8, 1, [63, 65], 65),
+    (192, 3, 4, 1, 3, [400, 129], 400),          # one query head per KV head, d > 128
+    (96, 4, 2, 4, 2, [300, 77], 300),            # four per KV head, d <= 128
 ])
 def test_dense_attend_matches_oracle(d, kb, vb, G, Hkv, lengths, T):
     announce(f"dense attend d={d} K{kb}/V{vb} G={G} Hkv={Hkv} lengths={lengths}")
