@@ -6,7 +6,7 @@
 // The caller supplies m (d x d, m / sqrt(d) orthogonal, d a multiple of 32 up
 // to 256). With m = H diag(sigma) this is exactly the Walsh-Hadamard codec.
 //
-// Encode, per fp16 vector x (one wavefront per vector):
+// Encode, per fp16 vector x (four vectors per wavefront):
 //   N = sqrt(sum_j x_j^2)  fp64; pairwise tree in index order, an odd last
 //                          element carried up to the next level
 //   w = m x                fp64; products and sums in index order, no fused
@@ -98,75 +98,103 @@ __device__ __forceinline__ void dense_scores(const uint32_t* r, int d, int G, co
 
 // ---------------------------------------------------------------- encode
 
+constexpr int kVPW = 4;  // vectors per encode wavefront: each column load of m serves all
+
 __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
 #pragma clang fp contract(off)
   __shared__ float s_bnd[256];
-  __shared__ double s_x[kDW][kMaxDim];
+  __shared__ double s_x[kDW][kVPW][kMaxDim];
   __shared__ double s_t[kDW][2][kMaxDim];
-  __shared__ uint32_t s_row[kDW][kMaxDim * 8 / 32];
+  __shared__ uint32_t s_row[kDW][kVPW][kMaxDim * 8 / 32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb = (1 << a.bits) - 1;
   s_bnd[threadIdx.x] = (int)threadIdx.x < nb ? a.boundaries[threadIdx.x] : 0.f;
   __syncthreads();
   const long long nvec = (long long)a.n_tok * a.n_head;
-  const long long v = (long long)blockIdx.x * kDW + wave;
-  if (v >= nvec) return;  // whole wavefront
-  const long long t = v / a.n_head, h = v - t * a.n_head;
-  const int d = a.dim;
-  const __half* x = (const __half*)a.x + t * a.xs_tok + h * a.xs_head;
-  double* xs = s_x[wave];
-  double* cur = s_t[wave][0];
-  double* nxt = s_t[wave][1];
-  for (int j = lane; j < d; j += 64) {
-    const double xv = (double)__half2float(x[j]);
-    xs[j] = xv;
-    cur[j] = xv * xv;  // exact
-  }
-  dwave_sync();
-  for (int w = d; w > 1; w = (w + 1) >> 1) {
-    for (int i = lane; i < (w >> 1); i += 64) nxt[i] = cur[2 * i] + cur[2 * i + 1];
-    if ((w & 1) && lane == 0) nxt[w >> 1] = cur[w - 1];
-    dwave_sync();
-    double* tmp = cur;
-    cur = nxt;
-    nxt = tmp;
-  }
-  const double nrm = __builtin_sqrt(cur[0]);
-  const int b = a.bits, words = d * b / 32;
-  uint32_t* srow = s_row[wave];
-  for (int k = lane; k < words; k += 64) srow[k] = 0u;
-  dwave_sync();
-  double acc[kMaxDim / 64];
+  const long long v0 = ((long long)blockIdx.x * kDW + wave) * kVPW;
+  if (v0 >= nvec) return;  // whole wavefront
+  const int nv = nvec - v0 < kVPW ? (int)(nvec - v0) : kVPW;
+  const int d = a.dim, b = a.bits, words = d * b / 32;
+  double nrm[kVPW];
 #pragma unroll
-  for (int e = 0; e < kMaxDim / 64; ++e) acc[e] = 0.0;
-#pragma unroll 8
+  for (int u = 0; u < kVPW; ++u) {
+    double* xs = s_x[wave][u];
+    double* cur = s_t[wave][0];
+    double* nxt = s_t[wave][1];
+    if (u < nv) {
+      const long long v = v0 + u, t = v / a.n_head, h = v - t * a.n_head;
+      const __half* x = (const __half*)a.x + t * a.xs_tok + h * a.xs_head;
+      for (int j = lane; j < d; j += 64) {
+        const double xv = (double)__half2float(x[j]);
+        xs[j] = xv;
+        cur[j] = xv * xv;  // exact
+      }
+    } else {
+      for (int j = lane; j < d; j += 64) xs[j] = cur[j] = 0.0;
+    }
+    for (int k = lane; k < words; k += 64) s_row[wave][u][k] = 0u;
+    dwave_sync();
+    // sum of squares: pairwise tree in index order, an odd last element carried up
+    for (int w = d; w > 1; w = (w + 1) >> 1) {
+      for (int i = lane; i < (w >> 1); i += 64) nxt[i] = cur[2 * i] + cur[2 * i + 1];
+      if ((w & 1) && lane == 0) nxt[w >> 1] = cur[w - 1];
+      dwave_sync();
+      double* tmp = cur;
+      cur = nxt;
+      nxt = tmp;
+    }
+    nrm[u] = __builtin_sqrt(cur[0]);
+    dwave_sync();  // the tree buffers are reused by the next vector
+  }
+  // w = m x for the wavefront's vectors: products and sums in index order
+  double acc[kVPW][kMaxDim / 64];
+#pragma unroll
+  for (int u = 0; u < kVPW; ++u)
+#pragma unroll
+    for (int e = 0; e < kMaxDim / 64; ++e) acc[u][e] = 0.0;
+#pragma unroll 4
   for (int j = 0; j < d; ++j) {  // d is a multiple of 32
-    const double xj = xs[j];
     const double* col = a.mt + (size_t)j * d;
 #pragma unroll
     for (int e = 0; e < kMaxDim / 64; ++e) {
       const int i = lane + 64 * e;
-      if (i < d) acc[e] = acc[e] + col[i] * xj;
+      if (i < d) {
+        const double m = col[i];
+#pragma unroll
+        for (int u = 0; u < kVPW; ++u) acc[u][e] = acc[u][e] + m * s_x[wave][u][j];
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < kMaxDim / 64; ++e) {
-    const int i = lane + 64 * e;
-    if (i < d) {
-      const double z = nrm == 0.0 ? 0.0 : acc[e] / nrm;
-      int c = 0;
-      for (int s = (nb + 1) >> 1; s >= 1; s >>= 1)
-        if ((double)s_bnd[c + s - 1] < z) c += s;
-      // LSB-first: the code occupies stream bits i*b .. i*b + b - 1
-      const int p = i * b, wi = p >> 5, sh = p & 31;
-      atomicOr(&srow[wi], (uint32_t)c << sh);
-      if (sh + b > 32) atomicOr(&srow[wi + 1], (uint32_t)c >> (32 - sh));
+  for (int u = 0; u < kVPW; ++u) {
+    if (u < nv) {
+      uint32_t* srow = s_row[wave][u];
+#pragma unroll
+      for (int e = 0; e < kMaxDim / 64; ++e) {
+        const int i = lane + 64 * e;
+        if (i < d) {
+          const double z = nrm[u] == 0.0 ? 0.0 : acc[u][e] / nrm[u];
+          int c = 0;
+          for (int s = (nb + 1) >> 1; s >= 1; s >>= 1)
+            if ((double)s_bnd[c + s - 1] < z) c += s;
+          // LSB-first: the code occupies stream bits i*b .. i*b + b - 1
+          const int p = i * b, wi = p >> 5, sh = p & 31;
+          atomicOr(&srow[wi], (uint32_t)c << sh);
+          if (sh + b > 32) atomicOr(&srow[wi + 1], (uint32_t)c >> (32 - sh));
+        }
+      }
     }
   }
   dwave_sync();
-  uint32_t* row = (uint32_t*)(a.codes + t * a.cs_tok + h * a.cs_head);
-  for (int k = lane; k < words; k += 64) row[k] = srow[k];
-  if (lane == 0) a.norms[t * a.ns_tok + h * a.ns_head] = (float)nrm;
+#pragma unroll
+  for (int u = 0; u < kVPW; ++u) {
+    if (u < nv) {
+      const long long v = v0 + u, t = v / a.n_head, h = v - t * a.n_head;
+      uint32_t* row = (uint32_t*)(a.codes + t * a.cs_tok + h * a.cs_head);
+      for (int k = lane; k < words; k += 64) row[k] = s_row[wave][u][k];
+      if (lane == 0) a.norms[t * a.ns_tok + h * a.ns_head] = (float)nrm[u];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- attend
@@ -365,7 +393,8 @@ __global__ __launch_bounds__(256) void dense_combine_kernel(DenseAttendArgs a) {
 hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
   const long long nvec = (long long)a.n_tok * a.n_head;
   if (nvec <= 0) return hipSuccess;
-  const long long blocks = (nvec + kDW - 1) / kDW;
+  const long long per_block = (long long)kDW * kVPW;
+  const long long blocks = (nvec + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(dense_encode_kernel, dim3((unsigned)blocks), dim3(64 * kDW), 0, stream, a);
   return hipGetLastError();
