@@ -258,12 +258,13 @@ tq_status tq_codec_init_dense(int dim, int bits, const double* rotation, tq_code
   if (e == hipSuccess) e = hipMalloc((void**)&c->mt_dev, n * sizeof(double));
   if (e == hipSuccess) e = hipMemcpy(c->m_dev, rotation, n * sizeof(double), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->mt_dev, mt, n * sizeof(double), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = tq::prepare_attend_dense();
   delete[] mt;
   if (e != hipSuccess) {
     if (c->m_dev) (void)hipFree(c->m_dev);
     if (c->mt_dev) (void)hipFree(c->mt_dev);
     delete c;
-    return fail(TQ_ERR_HIP, "%s: device copy of the rotation failed: %s", fn,
+    return fail(TQ_ERR_HIP, "%s: device set-up failed: %s", fn,
                 hipGetErrorString(e));
   }
   *out = c;

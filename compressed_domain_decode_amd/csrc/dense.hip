@@ -400,10 +400,18 @@ hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+constexpr size_t kDenseLdsLimit = 160 * 1024;
+
+template <int GM, int EM, bool EX>
+hipError_t allow_dense_lds() {
+  return hipFuncSetAttribute((const void*)&dense_split_kernel<GM, EM, EX>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDenseLdsLimit);
+}
+
 template <int GM, int EM, bool EX>
 hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) {
   constexpr int kMaxWaves = GM * EM > 8 ? 8 : 16;
-  constexpr size_t kLdsLimit = 160 * 1024;
+  constexpr size_t kLdsLimit = kDenseLdsLimit;
   const int G = a.group, d = a.dim;
   const int kw = d * a.k_bits / 32, vw = d * a.v_bits / 32;
   a.rows_words = kDTile * (kw > vw ? kw : vw);
@@ -418,17 +426,19 @@ hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) 
   while (nw > 1 && bytes(nw) > kLdsLimit) nw >>= 1;
   const size_t lds = bytes(nw);
   if (lds > kLdsLimit) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)&dense_split_kernel<GM, EM, EX>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)kLdsLimit);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   hipLaunchKernelGGL((dense_split_kernel<GM, EM, EX>), dim3(a.splits, a.n_kv_heads, batch),
                      dim3(64 * nw), lds, stream, a);
   return hipGetLastError();
+}
+
+hipError_t prepare_attend_dense() {
+  const hipError_t e[] = {allow_dense_lds<1, 2, true>(),   allow_dense_lds<1, 4, true>(),
+                          allow_dense_lds<4, 2, true>(),   allow_dense_lds<4, 4, true>(),
+                          allow_dense_lds<4, 2, false>(),  allow_dense_lds<4, 4, false>(),
+                          allow_dense_lds<16, 2, false>(), allow_dense_lds<16, 4, false>()};
+  for (const hipError_t x : e)
+    if (x != hipSuccess) return x;
+  return hipSuccess;
 }
 
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream) {

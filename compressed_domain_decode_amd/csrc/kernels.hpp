@@ -144,6 +144,9 @@ struct DenseAttendArgs {
   float v_centroids[256];
 };
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream);
+// Lets the dense attend kernels use up to 160 KB of LDS on the current device;
+// called at codec set-up so no launch (or graph capture) makes the call.
+hipError_t prepare_attend_dense();
 float dense_qscale(float scale, int dim);
 
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).

@@ -175,3 +175,45 @@ def test_dense_codecs_rejected_where_unsupported():
         tq.tq_decode_attend_multi(kc, kc, q.view(1, 2, 1, d), k, n, k, n, lengths, 64, 0.1,
                                   out.view(1, 2, 1, d), ws)
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_dense_graph_replay_matches_eager():
+    """The dense attend captured in a HIP graph: three replays, with eager work
+    between them, bitwise equal to the eager call."""
+    d, G, Hkv, T = 96, 3, 2, 700
+    announce(f"dense attend graph replay d={d} G={G} T={T}")
+    kc, _ = dense_codecs(d, 4, 21)
+    vc, _ = dense_codecs(d, 3, 22)
+    rng = np.random.default_rng(23)
+    k = _inputs(rng, (1, Hkv, T, d), d)
+    v = _inputs(rng, (1, Hkv, T, d), d)
+    q = torch.from_numpy(rng.standard_normal((1, G * Hkv, d)).astype(np.float16)).to(DEV)
+    kcodes, knorms = gpu_encode_cache(kc, k)
+    vcodes, vnorms = gpu_encode_cache(vc, v)
+    lengths = torch.tensor([T], dtype=torch.int32, device=DEV)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(1, G * Hkv, Hkv, d, T), dtype=torch.uint8,
+                     device=DEV)
+    eager = torch.empty((1, G * Hkv, d), dtype=torch.float32, device=DEV)
+    tq.tq_decode_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, T, 0.1, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.full_like(eager, float("nan"))
+
+    def call():
+        tq.tq_decode_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths, T, 0.1, out, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        out.fill_(float("nan"))
+        ws.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
