@@ -153,7 +153,10 @@ tq_status tq_codec_init_prod(int dim, int bits, uint64_t seed, tq_codec** out);
  * two-phase cache return TQ_ERR_UNSUPPORTED for dense codecs.
  * dim: a multiple of 32 in [32, 256] (so rows are whole dwords), else
  * TQ_ERR_UNSUPPORTED; bits in [1, 8]. TQ_ERR_INVALID_ARG for a NULL rotation
- * or a non-finite entry, TQ_ERR_HIP if the device copy fails. tq_codec_tables
+ * or a non-finite entry, TQ_ERR_HIP if the device copy or the one-time set-up
+ * of the dense attend kernels (their LDS limit on the current device) fails.
+ * Codec set-up, not the attend call, makes that runtime call, so attend calls
+ * can be captured in a HIP graph. tq_codec_tables
  * reports signs of +1 and tq_codec_info a seed of 0 for a dense codec.
  */
 tq_status tq_codec_init_dense(int dim, int bits, const double* rotation, tq_codec** out);
