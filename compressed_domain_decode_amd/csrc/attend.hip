@@ -16,23 +16,36 @@
 // 1. attend_split (the hot one). Grid (splits, kv heads, batch); each
 //    workgroup owns one context range of one (sequence, KV head) and all G
 //    query heads that read it; its wavefronts stream 64-token tiles.
-//    Per tile, both contractions run on the fp32 matrix cores with the
-//    v_mfma_f32_4x4x1 16-block instruction, while the VALU and LDS only
-//    unpack codes and look centroids up:
+//    Both contractions run on the matrix cores as fp16 4x4x4 products with
+//    fp32 accumulation, each fp32 operand carried as an fp16 pair hi + lo
+//    (hi the nearest fp16, lo the nearest fp16 of the remainder; about 22
+//    significant bits). On gfx950 the fp16 matrix instructions issue
+//    alongside VALU work, which the fp32 ones do not, so the unpacking and
+//    table addressing overlap the products. The 4-deep reduction of an
+//    instruction is laid out as (hi_j, lo_j, hi_j', lo_j') of two
+//    coordinates (scores) or two tokens (values), so a centroid entry
+//    (hi, lo) read from LDS is an operand as it stands:
 //      scores  S[h][t] = sum_j q^[h][j] * cK[idxK[t][j]]
-//              lane t holds token t's packed K row; for each coordinate j the
-//              centroid it looks up is the B operand, and the A operand is
-//              q^[h][j] broadcast from one 4-lane block (CBSZ/ABID), so one
-//              VGPR carries q^ for 16 coordinates and lane t ends with the 4
-//              heads' scores of token t.
+//              lane t holds token t's packed K row. Per coordinate pair the
+//              B operand is the two centroid entries; the A operand, broadcast
+//              from one 4-lane block, is (qh_j, qh_j, qh_j', qh_j') for the
+//              first product and (ql_j, 0, ql_j', 0) for the second, so the
+//              sum is qh (ch + cl) + ql ch. Lane t ends with the 4 heads'
+//              scores of token t.
 //      softmax online softmax in base 2 (log2 e folded into q^), per head
 //              running max from a cross-lane reduction; weights p * nV_t.
 //      values  A[h][j] += sum_t w[h][t] * cV[idxV[t][j]]
 //              lanes own coordinates. The lane holding token t stages t's
 //              packed V row in LDS; per token each lane reads the two dwords
 //              that hold its code(s), funnel-shifts them and looks the
-//              centroid up. The 4 heads' weights are broadcast the same way
-//              as q^.
+//              centroid entry up; two tokens' entries form the B operand and
+//              the weights, (wh_t, wh_t, wh_t', wh_t') and (wl_t, 0, wl_t', 0),
+//              the broadcast A operand.
+//    Scale factors (powers of two, exact) keep every fp16 half in the normal
+//    range: the rotated queries of a workgroup and each codebook are scaled
+//    so their largest magnitude lies in [2^13, 2^14), and the weights carry
+//    2^(6 - Ev) with 2^Ev above every V norm seen so far (Ev only grows, and
+//    the accumulators are rescaled when it does).
 //    The online softmax moves its running maximum only when a tile's
 //    maximum exceeds it by more than 2^8, so the rescale is rare.
 //    Centroid tables live in LDS replicated once per bank (a 256-byte row
@@ -53,6 +66,7 @@
 #include <utility>
 
 #include "kernels.hpp"
+#include "xlane.hpp"
 
 namespace tq {
 
@@ -63,6 +77,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));  // two dwords, kept in registers
 
 template <int... Is, class F>
 __device__ __forceinline__ void sfor_impl(std::integer_sequence<int, Is...>, F&& f) {
@@ -80,6 +96,35 @@ __device__ __forceinline__ void sfor(F&& f) {
 template <int ABID>
 __device__ __forceinline__ v4f mfma_bcast(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
+}
+// The fp16 form: D[v] += sum_k A_bcast[v][k] * B[lane][k] over the 4 halves
+// k of the operands, A taken from block ABID (lane 4 ABID + v).
+template <int ABID>
+__device__ __forceinline__ v4f mfma16(v4h a, v4h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
+}
+__device__ __forceinline__ v4h as_v4h(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(v4h, u2v{lo, hi});
+}
+
+// x as an fp16 pair in one dword: the low half is the nearest fp16 of x, the
+// high half the nearest fp16 of what remains (x - hi is exact in fp32).
+__device__ __forceinline__ uint32_t split_hl(float x) {
+  const _Float16 h = (_Float16)x;
+  const _Float16 l = (_Float16)(x - (float)h);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+}
+// 2^e for e in [-126, 127].
+__device__ __forceinline__ float exp2i(int e) {
+  return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+// The exponent e with m * 2^e in [2^13, 2^14) for a positive finite m (0 for
+// anything else), clamped to the normal range.
+__device__ __forceinline__ int hl_exponent(float m) {
+  if (!(m > 0.f) || !(m < INFINITY)) return 0;
+  const int e = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;
+  return min(126, max(-126, 13 - e));
 }
 
 template <int CTRL>
@@ -101,20 +146,23 @@ __device__ __forceinline__ float wave_max(float v) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
-// Maximum over the wavefront of finite or -inf scores, returned in every lane:
-// the same DPP pattern on an order-preserving integer key (the bits, with the
-// magnitude bits flipped for negative values), so each step is one fused
-// v_max_i32_dpp with no NaN quieting, and the maximum is exact.
-__device__ __forceinline__ float wave_max_key(float f) {
-  const int b = __builtin_bit_cast(int, f);
-  int k = b ^ ((b >> 31) & 0x7FFFFFFF);
+// Maximum over the wavefront of signed integers, returned in every lane (the
+// same DPP pattern; each step one fused v_max_i32_dpp).
+__device__ __forceinline__ int wave_max_int(int k) {
   constexpr int kLow = (int)0x80000000;  // identity of the max for the DPP's inactive sources
   k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x141, 0xF, 0xF, false));  // row_half_mirror
   k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x140, 0xF, 0xF, false));  // row_mirror
-  const int r = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
-                    max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+  return max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+             max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+}
+// Maximum over the wavefront of finite or -inf scores, returned in every lane:
+// the integer maximum of an order-preserving key (the bits, with the
+// magnitude bits flipped for negative values), exact and without NaN quieting.
+__device__ __forceinline__ float wave_max_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  const int r = wave_max_int(b ^ ((b >> 31) & 0x7FFFFFFF));
   return __builtin_bit_cast(float, r ^ ((r >> 31) & 0x7FFFFFFF));
 }
 // Sum over the wavefront, returned in every lane (same DPP pattern).
@@ -154,9 +202,12 @@ __device__ __forceinline__ uint32_t field_at8(const uint32_t (&w)[NW]) {
 }
 
 // Centroid tables live in LDS as one 256-byte row per code (or code pair):
-// 64 copies of a 4-byte centroid, or 32 copies of an 8-byte centroid pair, so
-// that every lane reads its own copy and a lookup never has a bank conflict,
-// whatever the codes. A lookup address is (code << 8) | lane_offset.
+// 64 copies of a 4-byte entry (hi, lo) or 32 copies of an 8-byte pair entry
+// (hi, lo, hi', lo'), so that every lane reads its own copy and a lookup
+// never has a bank conflict, whatever the codes. A lookup address is
+// (code << 8) | lane_offset.
+constexpr int kVPad = 4;  // dwords of padding around a wavefront's staged V rows
+
 template <int D_, int BK_, int BV_, int NHG_, int WAVES_>
 struct CfgBase {
   static constexpr int D = D_, BK = BK_, BV = BV_, NHG = NHG_, WAVES = WAVES_;
@@ -172,58 +223,73 @@ struct CfgBase {
   static constexpr int KF = KPAIR ? 2 * KBITS : KBITS; // bits per K lookup
   static constexpr int SKW = PROD ? D / 32 : 1;        // sketch dwords per K row
   static constexpr int VF = VPAIR ? 2 * BV : BV;       // bits per V lookup
-  static constexpr int NKL = KPAIR ? D / 2 : D;        // K lookups per token
   static constexpr int NVS = VPAIR ? D / 128 : D / 64; // V lookups per lane per token
   static constexpr int RKW = D * KBITS / 32;           // dwords per K row
   static constexpr int RVW = D * BV / 32;              // dwords per V row
-  // V rows of a tile staged contiguously in LDS (row t at dword 2 + t RVW,
-  // 2 dwords of padding on each side): a lane reads the two dwords around its
-  // field, which may reach from the dword before the row to the dword after
-  // it (a neighbouring row or padding; those bits are masked off).
+  // K operand registers: raw keys take 4 coordinates per product (the row's
+  // own fp16 values), coded keys 2 coordinates (hi, lo each)
+  static constexpr int QREG = KRAW ? D / 64 : D / 32;  // v4h registers per head group (hi or lo)
+  // V rows of a tile staged contiguously in LDS (row t at dword kVPad + t RVW,
+  // kVPad dwords of padding on each side), copied there from HBM by the
+  // wavefront's own global-to-LDS loads: a lane reads the two dwords around
+  // its field, which may reach from the dword before the row to the dword
+  // after it (a neighbouring row or padding; those bits are masked off).
   static constexpr int VT_BYTES = (1 << VF) * 256;
   static constexpr int KT_BYTES = KRAW ? 0 : (1 << KF) * 256;
-  static constexpr int VS_BYTES = (kTile * RVW + 4) * 4;  // per wavefront
-  static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights of a tile
-  // rotated queries (and for Prod keys their sketch projections)
-  static constexpr int QS_BYTES = (PROD ? 2 : 1) * 4 * NHG * D * 4;
-  static constexpr int CEN_BYTES = 2 * 256 * 4;         // plain centroid tables while filling
-  static constexpr int GATE_BYTES = (WAVES * 4 + 15) / 16 * 16;  // first-tile arrival flags
+  static constexpr int VS_BYTES = (kTile * RVW + 2 * kVPad) * 4;  // per wavefront
+  // global-to-LDS copy of a tile's V rows: 16 bytes per lane when the block
+  // is a whole number of 1 KB pieces, else 4 bytes per lane
+  static constexpr bool VDMA16 = RVW % 4 == 0;
+  static constexpr int VDMA_OPS = VDMA16 ? RVW / 4 : RVW;
+  static constexpr int WB_BYTES = kTile * 4 * NHG * 4;  // per wavefront: weights (hi, lo) of a tile
+  // rotated queries (and for Prod keys their sketch projections), then one
+  // maximum magnitude per virtual head
+  static constexpr int QS_BYTES = (PROD ? 2 : 1) * 4 * NHG * D * 4 + 4 * NHG * 4;
+  // first-tile arrival flags and the workers' tables-ready counter
+  static constexpr int GATE_BYTES = ((WAVES + 1) * 4 + 15) / 16 * 16;
   static constexpr int MAIN_BYTES =
-      VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + CEN_BYTES + GATE_BYTES;
+      VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + GATE_BYTES;
   static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * NHG * D) * 4;
   static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+  // value accumulators per head group and half (hi or lo weights): one per
+  // coordinate a lane owns; two (even and odd token pairs) when it owns one
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
 };
 
 constexpr int kLdsPerCU = 163840;
 
-// Software-pipeline depths of the tile loop: K lookups per batch, tokens per
-// batch of the values phase.
-constexpr int kKBatch = 8;
-constexpr int kVBatch = 4;
+// Software-pipeline depths of the tile loop: K coordinate pairs whose
+// lookups run ahead of the products, token pairs per batch of the values
+// phase.
+constexpr int kKAhead = 6;
+constexpr int kVBatch = 1;
 
-// Rough count of the VGPRs one lane holds through the tile loop: rotated
-// queries, norms, value accumulators, weight and softmax state, V field
-// positions, the V row being staged, plus the larger of the scores phase (the
-// K row, two batches of lookups, four accumulator chains) and the values
-// phase (three batches of staged dwords, two of lookups).
+// Rough count of the VGPRs one lane holds through the tile loop: query
+// operands (hi and lo), norms, value accumulators, weight operands and
+// softmax state, V field positions, the tile's K row, plus the larger of the
+// scores phase (two batches of lookups, four accumulator chains) and the
+// values phase (three batches of staged dwords, two of lookups).
 template <class B>
 constexpr int vgpr_estimate() {
-  constexpr int base = B::NHG * B::D / 16 + 2 + B::NACC * B::NHG * 4 + B::NHG * 20 + 2 * B::NVS;
-  constexpr int kphase = B::RKW + 2 * kKBatch * (B::KPAIR ? 2 : 1) + 16 * B::NHG;
-  constexpr int vphase = 3 * kVBatch * B::NVS * 2 + 2 * kVBatch * B::NVS * (B::VPAIR ? 2 : 1);
-  constexpr int prod = B::PROD ? B::D / 32 + 1 + B::NHG * B::D / 16 + 16 * B::NHG : 0;
+  constexpr int base = B::NHG * B::QREG * 4 + 3 + 2 * B::NACC * B::NHG * 4 + B::NHG * 24 +
+                       2 * B::NVS + B::RKW + B::SKW;
+  constexpr int kphase = 2 * (kKAhead + 1) + 16 * B::NHG;
+  constexpr int vphase = 3 * 2 * kVBatch * B::NVS * 2 + 2 * 2 * kVBatch * B::NVS * (B::VPAIR ? 2 : 1);
+  constexpr int prod = B::PROD ? B::NHG * B::D / 16 + 16 * B::NHG : 0;
   return base + prod + (kphase > vphase ? kphase : vphase);
 }
 
 // Wavefronts per workgroup: as many as the LDS and the register file allow
 // (16, 12, 8 or 4; 128, 168 or 256 VGPRs per lane); the centroid tables are
 // shared by all of them.
+// The estimate runs about 20 above what the compiler allocates; 148 is the
+// largest value whose compiled kernel fits 128 VGPRs without spilling in the
+// tile loop (the 32K-context K8/V3 configuration sits just under it).
 template <int D, int BK, int BV, int NHG>
 constexpr int cfg_waves() {
   using B = CfgBase<D, BK, BV, NHG, 4>;
-  constexpr int need = vgpr_estimate<B>() + 24;  // + addresses, temporaries
-  if (NHG < 4 && need <= 128 && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
+  constexpr int need = vgpr_estimate<B>() + 16;  // + addresses, temporaries
+  if (NHG < 4 && need <= 152 && CfgBase<D, BK, BV, NHG, 16>::LDS_BYTES <= kLdsPerCU) return 16;
   if (NHG < 4 && need <= 168 && CfgBase<D, BK, BV, NHG, 12>::LDS_BYTES <= kLdsPerCU) return 12;
   if (CfgBase<D, BK, BV, NHG, 8>::LDS_BYTES <= kLdsPerCU) return 8;
   return 4;
@@ -244,14 +310,20 @@ struct CfgShort : CfgBase<D, BK, BV, NHG, 4> {
 };
 constexpr int kShortTiles = 4;  // ranges up to this many tiles use the short workgroup
 
-// One tile's worth of this lane's token: packed K and V rows and the norms.
+// One tile's worth of this lane's token in registers: the packed K row and
+// the norms (the V rows go straight to LDS).
 template <class C>
 struct TileRegs {
   uint32_t kw[C::RKW];
-  uint32_t vw[C::RVW];
   uint32_t sk[C::SKW];  // Prod keys: sketch bits
   float nk, nv, rn;     // rn: Prod keys' residual norm
 };
+// Vector-memory instructions of one load_k (its vmcnt footprint).
+template <class C>
+constexpr int k_loads() {
+  return 1 + (C::KRAW ? 0 : 1) + (C::PROD ? 1 + C::SKW / 2 : 0) +
+         (C::RKW % 4 == 0 ? C::RKW / 4 : C::RKW / 2);
+}
 
 // TurboQuant-Prod keys: per-row sketch bits [.][Hkv][max_ctx][D/8] and residual
 // norms [.][Hkv][max_ctx], the sketch signs sigma_S, and the factor taking the
@@ -268,6 +340,9 @@ struct ProdArgs {
 // is only moved when a tile's maximum exceeds it by more than this, so
 // weights stay below 2^8 and the rescale is rare.
 constexpr float kRescaleSlack = 8.f;
+// Weights are p * nV * 2^(kWeightExp - Ev) < 2^(8 + kWeightExp) (p <= 2^8,
+// nV < 2^Ev): below the fp16 maximum with room to spare.
+constexpr int kWeightExp = 6;
 
 // First tiles in flight per workgroup. Wavefronts 0 .. kGateDepth-1 request
 // their first tile at once; wavefront w >= kGateDepth requests its first tile
@@ -286,6 +361,7 @@ constexpr int kGateSpins = 1 << 16;
 // Flag word in LDS read and written with LDS instructions the compiler does not
 // order against vector memory, so polling never waits for this wavefront's own
 // outstanding row loads.
+typedef const __attribute__((address_space(3))) uint32_t lds_u32;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -303,6 +379,11 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt on the LDS (and scalar memory) counter only: lgkmcnt(0).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 // Workgroup barrier that orders LDS only: it does not wait for the caller's
@@ -327,10 +408,10 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int len = min(lengths[b], max_len);  // never read past the host bound
   const int t_begin = split * tokens_per_split;
-  if (t_begin >= len) return;  // whole workgroup: range past the sequence end
-  const int t_end = min(len, t_begin + tokens_per_split);
+  // rows [t_begin, t_host) lie inside the cache allocation whatever the
+  // device lengths are (max_len <= max_ctx)
+  const int t_host = min(max_len, t_begin + tokens_per_split);
   const int G = group;
   const int n_q_heads = n_kv_heads * G;
   // The workgroup serves GV = G * n_qtok virtual heads: virtual head vh is
@@ -342,10 +423,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   unsigned char* vt = lds;
   unsigned char* kt = lds + C::VT_BYTES;
   uint32_t* vstage = (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + wave * C::VS_BYTES);
-  float* wbuf = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + wave * C::WB_BYTES);
+  uint32_t* wbuf =
+      (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + wave * C::WB_BYTES);
   float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * (C::VS_BYTES + C::WB_BYTES));
-  float* cen = wq + C::QS_BYTES / 4;
-  int* gate = (int*)(cen + C::CEN_BYTES / 4);
+  float* qmax = wq + (C::PROD ? 2 : 1) * 4 * NHG * D;  // [4 NHG] largest |q^| per virtual head
+  int* gate = (int*)(qmax + 4 * NHG);
 
   const long long kvrow0 = ((long long)b * n_kv_heads + g) * max_ctx;
   const uint32_t* __restrict__ kbase = (const uint32_t*)k_codes + kvrow0 * RKW;
@@ -355,30 +437,39 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   const uint32_t* __restrict__ skb = (const uint32_t*)pa.sketch + kvrow0 * C::SKW;
   const float* __restrict__ rnb = pa.rnorms + kvrow0;
 
-  // ---- tile registers: this lane's token rows and norms. Lanes past the
-  //      range end load the range's last row instead (always in bounds); their
-  //      scores are masked to -inf, so the rows never contribute.
-  auto load_tile = [&](int tile, TileRegs<C>& r) __attribute__((always_inline)) {
-    const int t = min(tile + lane, t_end - 1);
-    const uint32_t* kr = kbase + (long long)t * RKW;
-    const uint32_t* vr = vbase + (long long)t * RVW;
-    // written in the order they are consumed (V norm and row, staged first;
-    // then K norm and row): vector loads complete in order, so the scores
-    // can start on the first pieces of the K row while the rest is in flight
-    r.nv = vnb[t];
-    if constexpr (RVW % 4 == 0) {
+  // ---- a tile's V rows: copied from HBM into this wavefront's LDS stage
+  //      in their own layout (rows contiguous), each instruction a coalesced
+  //      1 KB (or 256 B) piece; pieces past row `last` re-read the last
+  //      valid piece (always in bounds; those rows are never used)
+  auto load_v = [&](int tile, int last) __attribute__((always_inline)) {
+    const uint32_t* src = vbase + (long long)tile * RVW;
+    auto* dst = (__attribute__((address_space(3))) uint32_t*)(vstage + kVPad);
+    if constexpr (C::VDMA16) {
+      const int valid = (last - tile + 1) * (RVW / 4);  // 16-byte pieces
 #pragma unroll
-      for (int i = 0; i < RVW; i += 4) {
-        const uint4 x = *(const uint4*)(vr + i);
-        r.vw[i] = x.x; r.vw[i + 1] = x.y; r.vw[i + 2] = x.z; r.vw[i + 3] = x.w;
-      }
+      for (int i = 0; i < C::VDMA_OPS; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 4 * min(64 * i + lane, valid - 1)),
+                                         (__attribute__((address_space(3))) void*)(dst + 256 * i),
+                                         16, 0, 0);
     } else {
+      const int valid = (last - tile + 1) * RVW;  // dwords
 #pragma unroll
-      for (int i = 0; i < RVW; i += 2) {
-        const uint2 x = *(const uint2*)(vr + i);
-        r.vw[i] = x.x; r.vw[i + 1] = x.y;
-      }
+      for (int i = 0; i < C::VDMA_OPS; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(src + min(64 * i + lane, valid - 1)),
+                                         (__attribute__((address_space(3))) void*)(dst + 64 * i),
+                                         4, 0, 0);
     }
+  };
+  // ---- tile registers: this lane's token's norms and K row. Lanes past
+  //      `last` load row `last` instead (always in bounds); their scores are
+  //      masked to -inf and their weights are 0, so the rows never contribute.
+  auto load_k = [&](int tile, int last, TileRegs<C>& r) __attribute__((always_inline)) {
+    const int t = min(tile + lane, last);
+    const uint32_t* kr = kbase + (long long)t * RKW;
+    // V norm first, then K norm and row: vector loads complete in order, so
+    // the scores can start on the first pieces of the K row while the rest
+    // is in flight
+    r.nv = vnb[t];
     if constexpr (C::KRAW)
       r.nk = 1.f;
     else
@@ -407,119 +498,107 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
     }
   };
+  auto load_tile = [&](int tile, int last, TileRegs<C>& r) __attribute__((always_inline)) {
+    load_v(tile, last);
+    load_k(tile, last, r);
+  };
 
-  // ---- prologue, before any tile row is requested: fetch the centroid
-  //      tables, this wavefront's query rows and the sign words, build the LDS
-  //      tables and rotate the queries.
+  // ---- prologue. With more wavefronts than the gate depth, the ungated
+  //      ones (0 .. kGateDepth - 1) request their first tile at once, bounded
+  //      by the host's row bound (the device length is not waited for); the
+  //      others ("workers") fill the LDS tables and rotate the queries while
+  //      those tiles stream in. No workgroup barrier follows a tile request:
+  //      a wavefront that has requested rows may stall in issuing them for as
+  //      long as its CU's share of the bandwidth takes to drain what is ahead,
+  //      so every wavefront instead waits for an LDS counter the workers
+  //      raise when their part is written. With no more wavefronts than the
+  //      gate depth every wavefront is a worker and requests its first tile
+  //      once the tables are ready.
   const int nthr = 64 * WAVES;
-  constexpr int kCenPer = (512 + 64 * WAVES - 1) / (64 * WAVES);
-  float cenv[kCenPer];
-#pragma unroll
-  for (int u = 0; u < kCenPer; ++u) {
-    const int i = threadIdx.x + u * nthr;
-    cenv[u] = i < 256 ? tabs.v_centroids[i] : (i < 512 ? tabs.k_centroids[i - 256] : 0.f);
-  }
-  constexpr int kHeadsPerWave = (4 * NHG + WAVES - 1) / WAVES;  // GV <= 4 NHG
-  __half qx[kHeadsPerWave][E];
-#pragma unroll
-  for (int r = 0; r < kHeadsPerWave; ++r) {
-    const int vh = min(wave + r * WAVES, GV - 1);  // in bounds; surplus rows unused
-    const int qi = vh / G;
-    const __half* qrow =
-        q + (((long long)b * n_qtok + qi) * n_q_heads + (long long)g * G + (vh - qi * G)) * D;
-#pragma unroll
-    for (int e = 0; e < E; ++e) qx[r][e] = qrow[E * lane + e];
-  }
-  // sign word of this lane's coordinates E lane .. E lane + E - 1 (one word:
-  // E <= 4 consecutive coordinates never straddle a 32-bit boundary)
-  uint32_t sword = 0;
-#pragma unroll
-  for (int w = 0; w < D / 32; ++w)
-    if ((E * lane) >> 5 == w) sword = ksign.bits[w];
-
-  // ---- centroid tables: plain copies (the small loads are consumed before any
-  //      tile row is requested, so these waits cover only them), then one
-  //      replicated 256-byte row per code (pair)
-#pragma unroll
-  for (int u = 0; u < kCenPer; ++u) {
-    const int i = threadIdx.x + u * nthr;
-    if (i < 512) cen[i] = cenv[u];
-  }
-  float qf[kHeadsPerWave][E];
-#pragma unroll
-  for (int r = 0; r < kHeadsPerWave; ++r)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      qf[r][e] = __half2float(qx[r][e]);
-      asm volatile("" : "+v"(qf[r][e]) : : "memory");  // converted here, before the tile loads
-    }
-  if (threadIdx.x < WAVES) gate[threadIdx.x] = 0;
-
-  lds_barrier();
-  // the ungated wavefronts request their first tile now: every wavefront's
-  // small loads are done, and the rest of the prologue overlaps the transfer
+  constexpr bool kSplitRoles = WAVES > kGateDepth;
+  constexpr int kWorkers = kSplitRoles ? WAVES - kGateDepth : WAVES;
+  const bool worker = !kSplitRoles || wave >= kGateDepth;
+  const int widx = kSplitRoles ? wave - kGateDepth : wave;  // worker index
+  const int wtid = threadIdx.x - (kSplitRoles ? 64 * kGateDepth : 0);
   constexpr int kStride = WAVES * kTile;
   const int tile0 = t_begin + wave * kTile;
   TileRegs<C> ra;
-  // a wavefront past the range end (short ranges) has no tile: it requests
-  // nothing and waits for no gate (the later ones have none either)
-  const bool has_tile = tile0 < t_end;
-  if (wave < kGateDepth && has_tile) load_tile(tile0, ra);
-  auto fill = [&](unsigned char* tab, const float* c, int bits, bool pair) {
-    const int rows = 1 << (pair ? 2 * bits : bits);
-    const int mask = (1 << bits) - 1;
-    for (int i = threadIdx.x; i < rows * 16; i += nthr) {
-      const int e = i >> 4;
-      const v4f x = pair ? v4f{c[e & mask], c[e >> bits], c[e & mask], c[e >> bits]}
-                         : v4f{c[e], c[e], c[e], c[e]};
-      ((v4f*)tab)[i] = x;
-    }
-  };
-  fill(vt, cen, C::BV, C::VPAIR);
-  if constexpr (!C::KRAW) fill(kt, cen + 256, C::KBITS, C::KPAIR);
+  int* ready = gate + WAVES;  // worker wavefronts whose tables and queries are written
 
-  // ---- rotated queries: wavefront w rotates heads w, w + WAVES, ... into LDS
+  // table entries: 16 threads write one 256-byte row (four 16-byte copies
+  // each); a worker thread's entries are wtid, wtid + 64 kWorkers, ...
+  constexpr int kVRows = 1 << C::VF, kKRows = C::KRAW ? 0 : 1 << C::KF;
+  constexpr int kVEnt = (kVRows * 16 + 64 * kWorkers - 1) / (64 * kWorkers);
+  constexpr int kKEnt = (kKRows * 16 + 64 * kWorkers - 1) / (64 * kWorkers);
+  constexpr int kHeadsPerWave = (4 * NHG + kWorkers - 1) / kWorkers;  // GV <= 4 NHG
+  float vce[kVEnt][2], kce[kKEnt ? kKEnt : 1][2];
+  __half qx[kHeadsPerWave][E];
+  if (worker) {
+    // every small load a worker needs goes out before the barrier below,
+    // ahead of any tile row in the CU's memory pipeline (its loads drain
+    // roughly in order at its share of the bandwidth)
+    auto centroids = [&](const float* c, int bits, bool pair, int rows, float (&dst)[2], int u) {
+      const int e = min(wtid + u * 64 * kWorkers, rows * 16 - 1) >> 4;  // in bounds
+      const int mask = (1 << bits) - 1;
+      dst[0] = c[pair ? (e & mask) : e];
+      dst[1] = pair ? c[e >> bits] : 0.f;
+    };
 #pragma unroll
-  for (int r = 0; r < kHeadsPerWave; ++r) {
-    const int h = wave + r * WAVES;
-    if (h < GV) {
-      float u[E];
+    for (int u = 0; u < kVEnt; ++u) centroids(tabs.v_centroids, C::BV, C::VPAIR, kVRows, vce[u], u);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = E * lane + e;
-        const float x = qf[r][e];
-        u[e] = (!C::KRAW && ((sword >> (j & 31)) & 1u)) ? -x : x;
+    for (int u = 0; u < kKEnt; ++u)
+      centroids(tabs.k_centroids, C::KBITS, C::KPAIR, kKRows, kce[u], u);
+#pragma unroll
+    for (int r = 0; r < kHeadsPerWave; ++r) {
+      const int h = min(widx + r * kWorkers, GV - 1);  // in bounds; surplus rows unused
+      const int qi = h / G;
+      const __half* qrow =
+          q + (((long long)b * n_qtok + qi) * n_q_heads + (long long)g * G + (h - qi * G)) * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) qx[r][e] = qrow[E * lane + e];
+    }
+  }
+  if (threadIdx.x <= WAVES) gate[threadIdx.x] = 0;
+  lds_barrier();  // flags and counter cleared; the workers' small loads issued
+  if (kSplitRoles && !worker && tile0 < t_host) load_tile(tile0, t_host - 1, ra);
+
+  if (worker) {
+    // table rows of (hi, lo) entries
+    auto fill = [&](unsigned char* tab, int rows, bool pair, float cs, const float (&ce)[2], int u) {
+      const int i = wtid + u * 64 * kWorkers;
+      if (i < rows * 16) {
+        const uint32_t a = split_hl(ce[0] * cs);
+        const uint32_t bb = pair ? split_hl(ce[1] * cs) : a;
+        ((uint4*)tab)[i] = pair ? uint4{a, bb, a, bb} : uint4{a, a, a, a};
       }
-      // raw keys are scored in the original basis: no rotation
+    };
 #pragma unroll
-      for (int hs = 1; hs < (C::KRAW ? 1 : E); hs <<= 1)
+    for (int u = 0; u < kVEnt; ++u) fill(vt, kVRows, C::VPAIR, tabs.v_scale, vce[u], u);
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          if ((e & hs) == 0) {
-            const float a0 = u[e], a1 = u[e + hs];
-            u[e] = a0 + a1;
-            u[e + hs] = a0 - a1;
-          }
+    for (int u = 0; u < kKEnt; ++u) fill(kt, kKRows, C::KPAIR, tabs.k_scale, kce[u], u);
+
+    // rotated queries: worker w rotates heads w, w + kWorkers, ... into LDS
+    // and records each one's largest magnitude
+    // sign word of this lane's coordinates E lane .. E lane + E - 1 (one word:
+    // E <= 4 consecutive coordinates never straddle a 32-bit boundary)
+    uint32_t sword = 0;
 #pragma unroll
-      for (int m = 1; m < (C::KRAW ? 1 : 64); m <<= 1) {
-        const bool upper = (lane & m) != 0;
+    for (int w = 0; w < D / 32; ++w)
+      if ((E * lane) >> 5 == w) sword = ksign.bits[w];
+#pragma unroll
+    for (int r = 0; r < kHeadsPerWave; ++r) {
+      const int h = widx + r * kWorkers;
+      if (h < GV) {
+        float u[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float p = __shfl_xor(u[e], m);
-          u[e] = upper ? (p - u[e]) : (u[e] + p);
+          const int j = E * lane + e;
+          const float x = __half2float(qx[r][e]);
+          u[e] = (!C::KRAW && ((sword >> (j & 31)) & 1u)) ? -x : x;
         }
-      }
+        // raw keys are scored in the original basis: no rotation
 #pragma unroll
-      for (int e = 0; e < E; ++e) wq[h * D + E * lane + e] = u[e] * qscale;
-      if constexpr (C::PROD) {
-        // sketch projection H (sigma_S (.) q~) of the rotated query
-        uint32_t pw = pa.sign.bits[0];
-#pragma unroll
-        for (int w = 1; w < D / 32; ++w) pw = ((E * lane) >> 5 == w) ? pa.sign.bits[w] : pw;
-#pragma unroll
-        for (int e = 0; e < E; ++e) u[e] = ((pw >> ((E * lane + e) & 31)) & 1u) ? -u[e] : u[e];
-#pragma unroll
-        for (int hs = 1; hs < E; hs <<= 1)
+        for (int hs = 1; hs < (C::KRAW ? 1 : E); hs <<= 1)
 #pragma unroll
           for (int e = 0; e < E; ++e)
             if ((e & hs) == 0) {
@@ -527,37 +606,125 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
               u[e] = a0 + a1;
               u[e + hs] = a0 - a1;
             }
+        if constexpr (!C::KRAW) {
+          sfor<6>([&](auto MI) {
+            constexpr int m = 1 << MI;
+            const bool upper = (lane & m) != 0;
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-          const bool upper = (lane & m) != 0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float p = __shfl_xor(u[e], m);
-            u[e] = upper ? (p - u[e]) : (u[e] + p);
-          }
+            for (int e = 0; e < E; ++e) {
+              const float p = xor_lane_f32<m>(u[e]);
+              u[e] = upper ? (p - u[e]) : (u[e] + p);
+            }
+          });
         }
+        float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) wq[4 * NHG * D + h * D + E * lane + e] = u[e] * pa.uscale;
+        for (int e = 0; e < E; ++e) {
+          const float v = u[e] * qscale;
+          wq[h * D + E * lane + e] = v;
+          amax = fmaxf(amax, fabsf(v));
+        }
+        amax = wave_max(amax);
+        if (lane == 0) qmax[h] = amax;
+        if constexpr (C::PROD) {
+          // sketch projection H (sigma_S (.) q~) of the rotated query
+          uint32_t pw = pa.sign.bits[0];
+#pragma unroll
+          for (int w = 1; w < D / 32; ++w) pw = ((E * lane) >> 5 == w) ? pa.sign.bits[w] : pw;
+#pragma unroll
+          for (int e = 0; e < E; ++e) u[e] = ((pw >> ((E * lane + e) & 31)) & 1u) ? -u[e] : u[e];
+#pragma unroll
+          for (int hs = 1; hs < E; hs <<= 1)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if ((e & hs) == 0) {
+                const float a0 = u[e], a1 = u[e + hs];
+                u[e] = a0 + a1;
+                u[e + hs] = a0 - a1;
+              }
+          sfor<6>([&](auto MI) {
+            constexpr int m = 1 << MI;
+            const bool upper = (lane & m) != 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float p = xor_lane_f32<m>(u[e]);
+              u[e] = upper ? (p - u[e]) : (u[e] + p);
+            }
+          });
+#pragma unroll
+          for (int e = 0; e < E; ++e) wq[4 * NHG * D + h * D + E * lane + e] = u[e] * pa.uscale;
+        }
       }
     }
+    // this wavefront's table rows and queries are written: count it
+    wait_lgkmcnt0();
+    if (lane == 0) __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  lds_barrier();  // tables, rotated queries and gate flags ready
+  // every wavefront: wait until all workers have written their part (a
+  // bounded wait: a wavefront that gives up computes with what is there)
+  {
+    const uint32_t ra_addr = lds_addr(ready);
+    for (int i = 0; i < kGateSpins && flag_read(ra_addr) < kWorkers; ++i) __builtin_amdgcn_s_sleep(1);
+  }
+  if (!kSplitRoles && wave < kGateDepth && tile0 < t_host) load_tile(tile0, t_host - 1, ra);
 
-  // broadcast layout: lane 4c + v of VGPR Q[hg][m] holds q^[4 hg + v][16 m + c]
-  float Q[NHG][D / 16];
+  // the device length: a workgroup whose range starts past it has nothing
+  // to do (its early rows, if requested, are drained first)
+  const int len = min(lengths[b], max_len);  // never read past the host bound
+  if (t_begin >= len) {
+    wait_vmcnt<0>();
+    return;  // whole workgroup
+  }
+  const int t_end = min(len, t_host);
+
+  // one power-of-two scale for the workgroup's queries
+  float qm = 0.f;
+  for (int h = 0; h < GV; ++h) qm = fmaxf(qm, qmax[h]);
+  const int sq = hl_exponent(qm);
+  const float qs2 = exp2i(sq);
+  // score units: undo the query and key-table scales
+  const float kunscale = exp2i(-sq) * (C::KRAW ? 1.f : 1.f / tabs.k_scale);
+
+  // query operands in the broadcast layout. Coded keys: lane 4c + v of
+  // QH[hg][m] holds (qh_j, qh_j, qh_j', qh_j') and of QL[hg][m] (ql_j, 0,
+  // ql_j', 0) for virtual head 4 hg + v and coordinates j = 32 m + 2c,
+  // j' = j + 1. Raw keys: lane 4c + v holds coordinates 64 m + 4c .. + 3.
+  v4h QH[NHG][C::QREG], QL[NHG][C::QREG];
   float U[C::PROD ? NHG : 1][C::PROD ? D / 16 : 1];  // Prod keys: sketch projections
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 4 * hg + (lane & 3);
+    const int c = lane >> 2;
 #pragma unroll
-    for (int m = 0; m < D / 16; ++m) Q[hg][m] = h < GV ? wq[h * D + 16 * m + (lane >> 2)] : 0.f;
+    for (int m = 0; m < C::QREG; ++m) {
+      if constexpr (C::KRAW) {
+        const float4 x = h < GV ? *(const float4*)(wq + h * D + 64 * m + 4 * c)
+                                : float4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t a0 = split_hl(x.x * qs2), a1 = split_hl(x.y * qs2);
+        const uint32_t a2 = split_hl(x.z * qs2), a3 = split_hl(x.w * qs2);
+        QH[hg][m] = as_v4h(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                           __builtin_amdgcn_perm(a3, a2, 0x05040100u));
+        QL[hg][m] = as_v4h(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                           __builtin_amdgcn_perm(a3, a2, 0x07060302u));
+      } else {
+        const float2 x = h < GV ? *(const float2*)(wq + h * D + 32 * m + 2 * c) : float2{0.f, 0.f};
+        const uint32_t a0 = split_hl(x.x * qs2), a1 = split_hl(x.y * qs2);
+        QH[hg][m] = as_v4h(__builtin_amdgcn_perm(a0, a0, 0x01000100u),
+                           __builtin_amdgcn_perm(a1, a1, 0x01000100u));
+        QL[hg][m] = as_v4h(a0 >> 16, a1 >> 16);
+      }
+    }
     if constexpr (C::PROD) {
+      const int hh = 4 * hg + (lane & 3);
 #pragma unroll
       for (int m = 0; m < D / 16; ++m)
-        U[hg][m] = h < GV ? wq[4 * NHG * D + h * D + 16 * m + (lane >> 2)] : 0.f;
+        U[hg][m] = hh < GV ? wq[4 * NHG * D + hh * D + 16 * m + (lane >> 2)] : 0.f;
     }
   }
 
+  // a wavefront past the range end (short ranges) has no tile: it requests
+  // nothing more and waits for no gate (the later ones have none either)
+  const bool has_tile = tile0 < t_end;
   // The gated wavefronts request their first tile once the first tile of
   // wavefront w - kGateDepth has arrived. No workgroup barrier follows until
   // the merge: a wavefront may stall in issuing vector loads while the memory
@@ -565,7 +732,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   if (wave >= kGateDepth && has_tile) {
     const uint32_t ga = lds_addr(gate + (wave - kGateDepth));
     for (int i = 0; i < kGateSpins && flag_read(ga) == 0; ++i) __builtin_amdgcn_s_sleep(1);
-    load_tile(tile0, ra);
+    load_tile(tile0, t_end - 1, ra);
   }
   // this wavefront's first tile has arrived: open the gate of wavefront w + kGateDepth
   wait_vmcnt<0>();
@@ -578,18 +745,22 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
     for (int v = 0; v < 4; ++v) vlim[hg][v] = min(t_end, len - n_qtok + (4 * hg + v) / G + 1);
 
-  // ---- per-wave online-softmax state
+  // ---- per-wave online-softmax state. acc[0] collects the products with
+  //      the weights' high halves, acc[1] with their low halves.
   float m_run[NHG][4];
   v4f l_run[NHG];
-  v4f acc[C::NACC][NHG];
+  v4f acc[2][C::NACC][NHG];
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     l_run[hg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 4; ++v) m_run[hg][v] = kNoRow;
 #pragma unroll
-    for (int a = 0; a < C::NACC; ++a) acc[a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < C::NACC; ++a) acc[0][a][hg] = acc[1][a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  // every V norm seen so far is below 2^ev (ev only grows)
+  int ev = 0;
+  bool seen = false;  // a tile has been processed (the accumulators may be nonzero)
 
   const uint32_t koff = C::KPAIR ? (uint32_t)(lane & 31) << 3 : (uint32_t)lane << 2;
   const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 31) << 3 : (uint32_t)lane << 2;
@@ -597,87 +768,98 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   constexpr uint32_t VMASK = ((1u << C::VF) - 1u) << 8;
 
   // V fields of this lane: field 64k + lane of each staged row, read from bit
-  // o - 8 of the padded row so the field lands at bit 8
-  int vdw[C::NVS], vsh[C::NVS];
+  // o - 8 of the padded row so the field lands at bit 8. The two dwords
+  // around it are read through separate base addresses the compiler cannot
+  // relate (so it neither merges the reads into one register pair nor needs
+  // an address add per row: every row is a constant offset from them), and
+  // so are the two dwords of a V pair entry, each of which feeds its own
+  // product.
+  uint32_t va0[C::NVS], va1[C::NVS];
+  int vsh[C::NVS];
 #pragma unroll
   for (int k = 0; k < C::NVS; ++k) {
-    const int o = C::VF * (64 * k + lane) + 64 - 8;
-    vdw[k] = o >> 5;
+    const int o = C::VF * (64 * k + lane) + 32 * kVPad - 8;
+    va0[k] = lds_addr(vstage) + 4 * (o >> 5);
+    va1[k] = va0[k] + 4;
+    asm("" : "+v"(va1[k]));
     vsh[k] = o & 31;
   }
+  uint32_t voff_y = voff + 4, vmask_y = VMASK;  // opaque copies: one v_and_or per address
+  asm("" : "+v"(voff_y));
+  asm("" : "+s"(vmask_y));
 
   // One tile: scores, online softmax, values. `r` is consumed and refilled
   // with the wavefront's next tile as soon as its rows have been used.
   auto process = [&](int tile, TileRegs<C>& r) __attribute__((always_inline)) {
 
-    // stage this token's V row (row `lane`, after 2 dwords of padding)
-#pragma unroll
-    for (int i = 0; i < RVW; i += 2)
-      *(uint2*)(vstage + 2 + lane * RVW + i) = uint2{r.vw[i], r.vw[i + 1]};
-
-    // ---- scores on the matrix cores. The lookups of batch j + 1 are issued
-    //      before the products of batch j, so a batch's LDS latency hides
-    //      behind the previous batch's MFMAs; four accumulator chains.
-    using KLut = std::conditional_t<C::KPAIR, v2f, float>;
+    // ---- scores on the matrix cores: per coordinate pair (raw keys: per
+    //      four coordinates) one product with the high and one with the low
+    //      halves of the queries, into four accumulator chains. The lookups
+    //      of batch j + 1 are issued before the products of batch j, so a
+    //      batch's LDS latency hides behind the previous batch's products.
     v4f sc[4][NHG];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
       for (int hg = 0; hg < NHG; ++hg) sc[a4][hg] = v4f{0.f, 0.f, 0.f, 0.f};
-    auto k_lookup = [&](auto BI, KLut (&dst)[kKBatch]) __attribute__((always_inline)) {
-      sfor<kKBatch>([&](auto II) {
-        constexpr int f = BI * kKBatch + II;
-        constexpr int bit = C::KF * f;
-        uint32_t addr;
-        if constexpr (C::KRAW) {
-          // coordinate f of the raw key row: half f % 2 of dword f / 2
-          dst[II] = __half2float(__builtin_bit_cast(__half, (uint16_t)(r.kw[f >> 1] >> (16 * (f & 1)))));
-          return;
-        } else if constexpr (C::KF == 8) {
-          // whole byte: one byte permute builds (code << 8) | koff
-          addr = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
-                                       0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
-        } else {
-          addr = (field_at8<bit, C::KF>(r.kw) & KMASK) | koff;
+    if constexpr (C::KRAW) {
+      // coordinates 4f .. 4f + 3 of the raw key row are dwords 2f, 2f + 1
+      sfor<D / 4>([&](auto FI) {
+        constexpr int f = FI;
+        const v4h kb = as_v4h(r.kw[2 * f], r.kw[2 * f + 1]);
+#pragma unroll
+        for (int hg = 0; hg < NHG; ++hg) {
+          sc[2 * (f % 2)][hg] = mfma16<f % 16>(QH[hg][f / 16], kb, sc[2 * (f % 2)][hg]);
+          sc[2 * (f % 2) + 1][hg] = mfma16<f % 16>(QL[hg][f / 16], kb, sc[2 * (f % 2) + 1][hg]);
         }
-        dst[II] = *(const KLut*)(kt + addr);
       });
-    };
-    auto k_mfma = [&](auto BI, const KLut (&src)[kKBatch]) __attribute__((always_inline)) {
-      sfor<kKBatch>([&](auto II) {
-        constexpr int f = BI * kKBatch + II;
+    } else {
+      constexpr int NKP = D / 2;  // coordinate pairs
+      // rolling pipeline: the lookups of pair p + kKAhead are issued before
+      // the products of pair p, so up to 2 kKAhead lookups are in flight
+      u2v kl[kKAhead + 1];
+      auto k_lookup = [&](auto PI) __attribute__((always_inline)) {
+        constexpr int p = PI;
+        u2v& dst = kl[p % (kKAhead + 1)];
         if constexpr (C::KPAIR) {
-          constexpr int j0 = 2 * f, j1 = 2 * f + 1, a0 = 2 * (f % 2);
-#pragma unroll
-          for (int hg = 0; hg < NHG; ++hg) {
-            sc[a0][hg] = mfma_bcast<j0 % 16>(Q[hg][j0 / 16], src[II].x, sc[a0][hg]);
-            sc[a0 + 1][hg] = mfma_bcast<j1 % 16>(Q[hg][j1 / 16], src[II].y, sc[a0 + 1][hg]);
-          }
+          const uint32_t addr = (field_at8<C::KF * p, C::KF>(r.kw) & KMASK) | koff;
+          dst = u2v{*(const uint32_t*)(kt + addr), *(const uint32_t*)(kt + addr + 4)};
         } else {
+          uint32_t a2[2];
+          sfor<2>([&](auto SI) {
+            constexpr int j = 2 * p + SI;
+            constexpr int bit = C::KF * j;
+            if constexpr (C::KF == 8) {
+              // whole byte: one byte permute builds (code << 8) | koff
+              a2[SI] = __builtin_amdgcn_perm(r.kw[bit >> 5], koff,
+                                             0x0C0C0000u | ((4u + ((bit >> 3) & 3)) << 8));
+            } else {
+              a2[SI] = (field_at8<bit, C::KF>(r.kw) & KMASK) | koff;
+            }
+          });
+          dst = u2v{*(const uint32_t*)(kt + a2[0]), *(const uint32_t*)(kt + a2[1])};
+        }
+      };
+      auto k_mfma = [&](auto PI) __attribute__((always_inline)) {
+        constexpr int p = PI;
+        const u2v& src = kl[p % (kKAhead + 1)];
+        const v4h kb = as_v4h(src.x, src.y);
 #pragma unroll
-          for (int hg = 0; hg < NHG; ++hg)
-            sc[f % 4][hg] = mfma_bcast<f % 16>(Q[hg][f / 16], src[II], sc[f % 4][hg]);
+        for (int hg = 0; hg < NHG; ++hg) {
+          sc[2 * (p % 2)][hg] = mfma16<p % 16>(QH[hg][p / 16], kb, sc[2 * (p % 2)][hg]);
+          sc[2 * (p % 2) + 1][hg] = mfma16<p % 16>(QL[hg][p / 16], kb, sc[2 * (p % 2) + 1][hg]);
         }
-      });
-    };
-    {
-      constexpr int NKB = C::NKL / kKBatch;
-      KLut lb0[kKBatch], lb1[kKBatch];
-      k_lookup(std::integral_constant<int, 0>{}, lb0);
-      sfor<NKB>([&](auto BI) {
-        constexpr int bb = BI;
-        if constexpr (bb % 2 == 0) {
-          if constexpr (bb + 1 < NKB) k_lookup(std::integral_constant<int, bb + 1>{}, lb1);
-          k_mfma(BI, lb0);
-        } else {
-          if constexpr (bb + 1 < NKB) k_lookup(std::integral_constant<int, bb + 1>{}, lb0);
-          k_mfma(BI, lb1);
-        }
+      };
+      sfor<NKP + kKAhead>([&](auto I) {
+        constexpr int i = I;
+        if constexpr (i < NKP) k_lookup(std::integral_constant<int, i>{});
+        if constexpr (i >= kKAhead) k_mfma(std::integral_constant<int, i - kKAhead>{});
       });
     }
     v4f s0[NHG];
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) s0[hg] = (sc[0][hg] + sc[1][hg]) + (sc[2][hg] + sc[3][hg]);
+    for (int hg = 0; hg < NHG; ++hg)
+      s0[hg] = ((sc[0][hg] + sc[1][hg]) + (sc[2][hg] + sc[3][hg])) * kunscale;
     if constexpr (C::PROD) {
       // QJL correction: residual norm x sum_j sgn_j u^_j, sgn_j = -1 for a set
       // sketch bit (the bit becomes the sign of 1.0 as the MFMA operand)
@@ -699,17 +881,40 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         s0[hg] += r.rn * ((kc4[0][hg] + kc4[1][hg]) + (kc4[2][hg] + kc4[3][hg]));
     }
 
-    const float nv_cur = r.nv;
+    // a lane past the range end holds a repeated (or, for a first tile
+    // requested before the length was known, an unused) row: weight 0
+    const bool live = tile + lane < t_end;
+    const float nv_cur = live ? r.nv : 0.f;
     const float nk_cur = r.nk;
-    // the rows are consumed: refill with this wavefront's next tile
+    // the K row is consumed: refill the registers with this wavefront's next
+    // tile (its V rows follow once this tile's stage has been read)
     const int ahead = tile + kStride;
-    if (ahead < t_end) load_tile(ahead, r);
+    const bool more = ahead < t_end;
+    if (more) load_k(ahead, t_end - 1, r);
+
+    // V norm scale: every norm below 2^ev (rare: usually the first tile only)
+    if (__ballot(__builtin_bit_cast(int, nv_cur) >= ((ev + 127) << 23)) != 0ull) {
+      const int mx = wave_max_int(__builtin_bit_cast(int, nv_cur));
+      const int en = min(120, ((mx >> 23) & 0xFF) - 127 + 1);
+      if (seen) {  // before the first tile the accumulators are zero
+        const float f = exp2i(max(-126, ev - en));
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+          for (int a = 0; a < C::NACC; ++a)
+#pragma unroll
+            for (int hg = 0; hg < NHG; ++hg) acc[hl][a][hg] *= f;
+      }
+      ev = en;
+    }
+    seen = true;
+    const float wmul = nv_cur * exp2i(kWeightExp - ev);
 
     // ---- online softmax (base 2) with a lazily moved maximum
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
       const v4f s = s0[hg] * nk_cur;
-      v4f w;
+      uint32_t w[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float sv = tile + lane < vlim[hg][v] ? s[v] : -INFINITY;
@@ -718,74 +923,114 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         // taken then (always on a wavefront's first tile, rarely after)
         if (__ballot(sv > m_run[hg][v] + kRescaleSlack) != 0ull) {  // wavefront-uniform
           const float mt = wave_max_key(sv);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
-          l_run[hg][v] *= alpha;
+          // a head that has seen no row yet has zero sums: nothing to rescale
+          if (m_run[hg][v] != kNoRow) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
+            l_run[hg][v] *= alpha;
 #pragma unroll
-          for (int a = 0; a < C::NACC; ++a) acc[a][hg][v] *= alpha;
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+              for (int a = 0; a < C::NACC; ++a) acc[hl][a][hg][v] *= alpha;
+          }
           m_run[hg][v] = mt;
         }
         const float p = __builtin_amdgcn_exp2f(sv - m_run[hg][v]);
         l_run[hg][v] += p;
-        w[v] = p * nv_cur;
+        w[v] = split_hl(p * wmul);
       }
-      *(v4f*)(wbuf + (lane * NHG + hg) * 4) = w;
+      *(uint4*)(wbuf + (lane * NHG + hg) * 4) = uint4{w[0], w[1], w[2], w[3]};
     }
     wave_lds_sync();
 
-    // weights in the broadcast layout: lane 4c + v of Wr[hg][m] holds w[4 hg + v][16 m + c]
-    float Wr[NHG][4];
+    // this tile's V rows are in the stage: they were requested before its K
+    // row, whose loads have completed (only the refill may be in flight)
+    if (more)
+      wait_vmcnt<k_loads<C>()>();
+    else
+      wait_vmcnt<0>();
+
+    // weights in the broadcast layout: lane 4c + v of WH[hg][m] holds
+    // (wh_t, wh_t, wh_t', wh_t') and of WL[hg][m] (wl_t, 0, wl_t', 0) for
+    // virtual head 4 hg + v and tokens t = 2 (16 m + c), t' = t + 1
+    v4h WH[NHG][2], WL[NHG][2];
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg)
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        Wr[hg][m] = wbuf[((16 * m + (lane >> 2)) * NHG + hg) * 4 + (lane & 3)];
+      for (int m = 0; m < 2; ++m) {
+        const int t0 = 2 * (16 * m + (lane >> 2));
+        const uint32_t x0 = wbuf[(t0 * NHG + hg) * 4 + (lane & 3)];
+        const uint32_t x1 = wbuf[((t0 + 1) * NHG + hg) * 4 + (lane & 3)];
+        WH[hg][m] = as_v4h(__builtin_amdgcn_perm(x0, x0, 0x01000100u),
+                           __builtin_amdgcn_perm(x1, x1, 0x01000100u));
+        WL[hg][m] = as_v4h(x0 >> 16, x1 >> 16);
+      }
 
-    // ---- values on the matrix cores, lanes over coordinates. Three stages
-    //      over batches of tokens: the staged dwords around this lane's
-    //      fields (two batches ahead), the centroid lookups (one batch
-    //      ahead), the products.
-    using VLut = std::conditional_t<C::VPAIR, v2f, float>;
-    constexpr int TB = kVBatch, NTB = kTile / TB;
-    auto v_stage = [&](auto JI, uint2 (&dst)[TB][C::NVS]) __attribute__((always_inline)) {
+    // ---- values on the matrix cores, lanes over coordinates, two tokens
+    //      per product. Three stages over batches of token pairs: the staged
+    //      dwords around this lane's fields (two batches ahead), the centroid
+    //      entries (one batch ahead), the products.
+    // a pair entry is read as its two dwords (x: the first coordinate's
+    // (hi, lo), y: the second's), each straight into the operand it feeds
+    using VLut = std::conditional_t<C::VPAIR, u2v, uint32_t>;
+    constexpr int TB = kVBatch, NTB = kTile / 2 / TB;
+    auto v_stage = [&](auto JI, u2v (&dst)[TB][2][C::NVS]) __attribute__((always_inline)) {
       sfor<TB>([&](auto TI) {
-        constexpr int t = JI * TB + TI;
-        const uint32_t* row = vstage + t * RVW;
+        sfor<2>([&](auto SI) {
+          constexpr int t = 2 * (JI * TB + TI) + SI;
 #pragma unroll
-        for (int k = 0; k < C::NVS; ++k) dst[TI][k] = uint2{row[vdw[k]], row[vdw[k] + 1]};
+          for (int k = 0; k < C::NVS; ++k)
+            dst[TI][SI][k] = u2v{*(const lds_u32*)(uintptr_t)(va0[k] + 4 * t * RVW),
+                                 *(const lds_u32*)(uintptr_t)(va1[k] + 4 * t * RVW)};
+        });
       });
     };
-    auto v_lookup = [&](const uint2 (&xs)[TB][C::NVS], VLut (&dst)[TB][C::NVS]) __attribute__((always_inline)) {
+    auto v_lookup = [&](const u2v (&xs)[TB][2][C::NVS], VLut (&dst)[TB][2][C::NVS])
+                        __attribute__((always_inline)) {
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt)
 #pragma unroll
-        for (int k = 0; k < C::NVS; ++k) {
-          const uint32_t x = __builtin_amdgcn_alignbit(xs[tt][k].y, xs[tt][k].x, vsh[k]);
-          dst[tt][k] = *(const VLut*)(vt + ((x & VMASK) | voff));
-        }
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int k = 0; k < C::NVS; ++k) {
+            const uint32_t x = __builtin_amdgcn_alignbit(xs[tt][s][k].y, xs[tt][s][k].x, vsh[k]);
+            const uint32_t a = (x & VMASK) | voff;
+            if constexpr (C::VPAIR)
+              dst[tt][s][k] = u2v{*(const uint32_t*)(vt + a),
+                                  *(const uint32_t*)(vt + ((x & vmask_y) | voff_y))};
+            else
+              dst[tt][s][k] = *(const uint32_t*)(vt + a);
+          }
     };
-    auto v_mfma = [&](auto JI, const VLut (&cs)[TB][C::NVS]) __attribute__((always_inline)) {
+    auto v_mfma = [&](auto JI, const VLut (&cs)[TB][2][C::NVS]) __attribute__((always_inline)) {
       sfor<TB>([&](auto TI) {
-        constexpr int t = JI * TB + TI;
+        constexpr int tp = JI * TB + TI;  // token pair
 #pragma unroll
         for (int k = 0; k < C::NVS; ++k) {
           if constexpr (C::VPAIR) {
+            const v4h b0 = as_v4h(cs[TI][0][k].x, cs[TI][1][k].x);
+            const v4h b1 = as_v4h(cs[TI][0][k].y, cs[TI][1][k].y);
 #pragma unroll
             for (int hg = 0; hg < NHG; ++hg) {
-              acc[2 * k][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], cs[TI][k].x, acc[2 * k][hg]);
-              acc[2 * k + 1][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], cs[TI][k].y, acc[2 * k + 1][hg]);
+              acc[0][2 * k][hg] = mfma16<tp % 16>(WH[hg][tp / 16], b0, acc[0][2 * k][hg]);
+              acc[1][2 * k][hg] = mfma16<tp % 16>(WL[hg][tp / 16], b0, acc[1][2 * k][hg]);
+              acc[0][2 * k + 1][hg] = mfma16<tp % 16>(WH[hg][tp / 16], b1, acc[0][2 * k + 1][hg]);
+              acc[1][2 * k + 1][hg] = mfma16<tp % 16>(WL[hg][tp / 16], b1, acc[1][2 * k + 1][hg]);
             }
           } else {
-            constexpr int par = (C::NVS == 1) ? (t & 1) : 0;
+            constexpr int par = (C::NVS == 1) ? (tp & 1) : 0;
+            const v4h bv = as_v4h(cs[TI][0][k], cs[TI][1][k]);
 #pragma unroll
-            for (int hg = 0; hg < NHG; ++hg)
-              acc[k + par][hg] = mfma_bcast<t % 16>(Wr[hg][t / 16], cs[TI][k], acc[k + par][hg]);
+            for (int hg = 0; hg < NHG; ++hg) {
+              acc[0][k + par][hg] = mfma16<tp % 16>(WH[hg][tp / 16], bv, acc[0][k + par][hg]);
+              acc[1][k + par][hg] = mfma16<tp % 16>(WL[hg][tp / 16], bv, acc[1][k + par][hg]);
+            }
           }
         }
       });
     };
     {
-      uint2 xs0[TB][C::NVS], xs1[TB][C::NVS], xs2[TB][C::NVS];
-      VLut cv0[TB][C::NVS], cv1[TB][C::NVS];
+      u2v xs0[TB][2][C::NVS], xs1[TB][2][C::NVS], xs2[TB][2][C::NVS];
+      VLut cv0[TB][2][C::NVS], cv1[TB][2][C::NVS];
       v_stage(std::integral_constant<int, 0>{}, xs0);
       v_stage(std::integral_constant<int, 1>{}, xs1);
       v_lookup(xs0, cv0);
@@ -803,6 +1048,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       });
     }
     wave_lds_sync();
+    if (more) {
+      // every read of the stage has returned before it is overwritten
+      wait_lgkmcnt0();
+      load_v(ahead, t_end - 1);
+    }
   };
 
   // the first tile is peeled off the loop so that its register waits follow
@@ -811,13 +1061,20 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   for (int tile = tile0 + kStride; tile < t_end; tile += kStride) process(tile, ra);
 
   // ---- merge the wavefronts of this workgroup and write the split partial:
-  //      every wavefront stores its maxima, sums and unscaled accumulators,
-  //      then thread (virtual head, coordinate) folds the wavefronts with the
-  //      factors 2^(m_w - M), M their maximum (a wavefront that saw no row
-  //      has the finite sentinel maximum, so it weighs 0 next to one that did)
+  //      every wavefront stores its maxima, sums and accumulators (brought to
+  //      true scale), then thread (virtual head, coordinate) folds the
+  //      wavefronts with the factors 2^(m_w - M), M their maximum (a
+  //      wavefront that saw no row has the finite sentinel maximum, so it
+  //      weighs 0 next to one that did)
+  const float aunscale = exp2i(ev - kWeightExp) / tabs.v_scale;
+  v4f accf[C::NACC][NHG];
+#pragma unroll
+  for (int a = 0; a < C::NACC; ++a)
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) accf[a][hg] = (acc[0][a][hg] + acc[1][a][hg]) * aunscale;
   if constexpr (C::NVS == 1 && !C::VPAIR) {
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) acc[0][hg] += acc[1][hg];
+    for (int hg = 0; hg < NHG; ++hg) accf[0][hg] += accf[1][hg];
   }
   __syncthreads();  // all wavefronts are done with tables and buffers
   constexpr int NV = 4 * NHG;                   // virtual-head slots per wavefront
@@ -837,12 +1094,12 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       if constexpr (C::VPAIR) {
 #pragma unroll
         for (int k = 0; k < C::NVS; ++k) {
-          dst[2 * (64 * k + lane)] = acc[2 * k][hg][v];
-          dst[2 * (64 * k + lane) + 1] = acc[2 * k + 1][hg][v];
+          dst[2 * (64 * k + lane)] = accf[2 * k][hg][v];
+          dst[2 * (64 * k + lane) + 1] = accf[2 * k + 1][hg][v];
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = acc[k][hg][v];
+        for (int k = 0; k < C::NVS; ++k) dst[64 * k + lane] = accf[k][hg][v];
       }
     }
   __syncthreads();
@@ -1156,6 +1413,16 @@ const SplitEntry* find_split(int d, int bk, int bv, int group) {
   return best;
 }
 
+// 2^e with max |c| * 2^e in [2^13, 2^14) (1 for an all-zero table).
+float table_scale(const float* c, int n) {
+  float m = 0.f;
+  for (int i = 0; i < n; ++i) m = std::fmax(m, std::fabs(c[i]));
+  if (!(m > 0.f) || !std::isfinite(m)) return 1.f;
+  int e;
+  std::frexp(m, &e);  // m = f * 2^e, f in [0.5, 1): m in [2^(e-1), 2^e)
+  return std::ldexp(1.f, 14 - e);
+}
+
 }  // namespace
 
 AttendPlan plan_attend(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
@@ -1209,8 +1476,14 @@ hipError_t launch_attend(int dim, int k_bits, int v_bits, int batch, int n_qtok,
   pa.uscale = qscale * 1.2533141373155003f / (float)dim;  // sqrt(pi/2) / d
   const SplitFn fn =
       ent->short_fn && plan.tokens_per_split <= kShortTiles * kTile ? ent->short_fn : ent->fn;
+  // codebook scales: powers of two taking each table's largest magnitude
+  // into [2^13, 2^14), so both fp16 halves of every entry are normal numbers
+  AttendTables t2 = tabs;
+  const int kb = k_bits >= 32 ? k_bits - 32 : k_bits;
+  t2.k_scale = k_bits == 16 ? 1.f : table_scale(tabs.k_centroids, 1 << kb);
+  t2.v_scale = table_scale(tabs.v_centroids, 1 << v_bits);
   err = fn(plan, batch, n_kv_heads, group, n_qtok, q, k_codes, k_norms, v_codes, v_norms, lengths,
-           max_ctx, max_len, qscale, pacc, pml, tabs, k_sign, pa, ev_before, ev_after, stream);
+           max_ctx, max_len, qscale, pacc, pml, t2, k_sign, pa, ev_before, ev_after, stream);
   if (err != hipSuccess) return err;
   if (raw.lengths && n_qtok != 1) return hipErrorInvalidValue;
   RawArgs ra;

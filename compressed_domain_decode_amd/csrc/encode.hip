@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "kernels.hpp"
+#include "xlane.hpp"
 
 namespace tq {
 
@@ -56,34 +57,6 @@ constexpr int kWavesPerBlock = 4;
 constexpr long long kNarrowMinWaves = 1024;
 // Vector indices of the last workgroup stay below 2^31.
 constexpr long long kMaxEncodeVectors = 0x7fffffffLL - 64;
-
-// Value of lane (lane ^ M) for a 32-bit word, M a power of two below 64.
-template <int M>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (M == 1) {
-    return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-  } else if constexpr (M == 2) {
-    return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-  } else if constexpr (M == 4) {
-    // banks 1, 3 (lanes 4-7, 12-15 of a row) read lane - 4; banks 0, 2 read lane + 4
-    const uint32_t r = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xA, false);
-    return __builtin_amdgcn_update_dpp(r, v, 0x104, 0xF, 0x5, false);
-  } else if constexpr (M == 8) {
-    // banks 2, 3 (lanes 8-15 of a row) read lane - 8; banks 0, 1 read lane + 8
-    const uint32_t r = __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xC, false);
-    return __builtin_amdgcn_update_dpp(r, v, 0x108, 0xF, 0x3, false);
-  } else if constexpr (M == 16) {
-    // swap odd rows of the first copy with even rows of the second
-    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane & 16) ? p[0] : p[1];
-  } else {
-    static_assert(M == 32, "lane mask");
-    // swap the upper half of the first copy with the lower half of the second
-    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane & 32) ? p[0] : p[1];
-  }
-}
 
 template <int M>
 __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {

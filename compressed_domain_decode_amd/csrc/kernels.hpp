@@ -41,6 +41,7 @@ struct EncodeArgs {
 struct AttendTables {
   float k_centroids[256];
   float v_centroids[256];
+  float k_scale = 1.f, v_scale = 1.f;  // powers of two applied to the tables on the device
 };
 
 struct AttendPlan {
