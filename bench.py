@@ -39,11 +39,16 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--replays", type=int, default=7,
+                   help="timed replays of the K-step graph (>= 5); value is their median")
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default="llama8b_32k_k8v3")
     p.add_argument("--cold-bytes", type=float, default=512e6,
                    help="total bytes of cache copies cycled through (0: one warm copy)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--configs", default="tiny_d64_k4v4,llama3b_4k_k4v2,batch16_ragged_k3v3,"
+                   "long128k_d64_k3v3",
+                   help="other workloads to time on their own (comma list; empty: none)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     p.add_argument("--copy-calibration", action="store_true",
@@ -202,59 +207,237 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Worker threads for the CPU leg: the cores this process may run on,
+    at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(wl, inp, budget_s):
-    """The oracle as it stands, single-threaded, on KV heads of the same step
-    until about budget_s seconds of timed work: pending-batch encode of K and V
-    for that head plus attention of its query heads over the whole context."""
+    """The oracle as it stands, threaded over (sequence, KV head) units of the
+    step: each unit is the pending-batch encode of its K and V rows plus the
+    attention of its query heads over the whole context. The C oracle runs
+    with the GIL released, so the units of a wave run in parallel. Waves of
+    `threads` units (cycling through the step's units) are timed until about
+    budget_s seconds of wall time have passed."""
+    import concurrent.futures as cf
     import oracle
     ok = oracle.Codec(wl.dim, wl.k_bits, wl.codec_seed)
     ov = oracle.Codec(wl.dim, wl.v_bits, wl.codec_seed)
     G = wl.group
-    T = int(inp.lengths[0])
     P = wl.pending
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)]
+    nthreads = cpu_threads()
+    pool = cf.ThreadPoolExecutor(nthreads)
+    setup = {}
+
+    def prepare(u):
+        # untimed, as the GPU's cache is resident before its clock starts
+        b, g = u
+        L = int(inp.lengths[b])
+        kc, kn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L - P])
+        vc, vn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L - P])
+        return u, (kc, kn, vc, vn)
+
+    def work(u):
+        b, g = u
+        L = int(inp.lengths[b])
+        kc, kn, vc, vn = setup[u]
+        if P:
+            pkc, pkn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, L - P:L])
+            pvc, pvn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, L - P:L])
+            kc = np.concatenate([kc, pkc], axis=2)
+            kn = np.concatenate([kn, pkn], axis=2)
+            vc = np.concatenate([vc, pvc], axis=2)
+            vn = np.concatenate([vn, pvn], axis=2)
+        oracle.attend(ok, ov, inp.q[b:b + 1, g * G:(g + 1) * G], kc, kn, vc, vn,
+                      np.array([L], np.int32))
+        return L
+
     done_bytes = 0
     done_tokens = 0
+    done_units = 0
     timed = 0.0
-    heads = 0
-    for b in range(wl.batch):
-        for g in range(wl.n_kv_heads):
-            L = int(inp.lengths[b])
-            # setup (untimed, as the GPU's cache is resident before its clock starts)
-            kc, kn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L - P])
-            vc, vn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L - P])
-            t0 = time.perf_counter()
-            if P:
-                pkc, pkn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, L - P:L])
-                pvc, pvn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, L - P:L])
-                kc = np.concatenate([kc, pkc], axis=2)
-                kn = np.concatenate([kn, pkn], axis=2)
-                vc = np.concatenate([vc, pvc], axis=2)
-                vn = np.concatenate([vn, pvn], axis=2)
-            oracle.attend(ok, ov, inp.q[b:b + 1, g * G:(g + 1) * G], kc, kn, vc, vn,
-                          np.array([L], np.int32))
-            timed += time.perf_counter() - t0
-            heads += 1
+    nxt = 0
+    while timed < budget_s:
+        wave = [units[(nxt + i) % len(units)] for i in range(nthreads)]
+        nxt += nthreads
+        missing = [u for u in dict.fromkeys(wave) if u not in setup]
+        for u, val in pool.map(prepare, missing):
+            setup[u] = val
+        t0 = time.perf_counter()
+        lens = list(pool.map(work, wave))
+        timed += time.perf_counter() - t0
+        for L in lens:
+            done_units += 1
             done_tokens += L
             done_bytes += L * ((wl.dim * wl.k_bits // 8 + 4) + (wl.dim * wl.v_bits // 8 + 4))
-            if timed >= budget_s:
-                break
-        if timed >= budget_s:
-            break
+    pool.shutdown()
     return {
         "value": done_bytes / timed / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": nthreads,
         "kind": "oracle",
-        "sample": f"{heads} of {wl.batch * wl.n_kv_heads} (sequence, KV head) units of the step "
-                  f"({heads * G} query heads, {done_tokens} cached tokens, "
-                  f"{P}-token pending encode each); {timed:.2f} s timed, fp64 C oracle, 1 thread",
+        "cpu_model": cpu_model(),
+        "sample": f"{done_units} (sequence, KV head) units of the step in waves of {nthreads} "
+                  f"(the step has {len(units)}, cycled; {G} query heads, {P}-token pending "
+                  f"encode each; {done_tokens} cached tokens attended); {timed:.2f} s timed, "
+                  f"fp64 C oracle, {nthreads} threads",
         "ctx_tokens_per_s": done_tokens / timed,
         "seconds": timed,
     }
 
 
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
+FP16_MATRIX_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix
+
+
+def replay_stats(fn, ncalls, min_calls, replays):
+    """Per-call microseconds of fn(i) (i cycling over ncalls cold copies) from
+    `replays` timed replays of one graph holding a whole number of cycles and
+    at least min_calls calls: (median, min, max, calls per replay)."""
+    import torch
+    n = ncalls * max(1, math.ceil(min_calls / ncalls))
+    for i in range(ncalls):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    us = []
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g
+    return float(np.median(us)), min(us), max(us), n
+
+
+def config_line(name, args, hip):
+    """The decode attend of one more workload on its own: split-kernel time
+    (HIP events bound to its dispatch, median of >= 100 launches queued behind
+    graph replays), whole-attend time (graph replay, median of the replays) and
+    the rates they give, over cold copies of the packed cache."""
+    import torch
+    import workloads
+    import compressed_domain_decode_amd as tq
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.generate(wl)
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.dim
+    T = inp.k.shape[2]
+    lengths_np = inp.lengths
+    max_len = int(lengths_np.max())
+    kc = tq.tq_codec_init(d, wl.k_bits, wl.codec_seed)
+    vc = tq.tq_codec_init(d, wl.v_bits, wl.codec_seed)
+    kr, vr = kc.row_bytes, vc.row_bytes
+    footprint = B * Hkv * T * (kr + vr + 8)
+    ncopies = 1 if args.cold_bytes <= 0 else max(2, math.ceil(args.cold_bytes / footprint))
+    k_dev = torch.from_numpy(inp.k).to(dev)
+    v_dev = torch.from_numpy(inp.v).to(dev)
+    q_dev = torch.from_numpy(inp.q).to(dev)
+    lengths = torch.from_numpy(lengths_np).to(dev)
+    tmaj = lambda a, *row: a.view(B * Hkv, T, *row).permute(1, 0, *range(2, 2 + len(row)))
+    copies = []
+    for _ in range(ncopies):
+        c = (torch.empty((B, Hkv, T, kr), dtype=torch.uint8, device=dev),
+             torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+             torch.empty((B, Hkv, T, vr), dtype=torch.uint8, device=dev),
+             torch.empty((B, Hkv, T), dtype=torch.float32, device=dev))
+        tq.tq_encode(kc, tmaj(k_dev, d), tmaj(c[0], kr), tmaj(c[1]))
+        tq.tq_encode(vc, tmaj(v_dev, d), tmaj(c[2], vr), tmaj(c[3]))
+        copies.append(c)
+    del k_dev, v_dev
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_attend_workspace_bytes(B, Hq, Hkv, d, max_len), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+
+    def attend(i):
+        c = copies[i % ncopies]
+        tq.tq_decode_attend(kc, vc, q_dev, c[0], c[1], c[2], c[3], lengths, max_len, scale,
+                            out, ws)
+
+    att_med, att_min, att_max, calls = replay_stats(attend, ncopies, 100, args.replays)
+    # split kernel alone: events bound to its dispatch, launches queued behind
+    # replays of the same calls so they run back to back
+    n_ev = 100
+    evs = [(hip.event(), hip.event()) for _ in range(n_ev)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(ncopies):
+            attend(i)
+    for _ in range(max(1, math.ceil(4 * n_ev / ncopies))):
+        g.replay()
+    for i in range(n_ev):
+        tq.tq_set_split_events(evs[i][0], evs[i][1])
+        attend(i)
+    tq.tq_set_split_events(None, None)
+    torch.cuda.synchronize()
+    split = [hip.elapsed_ms(a, b) * 1e3 for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    split_med = float(np.median(split))
+    alg = workloads.algorithmic_bytes(lengths_np, Hkv, d, wl.k_bits, wl.v_bits)
+    # multiply-adds a dense evaluation needs: G d for the scores and G d for
+    # the weighted V sum, per cached token and KV head
+    flops = 4 * (Hq // Hkv) * d * int(lengths_np.sum()) * Hkv
+    line = {
+        "workload": wl.name,
+        "shape": f"{B} x {Hq}/{Hkv} heads, head dim {d}, K{wl.k_bits}/V{wl.v_bits}, "
+                 + (f"ragged lengths {int(lengths_np.min())}..{max_len}" if wl.ragged
+                    else f"{max_len} tokens"),
+        "algorithmic_bytes": alg, "cold_copies": ncopies,
+        "splits": tq.tq_attend_num_splits(B, Hq, Hkv, d, max_len),
+        "split_us_median": round(split_med, 3), "split_us_min": round(min(split), 3),
+        "split_us_max": round(max(split), 3), "split_launches": n_ev,
+        "attend_us_median": round(att_med, 3), "attend_us_min": round(att_min, 3),
+        "attend_us_max": round(att_max, 3), "attend_calls_per_replay": calls,
+        "attend_replays": args.replays,
+        "split_GBps": round(alg / (split_med * 1e-6) / 1e9, 2),
+        "split_frac_of_hbm_peak": round(alg / (split_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "attend_GBps": round(alg / (att_med * 1e-6) / 1e9, 2),
+        "attend_frac_of_hbm_peak": round(alg / (att_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "split_alg_TFLOPs": round(flops / (split_med * 1e-6) / 1e12, 2),
+        "split_frac_of_fp32_peak": round(flops / (split_med * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
+        "split_frac_of_fp16_matrix_peak":
+            round(flops / (split_med * 1e-6) / 1e12 / FP16_MATRIX_PEAK_TFLOPS, 5),
+    }
+    del copies, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return line
+
+
 def main():
     args = parse()
+    if args.replays < 5 or args.steps < 1:
+        print("need --replays >= 5 and --steps >= 1", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_mb, max(10, min(args.steps, 200)))
         return
@@ -327,13 +510,15 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- whole-step timing: K steps captured in a graph (one launch per step set)
+    # ---- whole-step timing: exactly K steps (cycling the cold copies) captured
+    #      in one graph, replayed REPLAYS times; each replay is one timed sample
+    K = args.steps
     graph = None
     if not args.no_graph:
         try:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for i in range(ncopies):
+                for i in range(K):
                     step(i)
             graph = g
         except Exception as e:  # capture unsupported: fall back to eager launches
@@ -349,7 +534,7 @@ def main():
     n_ev = max(args.steps, 20)
     evs = [(hip.event(), hip.event()) for _ in range(n_ev)]
     if graph is not None:
-        for _ in range(4 * math.ceil(n_ev / ncopies)):
+        for _ in range(max(1, math.ceil(4 * n_ev / K))):
             graph.replay()
     for i in range(n_ev):
         tq.tq_set_split_events(evs[i][0], evs[i][1])
@@ -362,27 +547,27 @@ def main():
         hip.destroy(b)
     split_avg_ms = float(np.mean(split_ms))
 
-    reps = max(1, args.steps // ncopies) if graph is not None else 0
-    n_steps = reps * ncopies if graph is not None else args.steps
     if graph is not None:
-        for _ in range(max(1, args.warmup // ncopies)):
-            graph.replay()
+        graph.replay()  # untimed
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    replay_ms = []
     t_host0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        for _ in range(reps):
+    for _ in range(args.replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        if graph is not None:
             graph.replay()
-    else:
-        for i in range(n_steps):
-            step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+        else:
+            for i in range(K):
+                step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        replay_ms.append(e0.elapsed_time(e1) / K)
     t_host = time.perf_counter() - t_host0
-    total_ms = e0.elapsed_time(e1)
-    ms_per_step = total_ms / n_steps
+    ms_per_step = float(np.median(replay_ms))
+    n_steps = K
 
     # ---- the step's phases on their own (graph replay, as in the step), and the
     #      bulk encode of a whole cache (prefill), which is not part of the step
@@ -656,6 +841,13 @@ def main():
         "steps": n_steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
+        "timing": {"replays": len(replay_ms), "steps_per_replay": n_steps,
+                   "ms_per_step_median": round(ms_per_step, 6),
+                   "ms_per_step_min": round(min(replay_ms), 6),
+                   "ms_per_step_max": round(max(replay_ms), 6),
+                   "split_us_median": round(float(np.median(split_ms)) * 1e3, 3),
+                   "split_us_min": round(min(split_ms) * 1e3, 3),
+                   "split_us_max": round(max(split_ms) * 1e3, 3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -693,6 +885,10 @@ def main():
         "two_phase_cache_decode": cache_line,
         "bulk_encode_kv": bulk,
     }
+    per_config = {}
+    for name in [n for n in args.configs.split(",") if n and n != wl.name]:
+        per_config[name] = config_line(name, args, hip)
+    result["per_config"] = per_config
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -18,7 +18,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIB_PATH names another build of the same sources (the sanitizer build of
+# the host code used by the CPU tests); by default the in-tree libtq.so.
+LIB_PATH = os.environ.get("TQ_LIB_PATH") or os.path.join(_HERE, "libtq.so")
 
 TQ_OK = 0
 TQ_ERR_INVALID_ARG = -1
@@ -176,6 +178,30 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _require(fn: str, specs, contiguous: bool = True) -> None:
+    """Check (name, tensor, dtype) triples before anything is enqueued: every
+    dtype first, then that all tensors sit on the current GPU, then (unless
+    contiguous is False) that each is contiguous. The C ABI takes raw pointers
+    and byte strides, so a tensor of another dtype or on the host would be
+    misread or written past its end by the kernels."""
+    import torch
+    for name, t, dt in specs:
+        if t.dtype != dt:
+            raise TQError(TQ_ERR_INVALID_ARG, f"{fn}: {name} must be {dt}, got {t.dtype}")
+    for name, t, _ in specs:
+        if t.device.type != "cuda":
+            raise TQError(TQ_ERR_INVALID_ARG, f"{fn}: {name} must be a GPU tensor, got {t.device}")
+    cur = torch.cuda.current_device()
+    for name, t, _ in specs:
+        if t.device.index != cur:
+            raise TQError(TQ_ERR_INVALID_ARG,
+                          f"{fn}: {name} is on {t.device}, the current device is cuda:{cur}")
+    if contiguous:
+        for name, t, _ in specs:
+            if not t.is_contiguous():
+                raise TQError(TQ_ERR_INVALID_ARG, f"{fn}: {name} must be contiguous")
+
+
 # ------------------------------------------------------------------ codec
 
 class Codec:
@@ -263,7 +289,10 @@ def tq_encode_prod(codec: ProdCodec, x, codes, sketch, norms, rnorms, stream=Non
     """Encode x[n_tok][n_head][dim] with a Prod codec into codes
     [n_tok][n_head][row_bytes], sketch [n_tok][n_head][dim/8] (uint8), norms and
     residual norms [n_tok][n_head] (fp32); any strides, last dims contiguous."""
-    j = _encode_views(codec, x, codes, norms)
+    import torch
+    j = _encode_views(codec, x, codes, norms, "tq_encode_prod")
+    _require("tq_encode_prod", (("sketch", sketch, torch.uint8), ("rnorms", rnorms, torch.float32)),
+             contiguous=False)
     n_tok, n_head = x.shape[0], x.shape[1]
     if tuple(sketch.shape) != (n_tok, n_head, codec.sketch_bytes) or sketch.stride(2) != 1:
         raise TQError(TQ_ERR_INVALID_ARG, "sketch must be [n_tok][n_head][dim/8], row contiguous")
@@ -302,7 +331,10 @@ def tq_row_bytes(dim: int, bits: int) -> int:
 
 # ------------------------------------------------------------------ encode
 
-def _encode_views(codec: Codec, x, codes, norms):
+def _encode_views(codec: Codec, x, codes, norms, fn="tq_encode"):
+    import torch
+    _require(fn, (("x", x, torch.float16), ("codes", codes, torch.uint8),
+                  ("norms", norms, torch.float32)), contiguous=False)
     n_tok, n_head, d = x.shape
     if d != codec.dim or x.stride(2) != 1:
         raise TQError(TQ_ERR_INVALID_ARG, "x must be [n_tok][n_head][dim] with contiguous dim")
@@ -333,13 +365,27 @@ def tq_encode_kv(kc: Codec, k, k_codes, k_norms, vc: Codec, v, v_codes, v_norms,
     the same [n_tok][n_head] grid, the other rules are tq_encode's."""
     if tuple(k.shape[:2]) != tuple(v.shape[:2]):
         raise TQError(TQ_ERR_INVALID_ARG, "k and v must share [n_tok][n_head]")
-    jk = _encode_views(kc, k, k_codes, k_norms)
-    jv = _encode_views(vc, v, v_codes, v_norms)
+    jk = _encode_views(kc, k, k_codes, k_norms, "tq_encode_kv")
+    jv = _encode_views(vc, v, v_codes, v_norms, "tq_encode_kv")
     _check(_lib.tq_encode_kv(ctypes.byref(jk), ctypes.byref(jv), k.shape[0], k.shape[1],
                              _stream_ptr(stream)))
 
 
 # ------------------------------------------------------------------ attend
+
+def _attend_tensors(fn, q, k_codes, k_norms, v_codes, v_norms, lengths, out, workspace,
+                    extra=()):
+    """The dtype / device / layout checks every attend call shares (workspace
+    None: the call takes none)."""
+    import torch
+    specs = [("q", q, torch.float16), ("k_codes", k_codes, torch.uint8),
+             ("k_norms", k_norms, torch.float32), ("v_codes", v_codes, torch.uint8),
+             ("v_norms", v_norms, torch.float32), ("lengths", lengths, torch.int32),
+             ("out", out, torch.float32)]
+    if workspace is not None:
+        specs.append(("workspace", workspace, torch.uint8))
+    _require(fn, tuple(specs) + tuple(extra))
+
 
 def tq_attend_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, dim: int,
                               max_len: int) -> int:
@@ -358,11 +404,8 @@ def tq_decode_attend(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms
     tq_attend_workspace_bytes(...) bytes. All contiguous."""
     B, Hq, d = q.shape
     Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
-    for name, t in (("q", q), ("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
-                    ("v_norms", v_norms), ("lengths", lengths), ("out", out),
-                    ("workspace", workspace)):
-        if not t.is_contiguous():
-            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    _attend_tensors("tq_decode_attend", q, k_codes, k_norms, v_codes, v_norms, lengths, out,
+                    workspace)
     if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
        tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
        tuple(v_norms.shape) != (B, Hkv, max_ctx) or tuple(out.shape) != (B, Hq, d) or \
@@ -389,11 +432,8 @@ def tq_decode_attend_multi(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v
     ones; the rest as tq_decode_attend."""
     B, S, Hq, d = q.shape
     Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
-    for name, t in (("q", q), ("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
-                    ("v_norms", v_norms), ("lengths", lengths), ("out", out),
-                    ("workspace", workspace)):
-        if not t.is_contiguous():
-            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    _attend_tensors("tq_decode_attend_multi", q, k_codes, k_norms, v_codes, v_norms, lengths, out,
+                    workspace)
     if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
        tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
        tuple(v_norms.shape) != (B, Hkv, max_ctx) or tuple(out.shape) != (B, S, Hq, d) or \
@@ -415,12 +455,11 @@ def tq_decode_attend_mixed(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v
     over both. The rest as tq_decode_attend."""
     B, Hq, d = q.shape
     Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
-    for name, t in (("q", q), ("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
-                    ("v_norms", v_norms), ("lengths", lengths), ("out", out),
-                    ("workspace", workspace), ("raw_k", raw_k), ("raw_v", raw_v),
-                    ("raw_lengths", raw_lengths)):
-        if not t.is_contiguous():
-            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    import torch
+    _attend_tensors("tq_decode_attend_mixed", q, k_codes, k_norms, v_codes, v_norms, lengths,
+                    out, workspace,
+                    (("raw_k", raw_k, torch.float16), ("raw_v", raw_v, torch.float16),
+                     ("raw_lengths", raw_lengths, torch.int32)))
     max_raw = raw_k.shape[2]
     if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
        tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
@@ -442,10 +481,11 @@ def tq_decode_attend_raw_k(vc: Codec, q, k, v_codes, v_norms, lengths, max_len: 
     tq_decode_attend."""
     B, Hq, d = q.shape
     Hkv, max_ctx = v_norms.shape[1], v_norms.shape[2]
-    for name, t in (("q", q), ("k", k), ("v_codes", v_codes), ("v_norms", v_norms),
-                    ("lengths", lengths), ("out", out), ("workspace", workspace)):
-        if not t.is_contiguous():
-            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    import torch
+    _require("tq_decode_attend_raw_k",
+             (("q", q, torch.float16), ("k", k, torch.float16), ("v_codes", v_codes, torch.uint8),
+              ("v_norms", v_norms, torch.float32), ("lengths", lengths, torch.int32),
+              ("out", out, torch.float32), ("workspace", workspace, torch.uint8)))
     if tuple(k.shape) != (B, Hkv, max_ctx, d) or \
        tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
        tuple(out.shape) != (B, Hq, d) or tuple(lengths.shape) != (B,):
@@ -464,11 +504,10 @@ def tq_decode_attend_prod(kc: ProdCodec, vc: Codec, q, k_codes, k_sketch, k_norm
     norms) with packed values; the rest as tq_decode_attend."""
     B, Hq, d = q.shape
     Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
-    for name, t in (("q", q), ("k_codes", k_codes), ("k_sketch", k_sketch), ("k_norms", k_norms),
-                    ("k_rnorms", k_rnorms), ("v_codes", v_codes), ("v_norms", v_norms),
-                    ("lengths", lengths), ("out", out), ("workspace", workspace)):
-        if not t.is_contiguous():
-            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    import torch
+    _attend_tensors("tq_decode_attend_prod", q, k_codes, k_norms, v_codes, v_norms, lengths, out,
+                    workspace,
+                    (("k_sketch", k_sketch, torch.uint8), ("k_rnorms", k_rnorms, torch.float32)))
     if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
        tuple(k_sketch.shape) != (B, Hkv, max_ctx, kc.sketch_bytes) or \
        tuple(k_rnorms.shape) != (B, Hkv, max_ctx) or \
@@ -494,6 +533,8 @@ def tq_stream_read(buf, sink, stream=None) -> None:
     aligned) device tensor buf; sink is a device tensor of at least 4 bytes."""
     if not buf.is_contiguous():
         raise ValueError("buf must be contiguous")
+    if buf.device.type != "cuda" or sink.device.type != "cuda":
+        raise TQError(TQ_ERR_INVALID_ARG, "tq_stream_read: buf and sink must be GPU tensors")
     nbytes = buf.numel() * buf.element_size()
     _check(_lib.tq_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
                                ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
@@ -539,11 +580,12 @@ def tq_cache_init(kc: Codec, vc: Codec, k_codes, k_norms, v_codes, v_norms, pend
     [B][Hkv][group_size][d], device int32 length arrays [B]."""
     B, Hkv, max_ctx = k_norms.shape
     G = pending_k.shape[2]
-    for name, t in (("k_codes", k_codes), ("k_norms", k_norms), ("v_codes", v_codes),
-                    ("v_norms", v_norms), ("pending_k", pending_k), ("pending_v", pending_v),
-                    ("packed_len", packed_len), ("pending_len", pending_len)):
-        if not t.is_contiguous():
-            raise TQError(TQ_ERR_INVALID_ARG, f"{name} must be contiguous")
+    import torch
+    _require("tq_cache_init",
+             (("k_codes", k_codes, torch.uint8), ("k_norms", k_norms, torch.float32),
+              ("v_codes", v_codes, torch.uint8), ("v_norms", v_norms, torch.float32),
+              ("pending_k", pending_k, torch.float16), ("pending_v", pending_v, torch.float16),
+              ("packed_len", packed_len, torch.int32), ("pending_len", pending_len, torch.int32)))
     if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
        tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
        tuple(v_norms.shape) != (B, Hkv, max_ctx) or \
@@ -572,8 +614,10 @@ def tq_cache_state(cache: Cache):
 
 def tq_cache_append(cache: Cache, k, v, stream=None) -> None:
     """Append k, v [B][Hkv][n][d] fp16 (contiguous) to the cache."""
-    if not k.is_contiguous() or not v.is_contiguous() or k.shape != v.shape:
-        raise TQError(TQ_ERR_INVALID_ARG, "k and v must be contiguous and of one shape")
+    import torch
+    _require("tq_cache_append", (("k", k, torch.float16), ("v", v, torch.float16)))
+    if k.shape != v.shape:
+        raise TQError(TQ_ERR_INVALID_ARG, "k and v must be of one shape")
     B, Hkv, n, d = k.shape
     pk = cache.buffers[4]
     if (B, Hkv, d) != (pk.shape[0], pk.shape[1], pk.shape[3]):
@@ -587,8 +631,9 @@ def tq_cache_workspace_bytes(cache: Cache, n_q_heads: int) -> int:
 
 def tq_cache_attend(cache: Cache, q, scale: float, out, workspace, stream=None) -> None:
     """Decode attention of q [B][Hq][d] over the cache's packed and pending rows."""
-    if not q.is_contiguous() or not out.is_contiguous() or not workspace.is_contiguous():
-        raise TQError(TQ_ERR_INVALID_ARG, "q, out and workspace must be contiguous")
+    import torch
+    _require("tq_cache_attend", (("q", q, torch.float16), ("out", out, torch.float32),
+                                 ("workspace", workspace, torch.uint8)))
     B, Hq, d = q.shape
     if tuple(out.shape) != (B, Hq, d):
         raise TQError(TQ_ERR_INVALID_ARG, "out shape disagrees with q")

@@ -420,13 +420,19 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
     return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale is NaN", fn);
   const int group = n_q_heads / n_kv_heads;
-  if (dense) {
-    const tq::AttendPlan dplan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
-    if (!workspace || workspace_bytes < dplan.total_bytes)
+  // The caller's workspace, checked against what the plan needs.
+  auto take_workspace = [&](size_t need) -> tq_status {
+    if (!workspace || workspace_bytes < need)
       return fail(TQ_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
-                  workspace ? workspace_bytes : (size_t)0, dplan.total_bytes);
+                  workspace ? workspace_bytes : (size_t)0, need);
     if ((uintptr_t)workspace & 255)
       return fail(TQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    return TQ_OK;
+  };
+  if (dense) {
+    const tq::AttendPlan dplan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
+    const tq_status ws = take_workspace(dplan.total_bytes);
+    if (ws != TQ_OK) return ws;
     tq::DenseAttendArgs da;
     std::memset(&da, 0, sizeof(da));
     da.q = q_fp16;
@@ -449,6 +455,7 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
     da.max_ctx = max_ctx;
     da.splits = dplan.splits;
     da.tokens_per_split = dplan.tokens_per_split;
+    da.max_len = max_len;
     da.qscale = tq::dense_qscale(scale, dim);
     std::memcpy(da.k_centroids, kc->tabs.centroids, sizeof(float) * (1 << da.k_bits));
     std::memcpy(da.v_centroids, vc->tabs.centroids, sizeof(float) * (1 << da.v_bits));
@@ -466,11 +473,8 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
       tq::plan_attend(batch, n_q_heads * n_qtok, n_kv_heads, dim, max_len);
   if ((long long)plan.splits > 0x7fffffffLL)
     return fail(TQ_ERR_UNSUPPORTED, "%s: context too long", fn);
-  if (!workspace || workspace_bytes < plan.total_bytes)
-    return fail(TQ_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
-                workspace ? workspace_bytes : (size_t)0, plan.total_bytes);
-  if ((uintptr_t)workspace & 255)
-    return fail(TQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  const tq_status ws = take_workspace(plan.total_bytes);
+  if (ws != TQ_OK) return ws;
   tq::AttendTables tabs;
   tq::SignArg ksign;
   if (raw_k) {
@@ -613,9 +617,12 @@ tq_encode_job cache_job(const tq_codec* c, const void* x, int rows_per_head, int
 }
 
 // One launch: K and V rows [row0, row0 + rows) of src ([heads][src_rows][dim])
-// to pending rows [dst_row0, ..) and the counts published to the length arrays.
+// to pending rows [dst_row0, ..) and the counts n_packed / n_pending published
+// to the length arrays. The caller commits those counts to the host state only
+// once this has returned TQ_OK, so a failed launch leaves host and device agreeing.
 tq_status cache_move_rows(tq_cache* c, const char* fn, const void* src_k, const void* src_v,
-                          int src_rows, int row0, int dst_row0, int rows, void* stream) {
+                          int src_rows, int row0, int dst_row0, int rows, int n_packed,
+                          int n_pending, void* stream) {
   const int dim = c->kc->tabs.dim;
   const int row16 = dim / 8;  // 16-byte words per fp16 row
   tq::CopyRowsArgs a;
@@ -629,8 +636,8 @@ tq_status cache_move_rows(tq_cache* c, const char* fn, const void* src_k, const 
   a.rows = rows;
   a.heads = c->d.batch * c->d.n_kv_heads;
   a.batch = c->d.batch;
-  a.n_packed = c->n_packed;
-  a.n_pending = c->n_pending;
+  a.n_packed = n_packed;
+  a.n_pending = n_pending;
   a.packed_len = c->d.packed_len;
   a.pending_len = c->d.pending_len;
   hipError_t err = tq::launch_pending_rows(a, (hipStream_t)stream);
@@ -712,9 +719,11 @@ tq_status tq_cache_append(tq_cache* c, const void* k_fp16, const void* v_fp16, i
   tq_status st;
   if (groups == 0) {
     // the rows join the pending buffer
+    if ((st = cache_move_rows(c, fn, k_fp16, v_fp16, n_tok, 0, (int)P, n_tok, c->n_packed,
+                              (int)total, stream)) != TQ_OK)
+      return st;
     c->n_pending = (int)total;
-    return cache_move_rows(c, fn, k_fp16, v_fp16, n_tok, 0, (int)P, n_tok, stream) == TQ_OK
-               ? ok() : TQ_ERR_HIP;
+    return ok();
   }
   // whole groups: the pending rows first, then the leading new rows
   if (P > 0) {
@@ -734,11 +743,16 @@ tq_status tq_cache_append(tq_cache* c, const void* k_fp16, const void* v_fp16, i
     tq_encode_job jobs[2] = {kj, vj};
     if ((st = encode_jobs(fn, jobs, 2, from_new, heads, stream)) != TQ_OK) return st;
   }
-  // the rest of the new rows start the next pending group
+  // the rest of the new rows start the next pending group; the encodes above
+  // wrote only rows past the published packed length, so until this launch
+  // succeeds the device state still matches the old counts
+  const int rest = n_tok - from_new;
+  if ((st = cache_move_rows(c, fn, k_fp16, v_fp16, n_tok, from_new, 0, rest, (int)new_packed,
+                            rest, stream)) != TQ_OK)
+    return st;
   c->n_packed = (int)new_packed;
-  c->n_pending = n_tok - from_new;
-  return cache_move_rows(c, fn, k_fp16, v_fp16, n_tok, from_new, 0, c->n_pending, stream) == TQ_OK
-             ? ok() : TQ_ERR_HIP;
+  c->n_pending = rest;
+  return ok();
 }
 
 size_t tq_cache_workspace_bytes(const tq_cache* c, int n_q_heads) {
@@ -753,7 +767,8 @@ tq_status tq_cache_attend(tq_cache* c, const void* q_fp16, int n_q_heads, float 
   if (!c) return fail(TQ_ERR_INVALID_ARG, "%s: cache is NULL", fn);
   const tq_cache_desc& d = c->d;
   if (!c->lengths_published) {
-    tq_status st = cache_move_rows(c, fn, d.pending_k, d.pending_v, d.group_size, 0, 0, 0, stream);
+    tq_status st = cache_move_rows(c, fn, d.pending_k, d.pending_v, d.group_size, 0, 0, 0,
+                                   c->n_packed, c->n_pending, stream);
     if (st != TQ_OK) return st;
   }
   return tq_decode_attend_mixed(c->kc, c->vc, q_fp16, d.batch, n_q_heads, d.n_kv_heads,

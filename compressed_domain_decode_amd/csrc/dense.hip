@@ -239,7 +239,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
   }
   __syncthreads();
 
-  const int len = a.lengths[b];
+  const int len = min(a.lengths[b], a.max_len);  // never read past the host bound
   const long long t_begin = (long long)s * a.tokens_per_split;
   const long long t_stop = t_begin + a.tokens_per_split;
   const int t_end = (int)(t_stop < len ? t_stop : (len > 0 ? len : 0));

@@ -139,6 +139,7 @@ struct DenseAttendArgs {
   float* pml;                  //            [batch][n_q_heads][splits][2]
   float* out;                  // [batch][n_q_heads][dim]
   int dim, k_bits, v_bits, n_q_heads, n_kv_heads, group, max_ctx, splits, tokens_per_split;
+  int max_len;                 // host bound of lengths (<= max_ctx); lengths are clamped to it
   int rows_words, wave_stride; // per-wavefront LDS region (set by the launcher)
   float qscale;                // scale * log2(e) / dim
   float k_centroids[256];      // unused entries zero

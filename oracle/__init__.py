@@ -25,7 +25,10 @@ from . import codebook
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tq_oracle.c")
-_LIB = os.path.join(_HERE, "_tq_oracle.so")
+# TQ_ORACLE_LIB names another build of tq_oracle.c (the sanitizer run of the
+# CPU tests); by default the library beside this file, rebuilt when stale.
+_LIB_DEFAULT = os.path.join(_HERE, "_tq_oracle.so")
+_LIB = os.environ.get("TQ_ORACLE_LIB") or _LIB_DEFAULT
 _lock = threading.Lock()
 _lib = None
 
@@ -34,18 +37,19 @@ CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
 
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    if force or not os.path.exists(_LIB_DEFAULT):
+        tmp = _LIB_DEFAULT + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _LIB_DEFAULT)
+    return _LIB_DEFAULT
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            if _LIB == _LIB_DEFAULT and (not os.path.exists(_LIB) or
+                                         os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
                 build()
             lib = ctypes.CDLL(_LIB)
             P = ctypes.c_void_p

@@ -54,10 +54,11 @@ def gpu_encode_cache(codec, x_np):
     return codes, norms
 
 
-def gpu_attend(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np):
+def gpu_attend(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np, max_len=None):
     B, Hq, d = q_np.shape
     Hkv = knorms.shape[1]
-    max_len = max(1, int(np.max(lengths_np)))
+    if max_len is None:
+        max_len = max(1, int(np.max(lengths_np)))
     q = torch.from_numpy(np.ascontiguousarray(q_np)).to(DEV)
     lengths = torch.from_numpy(np.asarray(lengths_np, dtype=np.int32)).to(DEV)
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
@@ -156,6 +157,38 @@ def test_dense_attend_phi3_mini_shape_sampled():
         ref = oracle.attend_dense(ko, vo, q[:, g * G:(g + 1) * G], okc, okn, ovc, ovn,
                                   np.array([T]))
         assert np.abs(out[:, g * G:(g + 1) * G] - ref).max() <= ATOL
+
+
+def test_dense_attend_rows_beyond_length_never_read():
+    """Rows past each sequence's length hold 0xFF codes and NaN norms; a device
+    length above max_len is clamped to it. The cache is allocated well past
+    what the launch covers (max_ctx 1000 against 5 splits of 64 tokens), so
+    every read stays in bounds even where a length exceeds max_len."""
+    d, kb, vb, G, Hkv, T, max_len = 96, 4, 2, 3, 2, 1000, 300
+    announce(f"dense attend poisoned rows d={d} max_ctx={T} max_len={max_len}")
+    kc, _ = dense_codecs(d, kb, 31)
+    vc, _ = dense_codecs(d, vb, 32)
+    rng = np.random.default_rng(33)
+    lens = [300, 77, 150]
+    B = len(lens)
+    k = _inputs(rng, (B, Hkv, T, d), d)
+    v = _inputs(rng, (B, Hkv, T, d), d)
+    q = rng.standard_normal((B, G * Hkv, d)).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(kc, k)
+    vcodes, vnorms = gpu_encode_cache(vc, v)
+    clean = gpu_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, lens, max_len=max_len)
+    for b, L in enumerate(lens):
+        kcodes[b, :, L:] = 0xFF
+        vcodes[b, :, L:] = 0xFF
+        knorms[b, :, L:] = float("nan")
+        vnorms[b, :, L:] = float("nan")
+    dirty = gpu_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, lens, max_len=max_len)
+    assert np.isfinite(dirty).all()
+    assert clean.tobytes() == dirty.tobytes()
+    # sequence 0 claims 900 rows on the device; max_len 300 bounds what is read
+    over = gpu_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, [900, 77, 150],
+                      max_len=max_len)
+    assert clean.tobytes() == over.tobytes()
 
 
 def test_dense_codecs_rejected_where_unsupported():

@@ -552,6 +552,70 @@ def test_prod_residual_reconstructs_and_sketch_is_dense_product(d, bits):
     assert np.array_equal(got[clear], want[clear])
 
 
+@pytest.mark.parametrize("d,bits,seed", [(64, 3, 5), (128, 2, 6), (128, 4, 7), (256, 3, 8)])
+def test_prod_sketch_signs_exact_outside_butterfly_error_bound(d, bits, seed):
+    """Each sketch bit against the exact sign of y_j = sum_i H_ji sigma_S,i rho_i.
+    Every term +-rho_i is an fp64 number, and math.fsum returns the correctly
+    rounded sum of its terms, so its sign is the sign of the exact sum. The
+    oracle's butterfly adds log2(d) times per output, each addition off by at
+    most one rounding, so |y_hat - y| <= gamma_k sum_i |rho_i| with k = log2 d
+    and gamma_k = k u / (1 - k u), u = 2^-53. Wherever |y| exceeds that bound the
+    bit must be the exact sign; entries under it are counted and must be rare."""
+    rng = np.random.default_rng(seed)
+    n = 60
+    x = (rng.standard_normal((n, d)) * rng.uniform(0.05, 20.0, (n, 1))).astype(np.float16)
+    x[0] = 0.0                                    # zero vector: rho = -c[idx], no zero sums
+    pc = oracle.ProdCodec(d, bits, 31 + seed)
+    codes, sketch, norms, gam = oracle.encode_prod(pc, x)
+    _, _, _, z = oracle.encode(pc.mse, x, want_z=True)
+    idx = np.stack([oracle.unpack(r, d, bits - 1) for r in codes])
+    rho = z - pc.mse.centroids.astype(np.float64)[idx]
+    H = _sylvester(d)
+    k = int(math.log2(d))
+    u = 2.0 ** -53
+    gamma_k = k * u / (1.0 - k * u)
+    got = np.unpackbits(sketch, axis=1, bitorder="little")[:, :d]
+    # the zero vector: rho = -c[2^(b-2) - 1] in every coordinate, so every partial
+    # sum of the butterfly is an exact multiple of it and y_j = 0 exactly where
+    # (H sigma_S)_j = 0; the bit is then (0 < 0) = 0
+    y0 = np.array([math.fsum((H[j] * rho[0] * pc.sketch_signs).tolist()) for j in range(d)])
+    assert np.array_equal(got[0], (y0 < 0).astype(np.uint8))
+    under = 0
+    for r in range(1, n):
+        terms = rho[r] * pc.sketch_signs.astype(np.float64)   # exact: a sign flip
+        bound = gamma_k * float(np.abs(terms).sum()) * (1.0 + 4.0 * d * u)  # + slack of the bound's own sum
+        for j in range(d):
+            y = math.fsum((H[j] * terms).tolist())               # H_ji = +-1: exact terms
+            if abs(y) > bound:
+                assert got[r, j] == (1 if y < 0 else 0), (r, j, y, bound)
+            else:
+                under += 1
+    print(f"d={d} bits={bits}: {under} of {(n - 1) * d} entries within the butterfly error bound")
+    assert under <= (n - 1) * d // 1000
+
+
+def test_prod_sketch_sign_pin_catches_a_wrong_bit():
+    """The exact-sign check above fails on a sketch computed from rho with one
+    coordinate's sign flipped (a plausible indexing mistake), so it can see
+    more than its own output."""
+    d, bits = 64, 3
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, d)).astype(np.float16)
+    pc = oracle.ProdCodec(d, bits, 9)
+    _, _, _, z = oracle.encode(pc.mse, x, want_z=True)
+    codes, sketch, _, _ = oracle.encode_prod(pc, x)
+    idx = np.stack([oracle.unpack(r, d, bits - 1) for r in codes])
+    rho = z - pc.mse.centroids.astype(np.float64)[idx]
+    bad = rho.copy()
+    bad[:, 5] = -bad[:, 5]
+    H = _sylvester(d)
+    terms = bad * pc.sketch_signs.astype(np.float64)
+    exact = np.array([[math.fsum((H[j] * terms[r]).tolist()) for j in range(d)]
+                      for r in range(4)])
+    got = np.unpackbits(sketch, axis=1, bitorder="little")[:, :d]
+    assert np.any(got != (exact < 0))
+
+
 def test_qjl_estimate_is_unbiased_over_sketch_draws():
     """Average of the estimate over random sketch sign vectors approaches
     <q~, rho>: a wrong sign or a missing sqrt(pi/2) fails it."""
