@@ -38,6 +38,7 @@ EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
     "tq_cache_init", "tq_cache_destroy", "tq_cache_state", "tq_cache_append",
     "tq_cache_workspace_bytes", "tq_cache_attend", "tq_codec_init_dense",
+    "tq_decode_attend_noalloc",
 )
 
 
@@ -94,6 +95,10 @@ _lib.tq_attend_num_splits.restype = _I
 _lib.tq_decode_attend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
                                   ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_decode_attend.restype = _I
+_lib.tq_decode_attend_noalloc.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
+                                          ctypes.c_float, _P, _P]
+_lib.tq_decode_attend_noalloc.restype = _I
+TQ_NOALLOC_SCRATCH_BYTES = 8 << 20  # include/tq.h
 _lib.tq_decode_attend_multi.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I,
                                         ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_decode_attend_multi.restype = _I
@@ -416,6 +421,26 @@ def tq_decode_attend(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms
                                  _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), max_ctx,
                                  _ptr(lengths), int(max_len), float(scale), _ptr(out),
                                  _ptr(workspace), nbytes, _stream_ptr(stream)))
+
+
+def tq_decode_attend_noalloc(kc: Codec, vc: Codec, q, k_codes, k_norms, v_codes, v_norms,
+                             lengths, max_len: int, scale: float, out, stream=None) -> None:
+    """tq_decode_attend with the library's fixed per-GPU scratch array in place
+    of a workspace (nothing is allocated); the arguments otherwise as there.
+    Calls that overlap on one GPU share that array and race."""
+    B, Hq, d = q.shape
+    Hkv, max_ctx = k_norms.shape[1], k_norms.shape[2]
+    _attend_tensors("tq_decode_attend_noalloc", q, k_codes, k_norms, v_codes, v_norms, lengths,
+                    out, None)
+    if tuple(k_codes.shape) != (B, Hkv, max_ctx, kc.row_bytes) or \
+       tuple(v_codes.shape) != (B, Hkv, max_ctx, vc.row_bytes) or \
+       tuple(v_norms.shape) != (B, Hkv, max_ctx) or tuple(out.shape) != (B, Hq, d) or \
+       tuple(lengths.shape) != (B,):
+        raise TQError(TQ_ERR_INVALID_ARG, "cache / output shapes disagree")
+    _check(_lib.tq_decode_attend_noalloc(kc.handle, vc.handle, _ptr(q), B, Hq, Hkv,
+                                         _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                                         _ptr(v_norms), max_ctx, _ptr(lengths), int(max_len),
+                                         float(scale), _ptr(out), _stream_ptr(stream)))
 
 
 def tq_attend_multi_workspace_bytes(batch: int, n_query_tokens: int, n_q_heads: int,

@@ -26,7 +26,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
-HIP_SOURCES = ["encode.hip", "attend.hip", "probe.hip", "cache.hip", "dense.hip"]
+HIP_SOURCES = ["encode.hip", "attend.hip", "probe.hip", "cache.hip", "dense.hip", "scratch.hip"]
 HOST_SOURCES = ["codec.cpp", "api.cpp"]
 
 

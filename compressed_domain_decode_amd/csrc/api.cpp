@@ -378,7 +378,7 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
                         const int32_t* lengths, int max_len, float scale, float* out,
                         void* workspace, size_t workspace_bytes, const tq::RawSegment& raw,
                         void* stream, bool raw_k = false,
-                        const tq::ProdKeys* prodk = nullptr) {
+                        const tq::ProdKeys* prodk = nullptr, bool use_scratch = false) {
   // raw_k: k_codes holds fp16 key rows, there is no K codec and no key norm
   if ((!kc && !raw_k) || !vc) return fail(TQ_ERR_INVALID_ARG, "%s: codec is NULL", fn);
   if (kc && kc->tabs.prod != (prodk != nullptr))
@@ -420,8 +420,22 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
     return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (!(scale == scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale is NaN", fn);
   const int group = n_q_heads / n_kv_heads;
-  // The caller's workspace, checked against what the plan needs.
+  // The caller's workspace, or (use_scratch) this device's fixed scratch
+  // array, checked against what the plan needs.
   auto take_workspace = [&](size_t need) -> tq_status {
+    if (use_scratch) {
+      if (need > (size_t)TQ_NOALLOC_SCRATCH_BYTES)
+        return fail(TQ_ERR_UNSUPPORTED,
+                    "%s: this shape needs %zu bytes of scratch, more than the fixed %zu", fn,
+                    need, (size_t)TQ_NOALLOC_SCRATCH_BYTES);
+      void* p = nullptr;
+      const hipError_t e = tq::scratch_region(&p);
+      if (e != hipSuccess)
+        return fail(TQ_ERR_HIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
+      workspace = p;
+      workspace_bytes = (size_t)TQ_NOALLOC_SCRATCH_BYTES;
+      return TQ_OK;
+    }
     if (!workspace || workspace_bytes < need)
       return fail(TQ_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
                   workspace ? workspace_bytes : (size_t)0, need);
@@ -508,6 +522,18 @@ tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q
   return decode_attend("tq_decode_attend", kc, vc, q_fp16, batch, 1, n_q_heads, n_kv_heads,
                        k_codes, k_norms, v_codes, v_norms, max_ctx, lengths, max_len, scale,
                        out, workspace, workspace_bytes, tq::RawSegment{}, stream);
+}
+
+tq_status tq_decode_attend_noalloc(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                   int batch, int n_q_heads, int n_kv_heads,
+                                   const uint8_t* k_codes, const float* k_norms,
+                                   const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                   const int32_t* lengths, int max_len, float scale, float* out,
+                                   void* stream) {
+  return decode_attend("tq_decode_attend_noalloc", kc, vc, q_fp16, batch, 1, n_q_heads,
+                       n_kv_heads, k_codes, k_norms, v_codes, v_norms, max_ctx, lengths,
+                       max_len, scale, out, nullptr, 0, tq::RawSegment{}, stream, false,
+                       nullptr, true);
 }
 
 size_t tq_attend_multi_workspace_bytes(int batch, int n_query_tokens, int n_q_heads,

@@ -151,6 +151,10 @@ hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t 
 hipError_t prepare_attend_dense();
 float dense_qscale(float scale, int dim);
 
+// Device address of this GPU's fixed scratch array (TQ_NOALLOC_SCRATCH_BYTES
+// bytes, 256-byte aligned), looked up on the first call per device.
+hipError_t scratch_region(void** ptr);
+
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

@@ -234,6 +234,31 @@ tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tq_decode_attend for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, with the per-split partials in a fixed array the library
+ * holds on each GPU (TQ_NOALLOC_SCRATCH_BYTES bytes in its code object, kept
+ * until the process ends) instead of a caller workspace. The call allocates
+ * nothing; its first call on a device looks up that device's array.
+ *   Arguments as tq_decode_attend without the workspace pair; the caller still
+ *   owns q, the cache, lengths and out.
+ *   Errors as tq_decode_attend; TQ_ERR_UNSUPPORTED when the shape needs more
+ *   than TQ_NOALLOC_SCRATCH_BYTES of partials (tq_attend_workspace_bytes of the
+ *   same shape tells), TQ_ERR_HIP if the array's address cannot be found.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one device (two streams, two threads) race and must be ordered by the caller.
+ * The kernels write every partial they later read, so nothing carries over
+ * from the previous call. Results equal tq_decode_attend's bit for bit.
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+tq_status tq_decode_attend_noalloc(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
+                                   int batch, int n_q_heads, int n_kv_heads,
+                                   const uint8_t* k_codes, const float* k_norms,
+                                   const uint8_t* v_codes, const float* v_norms, int max_ctx,
+                                   const int32_t* lengths, int max_len, float scale, float* out,
+                                   void* stream);
+
+/*
  * Multi-token decode: n_query_tokens new query rows per sequence attend the
  * packed cache at once, causal among themselves (verifying a speculative
  * draft, or a chunk of queries; PR #232's review threads on the multi-query

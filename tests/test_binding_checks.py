@@ -27,8 +27,12 @@ def _attend_args(kc, vc):
 
 
 def _call_attend(fn_name, kc, vc, a):
-    tq.tq_decode_attend(kc, vc, a["q"], a["k_codes"], a["k_norms"], a["v_codes"],
-                        a["v_norms"], a["lengths"], T, 0.125, a["out"], a["workspace"])
+    if fn_name == "tq_decode_attend":
+        tq.tq_decode_attend(kc, vc, a["q"], a["k_codes"], a["k_norms"], a["v_codes"],
+                            a["v_norms"], a["lengths"], T, 0.125, a["out"], a["workspace"])
+    else:
+        tq.tq_decode_attend_noalloc(kc, vc, a["q"], a["k_codes"], a["k_norms"], a["v_codes"],
+                                    a["v_norms"], a["lengths"], T, 0.125, a["out"])
 
 
 # a wrong dtype of the same element count where sizes allow, else a plain mismatch
@@ -39,9 +43,11 @@ WRONG = {
 }
 
 
-@pytest.mark.parametrize("fn_name", ["tq_decode_attend"])
+@pytest.mark.parametrize("fn_name", ["tq_decode_attend", "tq_decode_attend_noalloc"])
 @pytest.mark.parametrize("name", list(WRONG))
 def test_attend_rejects_wrong_dtype(fn_name, name):
+    if fn_name == "tq_decode_attend_noalloc" and name == "workspace":
+        pytest.skip("the no-alloc call takes no workspace")
     kc, vc = _codecs()
     a = _attend_args(kc, vc)
     a[name] = a[name].to(WRONG[name])
@@ -51,7 +57,7 @@ def test_attend_rejects_wrong_dtype(fn_name, name):
     assert f"{name} must be" in str(e.value)
 
 
-@pytest.mark.parametrize("fn_name", ["tq_decode_attend"])
+@pytest.mark.parametrize("fn_name", ["tq_decode_attend", "tq_decode_attend_noalloc"])
 def test_attend_rejects_host_tensors(fn_name):
     kc, vc = _codecs()
     with pytest.raises(tq.TQError) as e:
