@@ -443,15 +443,28 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
       return fail(TQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     return TQ_OK;
   };
-  if (dense) {
+  // Walsh-Hadamard codec pairs with no matrix-core instance run the dense
+  // kernels with m = H diag(sigma) formed from the codecs' signs (the same
+  // result as the dense codec with that matrix): every bit width pair is served
+  const bool fast = !dense && tq::attend_supported(dim, k_bits, vc->tabs.bits, group * n_qtok);
+  const bool wht_fallback = !dense && !fast && n_qtok == 1 && !raw.lengths && !prodk && !raw_k;
+  if (dense || wht_fallback) {
     const tq::AttendPlan dplan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
     const tq_status ws = take_workspace(dplan.total_bytes);
     if (ws != TQ_OK) return ws;
     tq::DenseAttendArgs da;
     std::memset(&da, 0, sizeof(da));
     da.q = q_fp16;
-    da.mt_k = kc->mt_dev;
-    da.m_v = vc->m_dev;
+    if (dense) {
+      da.mt_k = kc->mt_dev;
+      da.m_v = vc->m_dev;
+      da.lds_limit = tq::kDenseLdsFull;  // raised at codec set-up
+    } else {
+      da.wht = 1;
+      da.wht_k = sign_arg(kc);
+      da.wht_v = sign_arg(vc);
+      da.lds_limit = tq::kDenseLdsDefault;
+    }
     da.k_codes = k_codes;
     da.k_norms = k_norms;
     da.v_codes = v_codes;
@@ -478,7 +491,7 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
       return fail(TQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return ok();
   }
-  if (!tq::attend_supported(dim, k_bits, vc->tabs.bits, group * n_qtok))
+  if (!fast)
     return fail(TQ_ERR_UNSUPPORTED,
                 "%s: no kernel for dim %d, K %d-bit%s, V %d-bit, %d heads per KV head", fn, dim,
                 prodk ? kc->tabs.bits + 1 : k_bits, prodk ? " Prod" : "", vc->tabs.bits,

@@ -1383,7 +1383,8 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(64, 8, 3, 1), TQ_SPLIT(64, 2, 2, 1), TQ_SPLIT(64, 1, 1, 1),
     TQ_SPLIT(64, 5, 7, 1), TQ_SPLIT(64, 6, 6, 4), TQ_SPLIT(64, 4, 4, 2),
     TQ_SPLIT(64, 8, 3, 2), TQ_SPLIT(64, 3, 3, 4), TQ_SPLIT(64, 16, 4, 1), TQ_SPLIT(64, 16, 4, 2),
-    TQ_SPLIT(64, 35, 4, 1),
+    TQ_SPLIT(64, 35, 4, 1), TQ_SPLIT(64, 4, 2, 1), TQ_SPLIT(64, 4, 3, 1),
+    TQ_SPLIT(64, 16, 2, 1),
     // head_dim 128
     TQ_SPLIT_S(128, 4, 2, 1), TQ_SPLIT(128, 8, 3, 1), TQ_SPLIT(128, 3, 3, 1),
     TQ_SPLIT(128, 4, 4, 1), TQ_SPLIT(128, 4, 3, 1), TQ_SPLIT(128, 2, 2, 1),
@@ -1399,7 +1400,8 @@ const SplitEntry kSplitTable[] = {
     TQ_SPLIT(128, 35, 4, 1), TQ_SPLIT(128, 35, 4, 2), TQ_SPLIT(128, 34, 3, 1),
     // head_dim 256
     TQ_SPLIT(256, 4, 4, 1), TQ_SPLIT(256, 8, 3, 1), TQ_SPLIT(256, 3, 3, 1),
-    TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2),
+    TQ_SPLIT(256, 8, 4, 1), TQ_SPLIT(256, 2, 2, 2), TQ_SPLIT(256, 4, 2, 1),
+    TQ_SPLIT(256, 4, 3, 1),
 };
 #undef TQ_SPLIT
 #undef TQ_SPLIT_S

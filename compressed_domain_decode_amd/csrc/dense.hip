@@ -199,6 +199,17 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
 
 // ---------------------------------------------------------------- attend
 
+// Rotation entries: m_K[i][j] and m_V[j][i]. For Walsh-Hadamard codecs
+// m = H diag(sigma) with H_ij = (-1)^popcount(i & j), so an entry is a sign.
+__device__ __forceinline__ double rot_k(const DenseAttendArgs& a, int i, int j) {
+  if (a.wht) return ((__popc(i & j) + (a.wht_k.bits[j >> 5] >> (j & 31))) & 1) ? -1.0 : 1.0;
+  return a.mt_k[(size_t)j * a.dim + i];
+}
+__device__ __forceinline__ double rot_v(const DenseAttendArgs& a, int j, int i) {
+  if (a.wht) return ((__popc(i & j) + (a.wht_v.bits[i >> 5] >> (i & 31))) & 1) ? -1.0 : 1.0;
+  return a.m_v[(size_t)j * a.dim + i];
+}
+
 // Grid (splits, n_kv_heads, batch); nw = blockDim.x / 64 wavefronts take the
 // range's 64-token tiles in turn and merge at the end; one partial
 // (m, l, acc[d]) per query head and split, in base-2 units. GM and EM bound
@@ -234,7 +245,7 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
     const __half* qh = qg + (size_t)h * d;
     double acc = 0.0;
 #pragma unroll 8
-    for (int j = 0; j < d; ++j) acc += a.mt_k[(size_t)j * d + i] * (double)__half2float(qh[j]);
+    for (int j = 0; j < d; ++j) acc += rot_k(a, i, j) * (double)__half2float(qh[j]);
     s_q[h * d + i] = (float)(acc * (double)a.qscale);
   }
   __syncthreads();
@@ -383,7 +394,7 @@ __global__ __launch_bounds__(256) void dense_combine_kernel(DenseAttendArgs a) {
   for (int i = tid; i < d; i += 256) {
     double o = 0.0;
 #pragma unroll 8
-    for (int j = 0; j < d; ++j) o += a.m_v[(size_t)j * d + i] * (double)s_a[j];
+    for (int j = 0; j < d; ++j) o += rot_v(a, j, i) * (double)s_a[j];
     a.out[((size_t)b * a.n_q_heads + h) * d + i] = (float)(o / d);
   }
 }
@@ -400,7 +411,7 @@ hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr size_t kDenseLdsLimit = 160 * 1024;
+constexpr size_t kDenseLdsLimit = kDenseLdsFull;
 
 template <int GM, int EM, bool EX>
 hipError_t allow_dense_lds() {
@@ -411,7 +422,8 @@ hipError_t allow_dense_lds() {
 template <int GM, int EM, bool EX>
 hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) {
   constexpr int kMaxWaves = GM * EM > 8 ? 8 : 16;
-  constexpr size_t kLdsLimit = kDenseLdsLimit;
+  const size_t kLdsLimit = a.lds_limit < (int)kDenseLdsLimit ? (size_t)a.lds_limit
+                                                               : kDenseLdsLimit;
   const int G = a.group, d = a.dim;
   const int kw = d * a.k_bits / 32, vw = d * a.v_bits / 32;
   a.rows_words = kDTile * (kw > vw ? kw : vw);

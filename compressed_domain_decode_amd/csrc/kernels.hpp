@@ -130,6 +130,10 @@ struct DenseAttendArgs {
   const void* q;               // fp16 [batch][n_q_heads][dim]
   const double* mt_k;          // transposed K rotation (device)
   const double* m_v;           // V rotation, row-major (device)
+  // wht != 0: the rotations are H diag(sigma) of Walsh-Hadamard codecs, their
+  // +-1 entries formed from these signs (mt_k and m_v unused)
+  int wht;
+  SignArg wht_k, wht_v;
   const uint8_t* k_codes;      // [batch][n_kv_heads][max_ctx][dim*k_bits/8], 4-byte aligned
   const float* k_norms;
   const uint8_t* v_codes;
@@ -140,6 +144,7 @@ struct DenseAttendArgs {
   float* out;                  // [batch][n_q_heads][dim]
   int dim, k_bits, v_bits, n_q_heads, n_kv_heads, group, max_ctx, splits, tokens_per_split;
   int max_len;                 // host bound of lengths (<= max_ctx); lengths are clamped to it
+  int lds_limit;               // bytes of LDS a split workgroup may use
   int rows_words, wave_stride; // per-wavefront LDS region (set by the launcher)
   float qscale;                // scale * log2(e) / dim
   float k_centroids[256];      // unused entries zero
@@ -148,7 +153,10 @@ struct DenseAttendArgs {
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream);
 // Lets the dense attend kernels use up to 160 KB of LDS on the current device;
 // called at codec set-up so no launch (or graph capture) makes the call.
+// Launches of codecs set up without it keep lds_limit at 64 KB.
 hipError_t prepare_attend_dense();
+constexpr int kDenseLdsFull = 160 * 1024;
+constexpr int kDenseLdsDefault = 64 * 1024;
 float dense_qscale(float scale, int dim);
 
 // Device address of this GPU's fixed scratch array (TQ_NOALLOC_SCRATCH_BYTES

@@ -22,8 +22,22 @@
  *     Calls enqueue work on it and return without waiting.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failing call enqueues nothing. tq_last_error() then holds a message.
- *   - Supported: dim in {64, 128, 256}; bits in [1, 8]; n_q_heads a multiple
- *     of n_kv_heads with n_q_heads / n_kv_heads <= 16.
+ *   - Codecs: dim in {64, 128, 256} and bits in [1, 8] (tq_codec_init), Prod
+ *     bits in [2, 8], dense-rotation dims any multiple of 32 up to 256.
+ *   - Attend coverage. n_q_heads must be a multiple of n_kv_heads with G =
+ *     n_q_heads / n_kv_heads <= 16. tq_decode_attend serves every (K bits,
+ *     V bits) pair of one dim: the pairs below run the matrix-core kernels,
+ *     every other pair a slower kernel that forms the rotation from the
+ *     codecs' signs (same results within the attend tolerance). Matrix-core
+ *     instances, as (K bits, V bits) up to G query heads per KV head:
+ *       dim 64:  4/4 (8), 3/3 (16), 8/3 (8), 6/6 (16), 2/2, 1/1, 5/7, 4/2, 4/3 (4)
+ *       dim 128: 8/3 (16), 3/3 (16), 4/4 (8), 4/2 (8), 7/5 (8), 4/3, 2/2, 8/4,
+ *                1/1 (4)
+ *       dim 256: 2/2 (8), 4/4, 8/3, 3/3, 8/4, 4/2, 4/3 (4)
+ *     tq_decode_attend_multi (G x query tokens heads) and tq_decode_attend_mixed
+ *     use these instances only; tq_decode_attend_raw_k and
+ *     tq_decode_attend_prod list theirs. A request outside them returns
+ *     TQ_ERR_UNSUPPORTED and enqueues nothing.
  */
 #ifndef TQ_H_
 #define TQ_H_
@@ -46,10 +60,13 @@ typedef enum {
 } tq_status;
 
 /* Opaque codec: sign vector and fp32 Lloyd-Max tables for one (dim, bits, seed).
- * Immutable after init, host memory only, shareable across threads, streams,
- * devices and layers (all layers with the same triple share one codec, as in
- * the PR's "shared codecs" design note). The tables travel to the GPU inside
- * each launch's kernel arguments, so a codec holds no device memory. */
+ * Immutable after init and shareable across threads, streams and layers (all
+ * layers with the same triple share one codec, as in the PR's "shared codecs"
+ * design note). A Walsh-Hadamard or Prod codec is host memory only: its tables
+ * travel to the GPU inside each launch's kernel arguments, so it holds no
+ * device memory and serves every device. A dense-rotation codec owns device
+ * memory (its rotation) on the device that was current at
+ * tq_codec_init_dense and is used on that device only. */
 typedef struct tq_codec tq_codec;
 
 /* Build a codec. dim: head dimension (64, 128 or 256; the Hadamard rotation
@@ -222,9 +239,13 @@ size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int d
  *               256-byte aligned; its contents need not be initialised. It
  *               holds one partial per (sequence, query head, split).
  * Two kernels are enqueued: split attend (the query rotation runs in its
- * prologue) and combine + inverse rotation. Results agree with softmax attention over the dequantised cache
- * (computed in fp64) to about 1e-5 absolute for unit-scale inputs; fp32 sums
- * in a different order make the low bits differ from any serial evaluation.
+ * prologue) and combine + inverse rotation. Every (K bits, V bits) pair of
+ * one dim is served (the coverage list at the top of this header names the
+ * matrix-core pairs; the others take the slower sign-formed rotation kernels).
+ * Results agree with softmax attention over the dequantised cache (computed
+ * in fp64) to about 1e-5 absolute for unit-scale inputs, and within 2e-3 for
+ * the tested workloads; sums in a different order make the low bits differ
+ * from any serial evaluation.
  */
 tq_status tq_decode_attend(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
                            int batch, int n_q_heads, int n_kv_heads,
@@ -272,9 +293,9 @@ tq_status tq_decode_attend_noalloc(const tq_codec* kc, const tq_codec* vc, const
  *   Every other argument is as for tq_decode_attend, with a workspace of at
  *   least tq_attend_multi_workspace_bytes(...) bytes. With n_query_tokens == 1
  *   this is tq_decode_attend.
- * Supported while (n_q_heads / n_kv_heads) * n_query_tokens <= 16 and a kernel
- * is instantiated for that many heads per KV head (TQ_ERR_UNSUPPORTED
- * otherwise).
+ * Supported while (n_q_heads / n_kv_heads) * n_query_tokens <= 16 and a
+ * matrix-core instance of the header's list covers that many heads per KV
+ * head (TQ_ERR_UNSUPPORTED otherwise).
  */
 tq_status tq_decode_attend_multi(const tq_codec* kc, const tq_codec* vc, const void* q_fp16,
                                  int batch, int n_query_tokens, int n_q_heads, int n_kv_heads,
@@ -324,8 +345,8 @@ tq_status tq_decode_attend_mixed(const tq_codec* kc, const tq_codec* vc, const v
  *           aligned.
  *   v_codes / v_norms, lengths, max_len, scale, out, workspace: as for
  *           tq_decode_attend (workspace size tq_attend_workspace_bytes).
- * Kernels exist for dim 128 with 2- or 4-bit V (up to 8 query heads per KV
- * head) and dim 64 with 4-bit V (up to 8); TQ_ERR_UNSUPPORTED otherwise.
+ * Kernels exist for dim 64 and 128 with 4-bit V (up to 8 query heads per KV
+ * head) or 2-bit V (up to 4); TQ_ERR_UNSUPPORTED otherwise.
  */
 tq_status tq_decode_attend_raw_k(const tq_codec* vc, const void* q_fp16, int batch,
                                  int n_q_heads, int n_kv_heads, const void* k_fp16,

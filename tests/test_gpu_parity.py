@@ -5,8 +5,10 @@ exact, stronger than the required 1e-5 relative); decode-attend outputs within
 2e-3 max-abs of the oracle's fp64 result. Oracle inputs never come from the
 HIP path: the oracle encodes its own copy of every cache it attends over.
 """
+import concurrent.futures as cf
 import functools
 import math
+import os
 import sys
 
 import numpy as np
@@ -74,6 +76,22 @@ def gpu_attend(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np, scale=N
 
 def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def oracle_threads():
+    """Threads for oracle work over independent units (the C oracle runs with
+    the GIL released): the cores this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def map_units(fn, units):
+    """fn over every unit on oracle_threads() threads; the first failure raises."""
+    with cf.ThreadPoolExecutor(oracle_threads()) as ex:
+        return list(ex.map(fn, units))
 
 
 # ------------------------------------------------------------------ encode
@@ -239,6 +257,8 @@ SUPPORTED_SMALL = [
     (128, 8, 4, 4), (128, 4, 4, 8), (128, 8, 3, 8), (128, 4, 2, 1), (128, 3, 3, 2), (128, 8, 3, 6),
     (128, 1, 1, 4), (128, 7, 5, 6), (128, 3, 3, 5), (128, 4, 2, 8),
     (256, 4, 4, 4), (256, 8, 3, 4), (256, 3, 3, 2), (256, 8, 4, 1), (256, 2, 2, 8),
+    # PR #232's turbo4v2 / turbo4v3 at head dims 64 and 256
+    (64, 4, 2, 3), (64, 4, 3, 4), (256, 4, 2, 4), (256, 4, 3, 2),
 ]
 
 
@@ -250,6 +270,40 @@ def test_attend_matches_oracle_small(d, kb, vb, G):
     print(f"  max abs err {err:.3e}", flush=True)
     assert np.isfinite(got).all()
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_attend_every_bit_width_pair(d):
+    """Every (K bits, V bits) pair the codecs accept is attended: pairs with a
+    matrix-core instance run it, the others the rotation-matrix kernels with
+    m = H diag(sigma) built from the codecs' signs. Ragged lengths with a
+    single-row sequence, three query heads per KV head."""
+    worst = 0.0
+    for kb in range(1, 9):
+        for vb in range(1, 9):
+            announce(f"attend every pair d={d} K{kb} V{vb}")
+            got, want = _attend_case(d, kb, vb, 3, lengths=[150, 1], seed=d + 8 * kb + vb)
+            assert np.isfinite(got).all(), (kb, vb)
+            err = float(np.abs(got - want).max())
+            assert err <= ATOL, (kb, vb, err)
+            worst = max(worst, err)
+    print(f"  d={d}: worst max abs err {worst:.3e} over 64 pairs", flush=True)
+
+
+@pytest.mark.parametrize("d,kb,vb,G,lengths", [
+    (256, 8, 8, 16, [3000, 1234]),   # 16 query heads per KV head, several splits
+    (128, 8, 8, 2, [2500, 64]),      # 8-bit V
+    (64, 8, 8, 1, [4100, 0]),        # an empty sequence: zero rows
+    (128, 6, 5, 7, [777, 1, 300]),
+])
+def test_attend_fallback_pairs(d, kb, vb, G, lengths):
+    announce(f"attend fallback d={d} K{kb} V{vb} G={G} lengths={lengths}")
+    got, want = _attend_case(d, kb, vb, G, lengths=lengths, seed=5 * d + kb + vb + G)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= ATOL
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert np.all(got[b] == 0.0)
 
 
 @pytest.mark.parametrize("d,kb,vb,G", [(128, 8, 3, 4), (64, 3, 3, 8), (128, 4, 2, 3)])
@@ -340,9 +394,10 @@ def test_attend_large_scale_inputs():
 
 
 @pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
-def test_attend_workload_full_size_sampled(name):
-    """Full-size cache and launch configuration of each workload; sampled
-    (b, h) rows against the oracle, which encodes the sampled KV heads itself."""
+def test_attend_workload_full_size(name):
+    """Full-size cache and launch configuration of each workload; every
+    (sequence, KV head) unit against the oracle, which encodes each unit's
+    cache itself (those codes checked byte for byte against the GPU cache)."""
     wl = workloads.WORKLOADS[name]
     announce(f"attend full size {name}")
     inp = workloads.generate(wl)
@@ -351,27 +406,26 @@ def test_attend_workload_full_size_sampled(name):
     kc, kn = gpu_encode_cache(gk, to_dev(inp.k))
     vc, vn = gpu_encode_cache(gv, to_dev(inp.v))
     got = gpu_attend(gk, gv, inp.q, kc, kn, vc, vn, inp.lengths)
-    B, Hq = wl.batch, wl.n_q_heads
+    kc_h, vc_h = kc.cpu().numpy(), vc.cpu().numpy()
+    del kc, kn, vc, vn
     G = wl.group
-    rng = np.random.default_rng(123)
-    if B * Hq <= 8:
-        pairs = [(b, h) for b in range(B) for h in range(Hq)]
-    else:
-        pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(3)]
-        pairs.append((B - 1, Hq - 1))
-    worst = 0.0
-    for b, h in pairs:
-        g = h // G
+
+    def unit(bg):
+        b, g = bg
         L = int(inp.lengths[b])
         okc, okn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L])
         ovc, ovn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L])
-        assert kc[b, g, :L].cpu().numpy().tobytes() == okc.tobytes()
-        assert vc[b, g, :L].cpu().numpy().tobytes() == ovc.tobytes()
+        assert kc_h[b, g, :L].tobytes() == okc.tobytes(), bg
+        assert vc_h[b, g, :L].tobytes() == ovc.tobytes(), bg
         want = oracle.attend(ok, ov, inp.q[b:b + 1, g * G:(g + 1) * G], okc, okn, ovc, ovn,
                              np.array([L], np.int32))
-        err = np.abs(got[b, g * G:(g + 1) * G] - want[0]).max()
-        worst = max(worst, err)
-    print(f"  {name}: worst max-abs err {worst:.3e} over {len(pairs)} sampled rows", flush=True)
+        return float(np.abs(got[b, g * G:(g + 1) * G] - want[0]).max())
+
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)]
+    errs = map_units(unit, units)
+    worst = max(errs)
+    print(f"  {name}: worst max-abs err {worst:.3e} over all {len(units)} units "
+          f"({wl.batch * wl.n_q_heads} rows)", flush=True)
     assert np.isfinite(got).all()
     assert worst <= ATOL
 
@@ -442,9 +496,9 @@ def test_attend_multi_one_token_equals_single_decode():
 
 
 @pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
-def test_attend_multi_workload_full_size_sampled(name):
+def test_attend_multi_workload_full_size(name):
     """The most query tokens (4, else 2) a multi-token kernel covers for each
-    workload at full size; sampled (sequence, KV head) units against the oracle."""
+    workload at full size; every (sequence, KV head) unit against the oracle."""
     wl = workloads.WORKLOADS[name]
     G = wl.n_q_heads // wl.n_kv_heads
     gk, ok = codecs(wl.dim, wl.k_bits, wl.codec_seed)
@@ -467,15 +521,18 @@ def test_attend_multi_workload_full_size_sampled(name):
                 raise
     assert got is not None, "no multi-token kernel for this workload"
     del kc, kn, vc, vn
-    units = [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)]
-    pick = [units[i] for i in rng.choice(len(units), size=min(3, len(units)), replace=False)]
-    for b, g in pick:
+
+    def unit(bg):
+        b, g = bg
         L = int(inp.lengths[b])
         okc, okn, _ = oracle.encode(ok, inp.k[b:b + 1, g:g + 1, :L])
         ovc, ovn, _ = oracle.encode(ov, inp.v[b:b + 1, g:g + 1, :L])
         qs = q[b:b + 1, :, g * G:(g + 1) * G]
         want = oracle.attend_causal_queries(ok, ov, qs, okc, okn, ovc, ovn, np.array([L]))
-        assert np.max(np.abs(got[b:b + 1, :, g * G:(g + 1) * G] - want)) <= ATOL
+        return float(np.max(np.abs(got[b:b + 1, :, g * G:(g + 1) * G] - want)))
+
+    errs = map_units(unit, [(b, g) for b in range(wl.batch) for g in range(wl.n_kv_heads)])
+    assert max(errs) <= ATOL
 
 
 # ------------------------------------------------------------------ packed + raw fp16 rows
@@ -609,7 +666,7 @@ def test_attend_mixed_raw_rows_past_length_unused():
 
 def test_attend_mixed_workload_sink_prefix_full_size():
     """The 32K K8/V3 workload with its first 128 tokens kept as fp16 rows (the
-    guide's --kv-min-tokens 128): sampled KV heads against the oracle."""
+    guide's --kv-min-tokens 128): every KV head against the oracle."""
     wl = workloads.WORKLOADS["llama8b_32k_k8v3"]
     announce(f"attend mixed full size {wl.name} sink 128")
     G = wl.n_q_heads // wl.n_kv_heads
@@ -625,15 +682,17 @@ def test_attend_mixed_workload_sink_prefix_full_size():
     got = gpu_attend_mixed(gk, gv, inp.q, kc, kn, vc, vn, lengths, rk, rv,
                            np.full(wl.batch, S, dtype=np.int32))
     del kc, kn, vc, vn
-    rng = np.random.default_rng(8)
-    for g in rng.choice(wl.n_kv_heads, size=2, replace=False):
+
+    def unit(g):
         L = int(lengths[0])
         okc, okn, _ = oracle.encode(ok, inp.k[0:1, g:g + 1, S:S + L])
         ovc, ovn, _ = oracle.encode(ov, inp.v[0:1, g:g + 1, S:S + L])
         want = oracle.attend_mixed(ok, ov, inp.q[0:1, g * G:(g + 1) * G], okc, okn, ovc, ovn,
                                    np.array([L]), rk[0:1, g:g + 1], rv[0:1, g:g + 1],
                                    np.array([S]))
-        assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
+        return float(np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)))
+
+    assert max(map_units(unit, range(wl.n_kv_heads))) <= ATOL
 
 
 # ------------------------------------------------------------------ raw fp16 keys
@@ -653,7 +712,8 @@ def gpu_attend_raw_k(vc, q_np, k_dev, vcodes, vnorms, lengths_np, max_len=None):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("d,vb,G", [(128, 4, 4), (128, 2, 3), (128, 4, 8), (64, 4, 2), (64, 4, 8)])
+@pytest.mark.parametrize("d,vb,G", [(128, 4, 4), (128, 2, 3), (128, 4, 8), (64, 4, 2), (64, 4, 8),
+                                    (64, 2, 3)])
 def test_attend_raw_k_matches_oracle(d, vb, G):
     """Raw fp16 keys with packed values (turbo0v4 / turbo0v2) over ragged lengths
     spanning several tiles and splits, a length-1 and an empty sequence."""
@@ -675,9 +735,9 @@ def test_attend_raw_k_matches_oracle(d, vb, G):
     assert np.all(got[3] == 0.0)
 
 
-def test_attend_raw_k_llama8b_shape_32k_sampled():
+def test_attend_raw_k_llama8b_shape_32k():
     """32K context, 32/8 heads, d=128, fp16 K and 4-bit V (turbo0v4), the 32K
-    workload's synthetic K/V: sampled KV heads against the oracle."""
+    workload's synthetic K/V: every KV head against the oracle."""
     wl = workloads.WORKLOADS["llama8b_32k_k8v3"]
     announce("attend raw K 32K turbo0v4")
     G = wl.n_q_heads // wl.n_kv_heads
@@ -686,13 +746,15 @@ def test_attend_raw_k_llama8b_shape_32k_sampled():
     vcodes, vnorms = gpu_encode_cache(gv, to_dev(inp.v))
     got = gpu_attend_raw_k(gv, inp.q, to_dev(inp.k), vcodes, vnorms, inp.lengths)
     del vcodes, vnorms
-    rng = np.random.default_rng(4)
-    for g in rng.choice(wl.n_kv_heads, size=2, replace=False):
+
+    def unit(g):
         L = int(inp.lengths[0])
         ovc, ovn, _ = oracle.encode(ov, inp.v[0:1, g:g + 1, :L])
         want = oracle.attend_raw_k(ov, inp.q[0:1, g * G:(g + 1) * G], inp.k[0:1, g:g + 1, :L],
                                    ovc, ovn, np.array([L]))
-        assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
+        return float(np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)))
+
+    assert max(map_units(unit, range(wl.n_kv_heads))) <= ATOL
 
 
 # ------------------------------------------------------------------ TurboQuant-Prod keys
@@ -780,10 +842,10 @@ def test_attend_prod_matches_oracle(d, kb, vb, G):
     assert np.all(got[3] == 0.0)
 
 
-def test_attend_prod_llama8b_shape_32k_sampled():
+def test_attend_prod_llama8b_shape_32k():
     """32K context, 32/8 heads, d=128, 4-bit Prod keys (3-bit codes + sketch)
-    and 4-bit values over the 32K workload's synthetic K/V: sampled KV heads
-    against the oracle, the Prod encode of those heads checked bit-exact."""
+    and 4-bit values over the 32K workload's synthetic K/V: every KV head
+    against the oracle, the Prod encode of each head checked bit-exact."""
     wl = workloads.WORKLOADS["llama8b_32k_k8v3"]
     announce("attend prod 32K k4(prod) v4")
     G = wl.n_q_heads // wl.n_kv_heads
@@ -801,17 +863,20 @@ def test_attend_prod_llama8b_shape_32k_sampled():
                              lengths_d, T, 1.0 / math.sqrt(wl.dim), out, ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    rng = np.random.default_rng(6)
-    for g in rng.choice(Hkv, size=2, replace=False):
+    kc_h, ks_h, kr_h = kcodes.cpu().numpy(), ksk.cpu().numpy(), krn.cpu().numpy()
+
+    def unit(g):
         L = int(inp.lengths[0])
         okc, osk, okn, okr = oracle.encode_prod(ok, inp.k[0:1, g:g + 1, :L])
-        assert kcodes[0, g, :L].cpu().numpy().tobytes() == okc.tobytes()
-        assert ksk[0, g, :L].cpu().numpy().tobytes() == osk.tobytes()
-        assert krn[0, g, :L].cpu().numpy().tobytes() == okr.tobytes()
+        assert kc_h[0, g, :L].tobytes() == okc.tobytes(), g
+        assert ks_h[0, g, :L].tobytes() == osk.tobytes(), g
+        assert kr_h[0, g, :L].tobytes() == okr.tobytes(), g
         ovc, ovn, _ = oracle.encode(ov, inp.v[0:1, g:g + 1, :L])
         want = oracle.attend_prod(ok, ov, inp.q[0:1, g * G:(g + 1) * G], okc, osk, okn, okr,
                                   ovc, ovn, np.array([L]))
-        assert np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)) <= ATOL
+        return float(np.max(np.abs(got[0:1, g * G:(g + 1) * G] - want)))
+
+    assert max(map_units(unit, range(Hkv))) <= ATOL
 
 
 # ------------------------------------------------------------ two-phase cache
