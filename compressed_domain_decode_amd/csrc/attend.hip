@@ -207,6 +207,9 @@ __device__ __forceinline__ uint32_t field_at8(const uint32_t (&w)[NW]) {
 // never has a bank conflict, whatever the codes. A lookup address is
 // (code << 8) | lane_offset.
 constexpr int kVPad = 4;  // dwords of padding around a wavefront's staged V rows
+// Fourth word of a raw buffer resource on CDNA (32-bit data format, no
+// swizzle, no stride): loads past the resource's byte count read zero.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int D_, int BK_, int BV_, int NHG_, int WAVES_>
 struct CfgBase {
@@ -247,10 +250,14 @@ struct CfgBase {
   static constexpr int QS_BYTES = (PROD ? 2 : 1) * 4 * NHG * D * 4 + 4 * NHG * 4;
   // first-tile arrival flags and the workers' tables-ready counter
   static constexpr int GATE_BYTES = ((WAVES + 1) * 4 + 15) / 16 * 16;
-  static constexpr int MAIN_BYTES =
-      VT_BYTES + KT_BYTES + WAVES * (VS_BYTES + WB_BYTES) + QS_BYTES + GATE_BYTES;
+  // The V stages live in an LDS array of their own: the compiler then knows
+  // that reads of the tables, weights and queries cannot touch rows still in
+  // flight from HBM, and waits for those only before reading a stage.
+  static constexpr int STAGE_BYTES = WAVES * VS_BYTES;
+  static constexpr int MAIN_BYTES = VT_BYTES + KT_BYTES + WAVES * WB_BYTES + QS_BYTES + GATE_BYTES;
   static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * NHG * D) * 4;
-  static constexpr int LDS_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+  static constexpr int SHARED_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+  static constexpr int LDS_BYTES = SHARED_BYTES + STAGE_BYTES;  // the workgroup's whole LDS
   // value accumulators per head group and half (hi or lo weights): one per
   // coordinate a lane owns; two (even and odd token pairs) when it owns one
   static constexpr int NACC = (VPAIR ? 2 * NVS : NVS) < 2 ? 2 : (VPAIR ? 2 * NVS : NVS);
@@ -404,10 +411,13 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     ProdArgs pa) {
   constexpr int D = C::D, NHG = C::NHG, WAVES = C::WAVES, E = C::E;
   constexpr int RKW = C::RKW, RVW = C::RVW;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::SHARED_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t vstages[C::STAGE_BYTES / 4];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wavefront index is uniform: kept in a scalar register, so that the
+  // tile loop's control and the stage address need no vector registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t_begin = split * tokens_per_split;
   // rows [t_begin, t_host) lie inside the cache allocation whatever the
   // device lengths are (max_len <= max_ctx)
@@ -422,10 +432,9 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   unsigned char* vt = lds;
   unsigned char* kt = lds + C::VT_BYTES;
-  uint32_t* vstage = (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + wave * C::VS_BYTES);
-  uint32_t* wbuf =
-      (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::VS_BYTES + wave * C::WB_BYTES);
-  float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * (C::VS_BYTES + C::WB_BYTES));
+  uint32_t* vstage = vstages + wave * (C::VS_BYTES / 4);
+  uint32_t* wbuf = (uint32_t*)(lds + C::VT_BYTES + C::KT_BYTES + wave * C::WB_BYTES);
+  float* wq = (float*)(lds + C::VT_BYTES + C::KT_BYTES + WAVES * C::WB_BYTES);
   float* qmax = wq + (C::PROD ? 2 : 1) * 4 * NHG * D;  // [4 NHG] largest |q^| per virtual head
   int* gate = (int*)(qmax + 4 * NHG);
 
@@ -440,40 +449,53 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   // ---- a tile's V rows: copied from HBM into this wavefront's LDS stage
   //      in their own layout (rows contiguous), each instruction a coalesced
   //      1 KB (or 256 B) piece; pieces past row `last` re-read the last
-  //      valid piece (always in bounds; those rows are never used)
+  //      valid piece (always in bounds; those rows are never used). The
+  //      copies are buffer loads over a resource that spans exactly the
+  //      tile's valid rows: unlike the flat-encoded global-to-LDS form they
+  //      leave the compiler's count of the wavefront's other loads exact, so
+  //      a wait for the next tile's K row does not also wait for these rows.
   auto load_v = [&](int tile, int last) __attribute__((always_inline)) {
     const uint32_t* src = vbase + (long long)tile * RVW;
     auto* dst = (__attribute__((address_space(3))) uint32_t*)(vstage + kVPad);
     if constexpr (C::VDMA16) {
       const int valid = (last - tile + 1) * (RVW / 4);  // 16-byte pieces
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, valid * 16, kBufferWord3);
 #pragma unroll
       for (int i = 0; i < C::VDMA_OPS; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src + 4 * min(64 * i + lane, valid - 1)),
-                                         (__attribute__((address_space(3))) void*)(dst + 256 * i),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + 256 * i), 16,
+            16 * min(64 * i + lane, valid - 1), 0, 0, 0);
     } else {
       const int valid = (last - tile + 1) * RVW;  // dwords
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, valid * 4, kBufferWord3);
 #pragma unroll
       for (int i = 0; i < C::VDMA_OPS; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src + min(64 * i + lane, valid - 1)),
-                                         (__attribute__((address_space(3))) void*)(dst + 64 * i),
-                                         4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + 64 * i), 4,
+            4 * min(64 * i + lane, valid - 1), 0, 0, 0);
     }
   };
   // ---- tile registers: this lane's token's norms and K row. Lanes past
   //      `last` load row `last` instead (always in bounds); their scores are
   //      masked to -inf and their weights are 0, so the rows never contribute.
-  auto load_k = [&](int tile, int last, TileRegs<C>& r) __attribute__((always_inline)) {
+  //      The norms and the row are requested separately: inside the tile
+  //      loop the next tile's row goes out once the scores have consumed the
+  //      current one, its norms once the softmax has consumed the current
+  //      ones, so that no register holding a current value is also the
+  //      target of a load in flight (which would cost a wait for it).
+  auto load_norms = [&](int tile, int last, TileRegs<C>& r) __attribute__((always_inline)) {
     const int t = min(tile + lane, last);
-    const uint32_t* kr = kbase + (long long)t * RKW;
-    // V norm first, then K norm and row: vector loads complete in order, so
-    // the scores can start on the first pieces of the K row while the rest
-    // is in flight
     r.nv = vnb[t];
     if constexpr (C::KRAW)
       r.nk = 1.f;
     else
       r.nk = knb[t];
+  };
+  auto load_krow = [&](int tile, int last, TileRegs<C>& r) __attribute__((always_inline)) {
+    const int t = min(tile + lane, last);
+    const uint32_t* kr = kbase + (long long)t * RKW;
     if constexpr (C::PROD) {
       r.rn = rnb[t];
       const uint32_t* sr = skb + (long long)t * C::SKW;
@@ -498,9 +520,13 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
     }
   };
+  // a first tile: V rows, norms, then the K row (vector loads complete in
+  // order, so the scores can start on the first pieces of the K row while
+  // the rest is in flight)
   auto load_tile = [&](int tile, int last, TileRegs<C>& r) __attribute__((always_inline)) {
     load_v(tile, last);
-    load_k(tile, last, r);
+    load_norms(tile, last, r);
+    load_krow(tile, last, r);
   };
 
   // ---- prologue. With more wavefronts than the gate depth, the ungated
@@ -788,9 +814,14 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   asm("" : "+v"(voff_y));
   asm("" : "+s"(vmask_y));
 
-  // One tile: scores, online softmax, values. `r` is consumed and refilled
-  // with the wavefront's next tile as soon as its rows have been used.
-  auto process = [&](int tile, TileRegs<C>& r) __attribute__((always_inline)) {
+  // One tile: scores, online softmax, values. With MORE (another tile of
+  // this wavefront follows) `r` is refilled with the next tile as soon as
+  // its rows have been used, and the next V rows are requested once the
+  // stage has been read. MORE is a compile-time property of the call, so
+  // every load of a tile is issued on one path: the compiler then counts the
+  // loads in flight exactly and waits for each register only as long as it
+  // must.
+  auto process = [&](int tile, TileRegs<C>& r, auto MORE) __attribute__((always_inline)) {
 
     // ---- scores on the matrix cores: per coordinate pair (raw keys: per
     //      four coordinates) one product with the high and one with the low
@@ -886,11 +917,12 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     const bool live = tile + lane < t_end;
     const float nv_cur = live ? r.nv : 0.f;
     const float nk_cur = r.nk;
-    // the K row is consumed: refill the registers with this wavefront's next
-    // tile (its V rows follow once this tile's stage has been read)
+    // the K row is consumed: refill it with this wavefront's next tile's
+    // (its norms follow after the softmax, its V rows once this tile's stage
+    // has been read)
     const int ahead = tile + kStride;
-    const bool more = ahead < t_end;
-    if (more) load_k(ahead, t_end - 1, r);
+    constexpr bool more = decltype(MORE)::value;
+    if constexpr (more) load_krow(ahead, t_end - 1, r);
 
     // V norm scale: every norm below 2^ev (rare: usually the first tile only)
     if (__ballot(__builtin_bit_cast(int, nv_cur) >= ((ev + 127) << 23)) != 0ull) {
@@ -940,11 +972,12 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
       *(uint4*)(wbuf + (lane * NHG + hg) * 4) = uint4{w[0], w[1], w[2], w[3]};
     }
+    if constexpr (more) load_norms(ahead, t_end - 1, r);
     wave_lds_sync();
 
     // this tile's V rows are in the stage: they were requested before its K
     // row, whose loads have completed (only the refill may be in flight)
-    if (more)
+    if constexpr (more)
       wait_vmcnt<k_loads<C>()>();
     else
       wait_vmcnt<0>();
@@ -1048,17 +1081,19 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       });
     }
     wave_lds_sync();
-    if (more) {
+    if constexpr (more) {
       // every read of the stage has returned before it is overwritten
       wait_lgkmcnt0();
       load_v(ahead, t_end - 1);
     }
   };
 
-  // the first tile is peeled off the loop so that its register waits follow
-  // the order its loads were issued in
-  if (has_tile) process(tile0, ra);
-  for (int tile = tile0 + kStride; tile < t_end; tile += kStride) process(tile, ra);
+  // every tile but the wavefront's last prefetches the next one
+  if (has_tile) {
+    int tile = tile0;
+    for (; tile + kStride < t_end; tile += kStride) process(tile, ra, std::true_type{});
+    process(tile, ra, std::false_type{});
+  }
 
   // ---- merge the wavefronts of this workgroup and write the split partial:
   //      every wavefront stores its maxima, sums and accumulators (brought to
