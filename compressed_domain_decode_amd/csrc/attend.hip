@@ -49,8 +49,8 @@
 //    The online softmax moves its running maximum only when a tile's
 //    maximum exceeds it by more than 2^8, so the rescale is rare.
 //    Centroid tables live in LDS replicated once per bank (a 256-byte row
-//    per code: 32 copies of an 8-byte code-pair entry or 64 copies of a
-//    4-byte entry), so a lookup is conflict-free whatever the codes; codes of
+//    per code: 64 copies of a 4-byte entry, or 32 of an 8-byte code-pair
+//    entry), so a lookup is conflict-free whatever the codes; codes of
 //    <= 3 bits are looked up two coordinates at a time. The query rotation q^ = (scale log2 e / d)
 //    H (sigma_K (.) q) is done by every wavefront in its prologue.
 //    The wavefronts merge (max, sum, accumulator) through LDS and write one
@@ -201,11 +201,21 @@ __device__ __forceinline__ uint32_t field_at8(const uint32_t (&w)[NW]) {
   }
 }
 
-// Centroid tables live in LDS as one 256-byte row per code (or code pair):
-// 64 copies of a 4-byte entry (hi, lo) or 32 copies of an 8-byte pair entry
-// (hi, lo, hi', lo'), so that every lane reads its own copy and a lookup
-// never has a bank conflict, whatever the codes. A lookup address is
-// (code << 8) | lane_offset.
+// Centroid tables live in LDS as one 256-byte row per code (or code pair),
+// so that every lane reads its own copy and a lookup never has a bank
+// conflict, whatever the codes. A wave64 LDS read is served 32 lanes at a
+// time over 32 banks of 4 bytes:
+// - 4-byte entries (hi, lo): 64 copies, lane l at dword l;
+// - K pair entries (hi, lo, hi', lo'), read as one 8-byte access into the
+//   operand pair they feed: 32 interleaved copies, lane l at dwords
+//   2 (l % 32) and 2 (l % 32) + 1 (8 bytes per lane fill the 32 banks twice
+//   per pass, which is the access's own width, not a conflict);
+// - V pair entries, read as two 4-byte accesses that feed two different
+//   operands: 32 copies of the first coordinate's (hi, lo) in dwords 0..31
+//   and 32 of the second's in 32..63, lane l at dwords l % 32 and
+//   32 + l % 32 (interleaved, each 4-byte access would put two lanes of a
+//   pass on every even or odd bank).
+// A lookup address is (code << 8) | lane_offset.
 constexpr int kVPad = 4;  // dwords of padding around a wavefront's staged V rows
 // Fourth word of a raw buffer resource on CDNA (32-bit data format, no
 // swizzle, no stride): loads past the resource's byte count read zero.
@@ -255,7 +265,7 @@ struct CfgBase {
   // flight from HBM, and waits for those only before reading a stage.
   static constexpr int STAGE_BYTES = WAVES * VS_BYTES;
   static constexpr int MAIN_BYTES = VT_BYTES + KT_BYTES + WAVES * WB_BYTES + QS_BYTES + GATE_BYTES;
-  static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 2 + WAVES * 4 * NHG * D) * 4;
+  static constexpr int MERGE_BYTES = (WAVES * 4 * NHG * 3 + 2 * 4 * NHG + WAVES * 4 * NHG * D) * 4;
   static constexpr int SHARED_BYTES = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
   static constexpr int LDS_BYTES = SHARED_BYTES + STAGE_BYTES;  // the workgroup's whole LDS
   // value accumulators per head group and half (hi or lo weights): one per
@@ -590,18 +600,23 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   if (worker) {
     // table rows of (hi, lo) entries
-    auto fill = [&](unsigned char* tab, int rows, bool pair, float cs, const float (&ce)[2], int u) {
+    // (16-byte piece i of the table: row i / 16, piece i % 16 of that row)
+    auto fill = [&](unsigned char* tab, int rows, bool pair, bool halves, float cs,
+                    const float (&ce)[2], int u) {
       const int i = wtid + u * 64 * kWorkers;
       if (i < rows * 16) {
         const uint32_t a = split_hl(ce[0] * cs);
         const uint32_t bb = pair ? split_hl(ce[1] * cs) : a;
-        ((uint4*)tab)[i] = pair ? uint4{a, bb, a, bb} : uint4{a, a, a, a};
+        if (halves)  // pieces 0..7: the first coordinate's entry, 8..15: the second's
+          ((uint4*)tab)[i] = (i & 15) < 8 ? uint4{a, a, a, a} : uint4{bb, bb, bb, bb};
+        else
+          ((uint4*)tab)[i] = uint4{a, bb, a, bb};
       }
     };
 #pragma unroll
-    for (int u = 0; u < kVEnt; ++u) fill(vt, kVRows, C::VPAIR, tabs.v_scale, vce[u], u);
+    for (int u = 0; u < kVEnt; ++u) fill(vt, kVRows, C::VPAIR, C::VPAIR, tabs.v_scale, vce[u], u);
 #pragma unroll
-    for (int u = 0; u < kKEnt; ++u) fill(kt, kKRows, C::KPAIR, tabs.k_scale, kce[u], u);
+    for (int u = 0; u < kKEnt; ++u) fill(kt, kKRows, C::KPAIR, false, tabs.k_scale, kce[u], u);
 
     // rotated queries: worker w rotates heads w, w + kWorkers, ... into LDS
     // and records each one's largest magnitude
@@ -789,7 +804,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   bool seen = false;  // a tile has been processed (the accumulators may be nonzero)
 
   const uint32_t koff = C::KPAIR ? (uint32_t)(lane & 31) << 3 : (uint32_t)lane << 2;
-  const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 31) << 3 : (uint32_t)lane << 2;
+  const uint32_t voff = C::VPAIR ? (uint32_t)(lane & 31) << 2 : (uint32_t)lane << 2;
   constexpr uint32_t KMASK = ((1u << C::KF) - 1u) << 8;
   constexpr uint32_t VMASK = ((1u << C::VF) - 1u) << 8;
 
@@ -810,7 +825,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     asm("" : "+v"(va1[k]));
     vsh[k] = o & 31;
   }
-  uint32_t voff_y = voff + 4, vmask_y = VMASK;  // opaque copies: one v_and_or per address
+  uint32_t voff_y = voff + 128, vmask_y = VMASK;  // opaque copies: one v_and_or per address
   asm("" : "+v"(voff_y));
   asm("" : "+s"(vmask_y));
 
@@ -1097,10 +1112,11 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 
   // ---- merge the wavefronts of this workgroup and write the split partial:
   //      every wavefront stores its maxima, sums and accumulators (brought to
-  //      true scale), then thread (virtual head, coordinate) folds the
-  //      wavefronts with the factors 2^(m_w - M), M their maximum (a
-  //      wavefront that saw no row has the finite sentinel maximum, so it
-  //      weighs 0 next to one that did)
+  //      true scale); one lane per virtual head then takes the maximum M
+  //      over the wavefronts, their factors 2^(m_w - M) and the folded sum
+  //      (a wavefront that saw no row has the finite sentinel maximum, so it
+  //      weighs 0 next to one that did), and thread (virtual head,
+  //      coordinate) folds the accumulators with those factors
   const float aunscale = exp2i(ev - kWeightExp) / tabs.v_scale;
   v4f accf[C::NACC][NHG];
 #pragma unroll
@@ -1113,17 +1129,19 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   }
   __syncthreads();  // all wavefronts are done with tables and buffers
   constexpr int NV = 4 * NHG;                   // virtual-head slots per wavefront
-  float* mbuf = (float*)lds;                    // [WAVES][NV] maxima
-  float* lbuf = mbuf + WAVES * NV;              // [WAVES][NV] sums
-  float* abuf = lbuf + WAVES * NV;              // [WAVES][NV][D] accumulators
+  float* mbuf = (float*)lds;                    // [NV][WAVES] maxima
+  float* lbuf = mbuf + NV * WAVES;              // [NV][WAVES] sums
+  float* fbuf = lbuf + NV * WAVES;              // [NV][WAVES] factors 2^(m_w - M)
+  float* tot = fbuf + NV * WAVES;               // [NV][2] M and the folded sum
+  float* abuf = tot + 2 * NV;                   // [WAVES][NV][D] accumulators
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float lsum = wave_sum(l_run[hg][v]);
       if (lane == 0) {
-        mbuf[wave * NV + 4 * hg + v] = m_run[hg][v];
-        lbuf[wave * NV + 4 * hg + v] = lsum;
+        mbuf[(4 * hg + v) * WAVES + wave] = m_run[hg][v];
+        lbuf[(4 * hg + v) * WAVES + wave] = lsum;
       }
       float* dst = abuf + (wave * NV + 4 * hg + v) * D;
       if constexpr (C::VPAIR) {
@@ -1138,23 +1156,36 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       }
     }
   __syncthreads();
+  if (wave == 0 && lane < GV) {
+    const int h = lane;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[h * WAVES + w]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      // m_w - M <= 0: the hardware exponential (0 far below; 1 for the maximum)
+      const float f = __builtin_amdgcn_exp2f(mbuf[h * WAVES + w] - M);
+      fbuf[h * WAVES + w] = f;
+      L += f * lbuf[h * WAVES + w];
+    }
+    tot[2 * h] = M;
+    tot[2 * h + 1] = L;
+  }
+  __syncthreads();
   const int S = gridDim.x;
+  // D >= 64: a wavefront's threads share one virtual head
   for (int idx = threadIdx.x; idx < NV * D; idx += 64 * WAVES) {
     const int h = idx / D, j = idx - h * D;
     if (h >= GV) continue;
-    float M = -INFINITY;
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mbuf[w * NV + h]);
-    float a = 0.f, L = 0.f;
-    for (int w = 0; w < WAVES; ++w) {
-      const float f = exp2f(mbuf[w * NV + h] - M);
-      a += f * abuf[(w * NV + h) * D + j];
-      L += f * lbuf[w * NV + h];
-    }
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) a += fbuf[h * WAVES + w] * abuf[(w * NV + h) * D + j];
     const long long prow = (((long long)b * n_kv_heads + g) * GV + h) * S + split;
     part_acc[prow * D + j] = a;
     if (j == 0) {
-      part_ml[prow * 2] = M;
-      part_ml[prow * 2 + 1] = L;
+      part_ml[prow * 2] = tot[2 * h];
+      part_ml[prow * 2 + 1] = tot[2 * h + 1];
     }
   }
 }
