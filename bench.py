@@ -82,6 +82,17 @@ def copy_calibration(mb, steps):
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attend_split_traffic.txt")
+# At most this many cold copies of a cache are cycled through: a small
+# workload (the 256-token one is 37 KB) would otherwise give a graph of tens of
+# thousands of launches per replay (and such graphs under a counter profiler
+# have ended in a malformed-packet queue error). Small workloads are
+# launch-bound, so their few MB of copies do not change what they measure.
+MAX_COLD_COPIES = 256
+
+
+def cold_copies(cold_bytes, footprint):
+    """Copies of a footprint-byte cache that cover cold_bytes (2 .. MAX_COLD_COPIES)."""
+    return min(MAX_COLD_COPIES, max(2, math.ceil(cold_bytes / footprint)))
 KERNEL_SOURCE = os.path.join(ROOT, "compressed_domain_decode_amd", "csrc", "attend.hip")
 
 
@@ -354,7 +365,7 @@ def config_line(name, args, hip):
     vc = tq.tq_codec_init(d, wl.v_bits, wl.codec_seed)
     kr, vr = kc.row_bytes, vc.row_bytes
     footprint = B * Hkv * T * (kr + vr + 8)
-    ncopies = 1 if args.cold_bytes <= 0 else max(2, math.ceil(args.cold_bytes / footprint))
+    ncopies = 1 if args.cold_bytes <= 0 else cold_copies(args.cold_bytes, footprint)
     k_dev = torch.from_numpy(inp.k).to(dev)
     v_dev = torch.from_numpy(inp.v).to(dev)
     q_dev = torch.from_numpy(inp.q).to(dev)
@@ -471,7 +482,7 @@ def main():
     max_len = int(lengths_np.max())
 
     footprint = B * Hkv * T * (kr + vr + 8)
-    ncopies = 1 if args.cold_bytes <= 0 else max(2, math.ceil(args.cold_bytes / footprint))
+    ncopies = 1 if args.cold_bytes <= 0 else cold_copies(args.cold_bytes, footprint)
 
     def token_major(x, codes, norms, row, t0, t1):
         """[t][b*h][...] views of tokens t0..t1 of a [B][Hkv][T][...] cache."""
@@ -645,7 +656,7 @@ def main():
         try:
             vc4 = tq.tq_codec_init(d, 4, wl.codec_seed)
             vr4 = vc4.row_bytes
-            kcopies = max(2, math.ceil(args.cold_bytes / (B * Hkv * T * (2 * d + vr4 + 4))))
+            kcopies = cold_copies(args.cold_bytes, (B * Hkv * T * (2 * d + vr4 + 4)))
             rk_copies = []
             for i in range(kcopies):
                 v4c = torch.empty((B, Hkv, T, vr4), dtype=torch.uint8, device=dev)
@@ -681,7 +692,7 @@ def main():
             dv = torch.randn((1, dH, dT, dd), generator=gen, device=dev).half()
             dq = torch.randn((1, dH, dd), generator=gen, device=dev).half()
             drow = dkc.row_bytes + 4 + dvc.row_bytes + 4
-            dcopies = max(2, math.ceil(args.cold_bytes / (dH * dT * drow)))
+            dcopies = cold_copies(args.cold_bytes, (dH * dT * drow))
             tmaj = lambda a, *row: a.view(dH, dT, *row).permute(1, 0, *range(2, 2 + len(row)))
             d_copies = []
             for i in range(dcopies):
@@ -727,7 +738,7 @@ def main():
             pk = tq.tq_codec_init_prod(d, 4, wl.codec_seed)
             vc4 = tq.tq_codec_init(d, 4, wl.codec_seed)
             prow = pk.row_bytes + pk.sketch_bytes + 8 + vc4.row_bytes + 4
-            pcopies = max(2, math.ceil(args.cold_bytes / (B * Hkv * T * prow)))
+            pcopies = cold_copies(args.cold_bytes, (B * Hkv * T * prow))
             tmv = lambda a, *row: a.view(B * Hkv, T, *row).permute(1, 0, *range(2, 2 + len(row)))
             p_copies = []
             for i in range(pcopies):

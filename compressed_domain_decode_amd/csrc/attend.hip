@@ -1019,8 +1019,14 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     //      entries (one batch ahead), the products.
     // a pair entry is read as its two dwords (x: the first coordinate's
     // (hi, lo), y: the second's), each straight into the operand it feeds
-    using VLut = std::conditional_t<C::VPAIR, u2v, uint32_t>;
     constexpr int TB = kVBatch, NTB = kTile / 2 / TB;
+    // A batch's lookups: pair entries per (token pair, token, lookup) as
+    // their two dwords; single entries per (token pair, lookup) as the two
+    // tokens' dwords, which is the operand pair they feed (held any other
+    // way, the compiler has paired them through a stack round trip).
+    struct VLuts {
+      std::conditional_t<C::VPAIR, u2v[TB][2][C::NVS], u2v[TB][C::NVS]> e;
+    };
     auto v_stage = [&](auto JI, u2v (&dst)[TB][2][C::NVS]) __attribute__((always_inline)) {
       sfor<TB>([&](auto TI) {
         sfor<2>([&](auto SI) {
@@ -1032,8 +1038,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         });
       });
     };
-    auto v_lookup = [&](const u2v (&xs)[TB][2][C::NVS], VLut (&dst)[TB][2][C::NVS])
-                        __attribute__((always_inline)) {
+    auto v_lookup = [&](const u2v (&xs)[TB][2][C::NVS], VLuts& dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt)
 #pragma unroll
@@ -1042,21 +1047,25 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
           for (int k = 0; k < C::NVS; ++k) {
             const uint32_t x = __builtin_amdgcn_alignbit(xs[tt][s][k].y, xs[tt][s][k].x, vsh[k]);
             const uint32_t a = (x & VMASK) | voff;
-            if constexpr (C::VPAIR)
-              dst[tt][s][k] = u2v{*(const uint32_t*)(vt + a),
-                                  *(const uint32_t*)(vt + ((x & vmask_y) | voff_y))};
-            else
-              dst[tt][s][k] = *(const uint32_t*)(vt + a);
+            if constexpr (C::VPAIR) {
+              dst.e[tt][s][k] = u2v{*(const uint32_t*)(vt + a),
+                                    *(const uint32_t*)(vt + ((x & vmask_y) | voff_y))};
+            } else {
+              if (s == 0)
+                dst.e[tt][k].x = *(const uint32_t*)(vt + a);
+              else
+                dst.e[tt][k].y = *(const uint32_t*)(vt + a);
+            }
           }
     };
-    auto v_mfma = [&](auto JI, const VLut (&cs)[TB][2][C::NVS]) __attribute__((always_inline)) {
+    auto v_mfma = [&](auto JI, const VLuts& cs) __attribute__((always_inline)) {
       sfor<TB>([&](auto TI) {
         constexpr int tp = JI * TB + TI;  // token pair
 #pragma unroll
         for (int k = 0; k < C::NVS; ++k) {
           if constexpr (C::VPAIR) {
-            const v4h b0 = as_v4h(cs[TI][0][k].x, cs[TI][1][k].x);
-            const v4h b1 = as_v4h(cs[TI][0][k].y, cs[TI][1][k].y);
+            const v4h b0 = as_v4h(cs.e[TI][0][k].x, cs.e[TI][1][k].x);
+            const v4h b1 = as_v4h(cs.e[TI][0][k].y, cs.e[TI][1][k].y);
 #pragma unroll
             for (int hg = 0; hg < NHG; ++hg) {
               acc[0][2 * k][hg] = mfma16<tp % 16>(WH[hg][tp / 16], b0, acc[0][2 * k][hg]);
@@ -1066,7 +1075,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
             }
           } else {
             constexpr int par = (C::NVS == 1) ? (tp & 1) : 0;
-            const v4h bv = as_v4h(cs[TI][0][k], cs[TI][1][k]);
+            const v4h bv = __builtin_bit_cast(v4h, cs.e[TI][k]);
 #pragma unroll
             for (int hg = 0; hg < NHG; ++hg) {
               acc[0][k + par][hg] = mfma16<tp % 16>(WH[hg][tp / 16], bv, acc[0][k + par][hg]);
@@ -1078,7 +1087,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     };
     {
       u2v xs0[TB][2][C::NVS], xs1[TB][2][C::NVS], xs2[TB][2][C::NVS];
-      VLut cv0[TB][2][C::NVS], cv1[TB][2][C::NVS];
+      VLuts cv0, cv1;
       v_stage(std::integral_constant<int, 0>{}, xs0);
       v_stage(std::integral_constant<int, 1>{}, xs1);
       v_lookup(xs0, cv0);
