@@ -787,17 +787,22 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     for (int v = 0; v < 4; ++v) vlim[hg][v] = min(t_end, len - n_qtok + (4 * hg + v) / G + 1);
 
   // ---- per-wave online-softmax state. acc[0] collects the products with
-  //      the weights' high halves, acc[1] with their low halves.
+  //      the weights' high halves, acc[LO] with their low halves.
   float m_run[NHG][4];
   v4f l_run[NHG];
-  v4f acc[2][C::NACC][NHG];
+  // With four head groups their independent chains already keep the matrix
+  // unit busy, and the high- and low-half products share one accumulator
+  // (and one score chain per parity below), which saves the registers that
+  // would otherwise spill: HL accumulator sets, LO the low halves' set.
+  constexpr int HL = NHG >= 4 ? 1 : 2, LO = HL - 1;
+  v4f acc[HL][C::NACC][NHG];
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     l_run[hg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 4; ++v) m_run[hg][v] = kNoRow;
 #pragma unroll
-    for (int a = 0; a < C::NACC; ++a) acc[0][a][hg] = acc[1][a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < C::NACC; ++a) acc[0][a][hg] = acc[LO][a][hg] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   // every V norm seen so far is below 2^ev (ev only grows)
   int ev = 0;
@@ -843,9 +848,12 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     //      halves of the queries, into four accumulator chains. The lookups
     //      of batch j + 1 are issued before the products of batch j, so a
     //      batch's LDS latency hides behind the previous batch's products.
-    v4f sc[4][NHG];
+    // score chains: per parity of the product index, the high and the low
+    // halves' products (one chain per parity when HL == 1)
+    constexpr int SCN = 2 * HL;
+    v4f sc[SCN][NHG];
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4)
+    for (int a4 = 0; a4 < SCN; ++a4)
 #pragma unroll
       for (int hg = 0; hg < NHG; ++hg) sc[a4][hg] = v4f{0.f, 0.f, 0.f, 0.f};
     if constexpr (C::KRAW) {
@@ -855,8 +863,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         const v4h kb = as_v4h(r.kw[2 * f], r.kw[2 * f + 1]);
 #pragma unroll
         for (int hg = 0; hg < NHG; ++hg) {
-          sc[2 * (f % 2)][hg] = mfma16<f % 16>(QH[hg][f / 16], kb, sc[2 * (f % 2)][hg]);
-          sc[2 * (f % 2) + 1][hg] = mfma16<f % 16>(QL[hg][f / 16], kb, sc[2 * (f % 2) + 1][hg]);
+          sc[HL * (f % 2)][hg] = mfma16<f % 16>(QH[hg][f / 16], kb, sc[HL * (f % 2)][hg]);
+          sc[HL * (f % 2) + LO][hg] = mfma16<f % 16>(QL[hg][f / 16], kb, sc[HL * (f % 2) + LO][hg]);
         }
       });
     } else {
@@ -892,8 +900,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
         const v4h kb = as_v4h(src.x, src.y);
 #pragma unroll
         for (int hg = 0; hg < NHG; ++hg) {
-          sc[2 * (p % 2)][hg] = mfma16<p % 16>(QH[hg][p / 16], kb, sc[2 * (p % 2)][hg]);
-          sc[2 * (p % 2) + 1][hg] = mfma16<p % 16>(QL[hg][p / 16], kb, sc[2 * (p % 2) + 1][hg]);
+          sc[HL * (p % 2)][hg] = mfma16<p % 16>(QH[hg][p / 16], kb, sc[HL * (p % 2)][hg]);
+          sc[HL * (p % 2) + LO][hg] = mfma16<p % 16>(QL[hg][p / 16], kb, sc[HL * (p % 2) + LO][hg]);
         }
       };
       sfor<NKP + kKAhead>([&](auto I) {
@@ -905,7 +913,10 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
     v4f s0[NHG];
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg)
-      s0[hg] = ((sc[0][hg] + sc[1][hg]) + (sc[2][hg] + sc[3][hg])) * kunscale;
+      if constexpr (HL == 2)
+        s0[hg] = ((sc[0][hg] + sc[1][hg]) + (sc[SCN - 2][hg] + sc[SCN - 1][hg])) * kunscale;
+      else
+        s0[hg] = (sc[0][hg] + sc[SCN - 1][hg]) * kunscale;
     if constexpr (C::PROD) {
       // QJL correction: residual norm x sum_j sgn_j u^_j, sgn_j = -1 for a set
       // sketch bit (the bit becomes the sign of 1.0 as the MFMA operand)
@@ -946,7 +957,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
       if (seen) {  // before the first tile the accumulators are zero
         const float f = exp2i(max(-126, ev - en));
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
+        for (int hl = 0; hl < HL; ++hl)
 #pragma unroll
           for (int a = 0; a < C::NACC; ++a)
 #pragma unroll
@@ -975,7 +986,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
             const float alpha = __builtin_amdgcn_exp2f(m_run[hg][v] - mt);
             l_run[hg][v] *= alpha;
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
+            for (int hl = 0; hl < HL; ++hl)
 #pragma unroll
               for (int a = 0; a < C::NACC; ++a) acc[hl][a][hg][v] *= alpha;
           }
@@ -1069,9 +1080,9 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
             for (int hg = 0; hg < NHG; ++hg) {
               acc[0][2 * k][hg] = mfma16<tp % 16>(WH[hg][tp / 16], b0, acc[0][2 * k][hg]);
-              acc[1][2 * k][hg] = mfma16<tp % 16>(WL[hg][tp / 16], b0, acc[1][2 * k][hg]);
+              acc[LO][2 * k][hg] = mfma16<tp % 16>(WL[hg][tp / 16], b0, acc[LO][2 * k][hg]);
               acc[0][2 * k + 1][hg] = mfma16<tp % 16>(WH[hg][tp / 16], b1, acc[0][2 * k + 1][hg]);
-              acc[1][2 * k + 1][hg] = mfma16<tp % 16>(WL[hg][tp / 16], b1, acc[1][2 * k + 1][hg]);
+              acc[LO][2 * k + 1][hg] = mfma16<tp % 16>(WL[hg][tp / 16], b1, acc[LO][2 * k + 1][hg]);
             }
           } else {
             constexpr int par = (C::NVS == 1) ? (tp & 1) : 0;
@@ -1079,7 +1090,7 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
             for (int hg = 0; hg < NHG; ++hg) {
               acc[0][k + par][hg] = mfma16<tp % 16>(WH[hg][tp / 16], bv, acc[0][k + par][hg]);
-              acc[1][k + par][hg] = mfma16<tp % 16>(WL[hg][tp / 16], bv, acc[1][k + par][hg]);
+              acc[LO][k + par][hg] = mfma16<tp % 16>(WL[hg][tp / 16], bv, acc[LO][k + par][hg]);
             }
           }
         }
@@ -1131,7 +1142,8 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
 #pragma unroll
   for (int a = 0; a < C::NACC; ++a)
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) accf[a][hg] = (acc[0][a][hg] + acc[1][a][hg]) * aunscale;
+    for (int hg = 0; hg < NHG; ++hg)
+      accf[a][hg] = (HL == 2 ? acc[0][a][hg] + acc[LO][a][hg] : acc[0][a][hg]) * aunscale;
   if constexpr (C::NVS == 1 && !C::VPAIR) {
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) accf[0][hg] += accf[1][hg];
