@@ -790,12 +790,13 @@ __global__ __launch_bounds__(64 * C::WAVES) void attend_split_kernel(
   //      the weights' high halves, acc[LO] with their low halves.
   float m_run[NHG][4];
   v4f l_run[NHG];
-  // With two or more head groups their independent chains already keep the
-  // matrix unit busy, and the high- and low-half products share one
-  // accumulator (and one score chain per parity below): with four the
-  // separate sets would spill, with two sharing measured slightly faster.
-  // HL accumulator sets, LO the low halves' set.
-  constexpr int HL = NHG >= 2 ? 1 : 2, LO = HL - 1;
+  // The high- and low-half products of an operand go into one accumulator
+  // (and one score chain per product parity below): the chains of the
+  // accumulators, parities and head groups are enough to keep the matrix
+  // unit busy. Separate chains for the two halves (HL = 2) measured no
+  // faster with one head group and slower with two, and with four head
+  // groups they spill. HL accumulator sets, LO the low halves' set.
+  constexpr int HL = 1, LO = HL - 1;
   v4f acc[HL][C::NACC][NHG];
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
