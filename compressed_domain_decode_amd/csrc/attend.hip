@@ -1245,6 +1245,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   constexpr int NG = kCombineThreads / D;  // split groups
   constexpr int U = kCombineUnroll;
   constexpr int RL = 16;                   // lanes per raw row for its score
+  static_assert(RL == 16, "the raw-row score sums over 4 lane-xor steps");
   constexpr int RPD = D / RL;              // coordinates per lane
   __shared__ float s_acc[NG][D];
   __shared__ float s_racc[kRaw ? NG : 1][D];
@@ -1295,8 +1296,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       ok[u] = s0 + u * NG < ns && mv[u] != -INFINITY;
       if (ok[u]) mnew = fmaxf(mnew, mv[u]);
     }
+    // every exponent below is <= 0 (or -inf): the hardware exponential
     if (mnew != mg) {  // mnew > mg: rescale (by 0 while mg is still -inf)
-      const float r = exp2f(mg - mnew);
+      const float r = __builtin_amdgcn_exp2f(mg - mnew);
       a *= r;
       L *= r;
       mg = mnew;
@@ -1304,7 +1306,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (ok[u]) {
-        const float f = exp2f(mv[u] - mg);
+        const float f = __builtin_amdgcn_exp2f(mv[u] - mg);
         a = fmaf(f, av[u], a);
         L = fmaf(f, lv[u], L);
       }
@@ -1327,8 +1329,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       float sc = 0.f;
 #pragma unroll
       for (int i = 0; i < RPD; ++i) sc = fmaf(qv[i], __half2float(kr[i]), sc);
-#pragma unroll
-      for (int m = 1; m < RL; m <<= 1) sc += __shfl_xor(sc, m);
+      sfor<4>([&](auto MI) { sc += xor_lane_f32<1 << MI>(sc); });
       if (part == 0 && t < R) s_raw[t] = sc;
     }
     __syncthreads();
@@ -1342,7 +1343,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       for (int u = 0; u < 2 * U; ++u) {
         const int t = min(t0 + u * NG, R - 1);
         vv[u] = __half2float(vcol[(long long)t * D]);
-        pp[u] = t0 + u * NG < R ? exp2f(s_raw[t] - mr) : 0.f;
+        pp[u] = t0 + u * NG < R ? __builtin_amdgcn_exp2f(s_raw[t] - mr) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 2 * U; ++u) {
@@ -1371,10 +1372,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     float Lt = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
-      fg[g2] = s_m[g2] == -INFINITY ? 0.f : exp2f(s_m[g2] - M);
+      fg[g2] = s_m[g2] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[g2] - M);
       Lt = fmaf(fg[g2], s_l[g2], Lt);
     }
-    const float fr = kRaw && mr != -INFINITY ? exp2f(mr - M) : 0.f;
+    const float fr = kRaw && mr != -INFINITY ? __builtin_amdgcn_exp2f(mr - M) : 0.f;
     if constexpr (kRaw) {
       float lr = 0.f;
 #pragma unroll
@@ -1403,15 +1404,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
           u[e] = x0 + x1;
           u[e + hs] = x0 - x1;
         }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
+    // (cross-lane steps on DPP and permlane swaps: wavefront 0 is whole)
+    sfor<6>([&](auto MI) {
+      constexpr int m = 1 << MI;
       const bool upper = (lane & m) != 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float p = __shfl_xor(u[e], m);
+        const float p = xor_lane_f32<m>(u[e]);
         u[e] = upper ? (p - u[e]) : (u[e] + p);
       }
-    }
+    });
     const float invd = 1.f / (float)D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
