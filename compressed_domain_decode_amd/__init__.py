@@ -36,6 +36,7 @@ EXPORTED = (
     "tq_attend_multi_workspace_bytes", "tq_decode_attend_mixed", "tq_decode_attend_raw_k",
     "tq_codec_init_prod", "tq_encode_prod", "tq_decode_attend_prod", "tq_decode_attend", "tq_attend_num_splits",
     "tq_status_string", "tq_last_error", "tq_set_split_events", "tq_stream_read",
+    "tq_stream_read_resident",
     "tq_cache_init", "tq_cache_destroy", "tq_cache_state", "tq_cache_append",
     "tq_cache_workspace_bytes", "tq_cache_attend", "tq_codec_init_dense",
     "tq_decode_attend_noalloc",
@@ -122,6 +123,8 @@ _lib.tq_attend_multi_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_set_split_events.argtypes = [_P, _P]
 _lib.tq_stream_read.restype = _I
 _lib.tq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+_lib.tq_stream_read_resident.restype = _I
+_lib.tq_stream_read_resident.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.tq_set_split_events.restype = _I
 
 
@@ -553,15 +556,17 @@ def tq_set_split_events(before, after) -> None:
     _check(_lib.tq_set_split_events(before, after))
 
 
-def tq_stream_read(buf, sink, stream=None) -> None:
+def tq_stream_read(buf, sink, stream=None, resident=False) -> None:
     """Measurement aid: a plain streaming read of the whole (contiguous, 16-byte
-    aligned) device tensor buf; sink is a device tensor of at least 4 bytes."""
+    aligned) device tensor buf; sink is a device tensor of at least 4 bytes.
+    resident=True reads with the resident-grid design (tq_stream_read_resident)."""
+    name = "tq_stream_read_resident" if resident else "tq_stream_read"
     if not buf.is_contiguous():
         raise ValueError("buf must be contiguous")
     if buf.device.type != "cuda" or sink.device.type != "cuda":
-        raise TQError(TQ_ERR_INVALID_ARG, "tq_stream_read: buf and sink must be GPU tensors")
+        raise TQError(TQ_ERR_INVALID_ARG, f"{name}: buf and sink must be GPU tensors")
     nbytes = buf.numel() * buf.element_size()
-    _check(_lib.tq_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
+    _check(getattr(_lib, name)(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
                                ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
 
 

@@ -348,6 +348,20 @@ tq_status tq_stream_read(const void* buf, size_t bytes, void* sink, void* stream
   return ok();
 }
 
+tq_status tq_stream_read_resident(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(TQ_ERR_INVALID_ARG, "tq_stream_read_resident: NULL buffer or sink");
+  if ((uintptr_t)buf % 16 || bytes % 16 || (uintptr_t)sink % 4)
+    return fail(TQ_ERR_INVALID_ARG,
+                "tq_stream_read_resident: buffer must be 16-byte aligned, bytes a multiple of 16, "
+                "sink 4-byte aligned");
+  const hipError_t e =
+      tq::launch_stream_read_resident(buf, bytes, (uint32_t*)sink, (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(TQ_ERR_HIP, "tq_stream_read_resident: %s", hipGetErrorString(e));
+  return ok();
+}
+
 static bool attend_shape_ok(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len) {
   return batch > 0 && n_kv_heads > 0 && n_q_heads > 0 && n_q_heads % n_kv_heads == 0 &&
          n_q_heads / n_kv_heads <= 16 && dense_dim_ok(dim) && max_len > 0 && batch <= 65535 &&

@@ -165,5 +165,7 @@ hipError_t scratch_region(void** ptr);
 
 // Plain streaming read of `bytes` (a multiple of 16) at buf (16-byte aligned).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_stream_read_resident(const void* buf, size_t bytes, uint32_t* sink,
+                                       hipStream_t stream);
 
 }  // namespace tq

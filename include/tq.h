@@ -443,6 +443,13 @@ tq_status tq_set_split_events(void* before, void* after);
  * ceiling next to the nominal peak. bytes == 0 does nothing. */
 tq_status tq_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
 
+/* Measurement aid, the same read by a second design: a resident grid of one
+ * 1024-thread workgroup per compute unit whose threads loop over their share
+ * with eight 16-byte loads in flight per pass (tq_stream_read launches one
+ * 256-thread workgroup per 32 KB). Same arguments, alignment rules and
+ * errors as tq_stream_read. */
+tq_status tq_stream_read_resident(const void* buf, size_t bytes, void* sink, void* stream);
+
 /* Number of context splits tq_decode_attend launches for this shape (for
  * measurement and tests); 0 on invalid input. */
 int tq_attend_num_splits(int batch, int n_q_heads, int n_kv_heads, int dim, int max_len);

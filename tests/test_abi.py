@@ -320,15 +320,17 @@ def test_single_hip_runtime_in_process():
     assert len(hip) == 1, hip
 
 
-def test_stream_read_validation():
+@pytest.mark.parametrize("name", ["tq_stream_read", "tq_stream_read_resident"])
+def test_stream_read_validation(name):
     lib = ctypes.CDLL(tq.LIB_PATH)
-    lib.tq_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-    assert lib.tq_stream_read(None, 0, None, None) == tq.TQ_OK          # nothing to read
-    assert lib.tq_stream_read(None, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG
-    assert lib.tq_stream_read(FAKE, 64, None, None) == tq.TQ_ERR_INVALID_ARG
-    assert lib.tq_stream_read(FAKE + 8, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG  # alignment
-    assert lib.tq_stream_read(FAKE, 60, FAKE, None) == tq.TQ_ERR_INVALID_ARG      # size
-    assert "tq_stream_read" in tq.tq_last_error()
+    fn = getattr(lib, name)
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert fn(None, 0, None, None) == tq.TQ_OK          # nothing to read
+    assert fn(None, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+    assert fn(FAKE, 64, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert fn(FAKE + 8, 64, FAKE, None) == tq.TQ_ERR_INVALID_ARG  # alignment
+    assert fn(FAKE, 60, FAKE, None) == tq.TQ_ERR_INVALID_ARG      # size
+    assert name in tq.tq_last_error()
 
 
 def _cache_desc(**kw):
