@@ -855,6 +855,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": n_steps,
+        "steps_match": n_steps == args.steps,  # each replay times exactly --steps steps
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "timing": {"replays": len(replay_ms), "steps_per_replay": n_steps,
