@@ -19,9 +19,9 @@
 //    Both contractions run on the matrix cores as fp16 4x4x4 products with
 //    fp32 accumulation, each fp32 operand carried as an fp16 pair hi + lo
 //    (hi the nearest fp16, lo the nearest fp16 of the remainder; about 22
-//    significant bits). On gfx950 the fp16 matrix instructions issue
-//    alongside VALU work, which the fp32 ones do not, so the unpacking and
-//    table addressing overlap the products. The 4-deep reduction of an
+//    significant bits). On gfx950 the fp16 matrix instructions can execute
+//    alongside VALU work, which the fp32 ones do not, so part of the
+//    unpacking and table addressing overlaps the products. The 4-deep reduction of an
 //    instruction is laid out as (hi_j, lo_j, hi_j', lo_j') of two
 //    coordinates (scores) or two tokens (values), so a centroid entry
 //    (hi, lo) read from LDS is an operand as it stands:
@@ -35,8 +35,9 @@
 //      softmax online softmax in base 2 (log2 e folded into q^), per head
 //              running max from a cross-lane reduction; weights p * nV_t.
 //      values  A[h][j] += sum_t w[h][t] * cV[idxV[t][j]]
-//              lanes own coordinates. The lane holding token t stages t's
-//              packed V row in LDS; per token each lane reads the two dwords
+//              lanes own coordinates. A tile's packed V rows are copied into
+//              the wavefront's LDS stage by buffer loads straight to LDS;
+//              per token each lane reads the two dwords
 //              that hold its code(s), funnel-shifts them and looks the
 //              centroid entry up; two tokens' entries form the B operand and
 //              the weights, (wh_t, wh_t, wh_t', wh_t') and (wl_t, 0, wl_t', 0),
@@ -51,8 +52,9 @@
 //    Centroid tables live in LDS replicated once per bank (a 256-byte row
 //    per code: 64 copies of a 4-byte entry, or 32 of an 8-byte code-pair
 //    entry), so a lookup is conflict-free whatever the codes; codes of
-//    <= 3 bits are looked up two coordinates at a time. The query rotation q^ = (scale log2 e / d)
-//    H (sigma_K (.) q) is done by every wavefront in its prologue.
+//    <= 3 bits are looked up two coordinates at a time. The query rotation
+//    q^ = (scale log2 e / d) H (sigma_K (.) q) is done in the prologue, one
+//    head per worker wavefront at a time, into LDS.
 //    The wavefronts merge (max, sum, accumulator) through LDS and write one
 //    partial per (sequence, query head, split).
 // 2. combine: log-sum-exp merge of the split partials, normalisation, inverse
