@@ -27,6 +27,7 @@
 
 #include "codec.hpp"
 #include "kernels.hpp"
+#include "xlane.hpp"
 
 namespace tq {
 namespace {
@@ -373,10 +374,261 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
   }
 }
 
-// Grid (n_q_heads, batch): merge the splits by log-sum-exp, then
-// out_i = sum_j m_V[j][i] a_j / d (fp64 sums).
-__global__ __launch_bounds__(256) void dense_combine_kernel(DenseAttendArgs a) {
+// ------------------------------------------------ attend, one query head per KV head
+//
+// With one query head per KV head (multi-head attention: no group shares a
+// KV row) the kernel above spends its time in dependent LDS round trips
+// (staged row, then centroid, per token and coordinate) with a quarter of
+// its lanes idle at head dim 96. Here everything a token needs stays in
+// registers: two lanes share a token, each holding half of the rotated query
+// and half of the value accumulator, and each lane keeps its own online
+// softmax state (running maximum, sum) over the tokens it visits, so a step
+// needs no cross-lane work beyond adding the two half scores. A lane loads
+// its half row straight from global memory, one step ahead. The lanes'
+// states are merged once, at the end of the range: per wavefront by two
+// transposing lane swaps and LDS, then across wavefronts.
+
+constexpr int kLtWaves = 12;     // wavefronts per workgroup (3 per SIMD at <= 168 VGPRs)
+constexpr int kLtStep = 32;      // tokens per wavefront step (two lanes per token)
+constexpr float kLtSlack = 8.f;  // the running maximum moves only when a score exceeds it by more
+
+template <int D, int KB, int VB>
+struct LtShape {
+  static constexpr int H = D / 2;                           // coordinates per lane
+  static constexpr int HK = H * KB, HV = H * VB;            // bits of a half row
+  static constexpr int KW = D * KB / 32, VW = D * VB / 32;  // dwords per row
+  // dwords a lane loads (the second half may start inside a dword) and keeps
+  // once its half is shifted down to bit 0
+  static constexpr int KL = (HK % 32 + HK + 31) / 32, VL = (HV % 32 + HV + 31) / 32;
+  static constexpr int KS = (HK + 31) / 32, VS = (HV + 31) / 32;
+  static constexpr int R = H / 4;   // accumulators per lane after the two swaps
+  static constexpr int RP = R | 1;  // their LDS stride (odd: no bank conflicts)
+  static_assert(D % 32 == 0 && H % 16 == 0, "head dim");
+};
+
+// Bits [off, off + 32 S) of the window w (0 <= off < 32) as S dwords.
+template <int L, int S>
+__device__ __forceinline__ void lt_shift(const uint32_t (&w)[L], int off, uint32_t (&o)[S]) {
+#pragma unroll
+  for (int k = 0; k < S; ++k) o[k] = __builtin_amdgcn_alignbit(k + 1 < L ? w[k + 1] : 0u, w[k], off);
+}
+// Code j of a B-bit LSB-first stream held in registers (j a compile-time index).
+template <int B, int S>
+__device__ __forceinline__ uint32_t lt_field(const uint32_t (&w)[S], int j) {
+  const int p = j * B, wi = p >> 5, sh = p & 31;
+  uint32_t f = w[wi] >> sh;
+  if (sh + B > 32) f |= w[wi + 1] << (32 - sh);
+  return f & ((1u << B) - 1u);
+}
+
+// Sum of the two registers a lane swap returns. Each is copied to a named
+// word before it is reinterpreted: a bit cast taken straight from an element
+// of the returned pair compiles to a read of its first element for both.
+template <class P>
+__device__ __forceinline__ float swap_sum(const P& p) {
+  const uint32_t x = p[0], y = p[1];
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+
+template <int D, int KB, int VB>
+struct LtRows {
+  uint32_t k[LtShape<D, KB, VB>::KL];
+  uint32_t v[LtShape<D, KB, VB>::VL];
+  float nk, nv;
+};
+
+// Grid (splits, n_kv_heads, batch), kLtWaves wavefronts; the partials have
+// the layout of dense_split_kernel's, so dense_combine_kernel finishes both.
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs a) {
+  using S = LtShape<D, KB, VB>;
+  constexpr int H = S::H, NT = 64 * kLtWaves;
+  __shared__ float s_q[D];
+  __shared__ float s_ck[1 << KB], s_cv[1 << VB];
+  constexpr int QP = NT / D;  // threads per rotated query coordinate
+  __shared__ double s_qp[QP][D];
+  __shared__ float s_red[kLtWaves][64][S::RP];
+  __shared__ float s_ml[kLtWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int half = lane & 1;
+
+  // the range, and its first rows (in flight during the query rotation)
+  const int len = min(a.lengths[b], a.max_len);  // never read past the host bound
+  const long long t_stop = (long long)s * a.tokens_per_split + a.tokens_per_split;
+  const int t_begin = s * a.tokens_per_split;
+  const int t_end = (int)(t_stop < len ? t_stop : (len > 0 ? len : 0));
+  const int last = t_end > 0 ? t_end - 1 : 0;  // a row that exists even for an empty range
+  const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_ctx;
+  const uint32_t* kbase = (const uint32_t*)a.k_codes + row0 * S::KW + half * (S::HK / 32);
+  const uint32_t* vbase = (const uint32_t*)a.v_codes + row0 * S::VW + half * (S::HV / 32);
+  const float* kn = a.k_norms + row0;
+  const float* vn = a.v_norms + row0;
+  const int me = t_begin + (lane >> 1);
+  // rows of step st; tokens past the range read its last row (in bounds)
+  auto load = [&](int st, LtRows<D, KB, VB>& r) {
+    const int t = me + st * kLtStep, rr = t < t_end ? t : last;
+    const uint32_t* kp = kbase + (size_t)rr * S::KW;
+    const uint32_t* vp = vbase + (size_t)rr * S::VW;
+#pragma unroll
+    for (int k = 0; k < S::KL; ++k) r.k[k] = kp[k];
+#pragma unroll
+    for (int k = 0; k < S::VL; ++k) r.v[k] = vp[k];
+    r.nk = kn[rr];
+    r.nv = vn[rr];
+  };
+  LtRows<D, KB, VB> cur, nxt;
+  load(wave, cur);
+
+  for (int k = tid; k < (1 << KB); k += NT) s_ck[k] = a.k_centroids[k];
+  for (int k = tid; k < (1 << VB); k += NT) s_cv[k] = a.v_centroids[k];
+  // rotated query of this KV head's one query head, q_hat_i = sum_j m_ij q_j:
+  // QP threads per coordinate sum consecutive stretches of j, then one adds
+  // the partial sums in order (fp64 throughout)
+  const __half* qg = (const __half*)a.q + ((size_t)b * a.n_q_heads + g) * D;
+  if (tid < QP * D) {
+    const int i = tid % D, part = tid / D;
+    const int j0 = part * D / QP, j1 = (part + 1) * D / QP;
+    double acc = 0.0;
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j) acc += rot_k(a, i, j) * (double)__half2float(qg[j]);
+    s_qp[part][i] = acc;
+  }
+  __syncthreads();
+  if (tid < D) {
+    double acc = 0.0;
+#pragma unroll
+    for (int p = 0; p < QP; ++p) acc += s_qp[p][tid];
+    s_q[tid] = (float)(acc * (double)a.qscale);
+  }
+  __syncthreads();
+
+  float qv[H], acc[H];
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    qv[i] = s_q[half * H + i];
+    acc[i] = 0.f;
+  }
+  float m = kDNoRow, l = 0.f;
+  if (t_end > t_begin) {  // uniform over the workgroup
+    const int koff = half * (S::HK % 32), voff = half * (S::HV % 32);
+    const int steps = (t_end - t_begin + kLtStep - 1) / kLtStep;
+    for (int st = wave; st < steps; st += kLtWaves) {
+      load(st + kLtWaves, nxt);  // unconditional: the prefetch has no branch
+      const bool valid = me + st * kLtStep < t_end;
+      uint32_t kw[S::KS];
+      if constexpr (S::HK % 32 != 0) {
+        lt_shift(cur.k, koff, kw);
+      } else {
+#pragma unroll
+        for (int k = 0; k < S::KS; ++k) kw[k] = cur.k[k];
+      }
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < H; ++j) p4[j & 3] = fmaf(qv[j], s_ck[lt_field<KB>(kw, j)], p4[j & 3]);
+      float sk = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      sk += xor_lane_f32<1>(sk);  // the token's other half; the same sum on both lanes
+      const float sc = valid ? sk * cur.nk : -INFINITY;
+      if (sc > m + kLtSlack) {
+        const float al = exp2f(m - sc);
+        l *= al;
+#pragma unroll
+        for (int i = 0; i < H; ++i) acc[i] *= al;
+        m = sc;
+      }
+      const float p = exp2f(sc - m);  // at most 2^kLtSlack
+      l += p;
+      const float w = p * cur.nv;
+      uint32_t vw[S::VS];
+      if constexpr (S::HV % 32 != 0) {
+        lt_shift(cur.v, voff, vw);
+      } else {
+#pragma unroll
+        for (int k = 0; k < S::VS; ++k) vw[k] = cur.v[k];
+      }
+#pragma unroll
+      for (int j = 0; j < H; ++j) acc[j] = fmaf(w, s_cv[lt_field<VB>(vw, j)], acc[j]);
+      cur = nxt;
+    }
+  }
+
+  // merge the lanes: scale to the wavefront's maximum, fold lanes l, l^16,
+  // l^32, l^48 by two transposing swaps, then the rest through LDS
+  float mw = m;
+  mw = fmaxf(mw, xor_lane_f32<1>(mw));
+  mw = fmaxf(mw, xor_lane_f32<2>(mw));
+  mw = fmaxf(mw, xor_lane_f32<4>(mw));
+  mw = fmaxf(mw, xor_lane_f32<8>(mw));
+  mw = fmaxf(mw, xor_lane_f32<16>(mw));
+  mw = fmaxf(mw, xor_lane_f32<32>(mw));
+  const float f = exp2f(m - mw);  // 1 where no lane saw a token (then l and acc are 0)
+  float lw = half ? 0.f : l * f;  // a token's sum is held by both of its lanes
+  lw += xor_lane_f32<1>(lw);
+  lw += xor_lane_f32<2>(lw);
+  lw += xor_lane_f32<4>(lw);
+  lw += xor_lane_f32<8>(lw);
+  lw += xor_lane_f32<16>(lw);
+  lw += xor_lane_f32<32>(lw);
+  float r1[H / 2];
+#pragma unroll
+  for (int i = 0; i < H / 2; ++i) {
+    // lanes below 32 end with coordinate i, the others with i + H/2
+    const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, acc[i] * f),
+                                                    __builtin_bit_cast(uint32_t, acc[i + H / 2] * f),
+                                                    false, false);
+    r1[i] = swap_sum(p);
+  }
+#pragma unroll
+  for (int i = 0; i < S::R; ++i) {
+    // rows 0 and 2 end with r1[i], rows 1 and 3 with r1[i + R]
+    const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, r1[i]),
+                                                    __builtin_bit_cast(uint32_t, r1[i + S::R]),
+                                                    false, false);
+    s_red[wave][lane][i] = swap_sum(p);
+  }
+  if (lane == 0) {
+    s_ml[wave][0] = mw;
+    s_ml[wave][1] = lw;
+  }
+  __syncthreads();
+  // coordinate c: half c / H, index i within it, held by the 8 lanes of parity
+  // half in row (i / (H/2), i % (H/2) / R) at slot i % R
+  for (int c = tid; c < D; c += NT) {
+    const int hh = c / H, i = c - hh * H;
+    const int b5 = i / (H / 2), i2 = i - b5 * (H / 2), b4 = i2 / S::R, k = i2 - b4 * S::R;
+    const int l0 = 32 * b5 + 16 * b4 + hh;
+    float mx = s_ml[0][0];
+#pragma unroll
+    for (int w = 1; w < kLtWaves; ++w) mx = fmaxf(mx, s_ml[w][0]);
+    float A = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kLtWaves; ++w) {
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += s_red[w][l0 + 2 * u][k];
+      const float fw = exp2f(s_ml[w][0] - mx);
+      A += sum * fw;
+      L += s_ml[w][1] * fw;
+    }
+    const size_t slot = ((size_t)b * a.n_q_heads + g) * a.splits + s;
+    a.pacc[slot * D + c] = A;
+    if (c == 0) {
+      a.pml[slot * 2] = mx;
+      a.pml[slot * 2 + 1] = L;
+    }
+  }
+}
+
+// Grid (n_q_heads, batch), kDCombineThreads threads: merge the splits by
+// log-sum-exp, then out_i = sum_j m_V[j][i] a_j / d (fp64 sums; several
+// threads per output coordinate sum consecutive stretches of j, and one adds
+// their partial sums in order).
+constexpr int kDCombineThreads = 512;
+__global__ __launch_bounds__(kDCombineThreads) void dense_combine_kernel(DenseAttendArgs a) {
+  constexpr int kParts = kDCombineThreads / 32;  // at most, for d = 32
   __shared__ float s_a[kMaxDim];
+  __shared__ double s_part[kParts * 32];
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y, d = a.dim;
   const size_t slot0 = ((size_t)b * a.n_q_heads + h) * a.splits;
   float mx = -INFINITY;
@@ -384,17 +636,26 @@ __global__ __launch_bounds__(256) void dense_combine_kernel(DenseAttendArgs a) {
   float L = 0.f;
   for (int s = 0; s < a.splits; ++s)
     L += a.pml[(slot0 + s) * 2 + 1] * exp2f(a.pml[(slot0 + s) * 2] - mx);
-  for (int j = tid; j < d; j += 256) {
+  for (int j = tid; j < d; j += kDCombineThreads) {
     float A = 0.f;
     for (int s = 0; s < a.splits; ++s)
       A += a.pacc[(slot0 + s) * d + j] * exp2f(a.pml[(slot0 + s) * 2] - mx);
     s_a[j] = L > 0.f ? A / L : 0.f;  // no visible row: a zero output
   }
   __syncthreads();
-  for (int i = tid; i < d; i += 256) {
+  const int parts = kDCombineThreads / d;  // d <= 256: at least 2
+  if (tid < parts * d) {
+    const int i = tid % d, part = tid / d;
+    const int j0 = part * d / parts, j1 = (part + 1) * d / parts;
     double o = 0.0;
-#pragma unroll 8
-    for (int j = 0; j < d; ++j) o += rot_v(a, j, i) * (double)s_a[j];
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j) o += rot_v(a, j, i) * (double)s_a[j];
+    s_part[part * d + i] = o;
+  }
+  __syncthreads();
+  for (int i = tid; i < d; i += kDCombineThreads) {
+    double o = 0.0;
+    for (int p = 0; p < parts; ++p) o += s_part[p * d + i];
     a.out[((size_t)b * a.n_q_heads + h) * d + i] = (float)(o / d);
   }
 }
@@ -453,11 +714,47 @@ hipError_t prepare_attend_dense() {
   return hipSuccess;
 }
 
+template <int D, int KB, int VB>
+hipError_t launch_dense_lt(const DenseAttendArgs& a, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL((dense_lt_kernel<D, KB, VB>), dim3(a.splits, a.n_kv_heads, batch),
+                     dim3(64 * kLtWaves), 0, stream, a);
+  return hipGetLastError();
+}
+using DenseLaunch = hipError_t (*)(const DenseAttendArgs&, int, hipStream_t);
+template <int D, int KB>
+DenseLaunch lt_for_v(int vb) {
+  switch (vb) {
+    case 2: return &launch_dense_lt<D, KB, 2>;
+    case 3: return &launch_dense_lt<D, KB, 3>;
+    case 4: return &launch_dense_lt<D, KB, 4>;
+    default: return nullptr;
+  }
+}
+template <int D>
+DenseLaunch lt_for_bits(int kb, int vb) {
+  switch (kb) {
+    case 2: return lt_for_v<D, 2>(vb);
+    case 3: return lt_for_v<D, 3>(vb);
+    case 4: return lt_for_v<D, 4>(vb);
+    case 8: return lt_for_v<D, 8>(vb);
+    default: return nullptr;
+  }
+}
+// The register-held kernel's instances: one query head per KV head, dense
+// rotations, head dim 96, K 2/3/4/8 and V 2/3/4 bits.
+DenseLaunch find_dense_lt(const DenseAttendArgs& a) {
+  if (a.group != 1 || a.wht) return nullptr;
+  if (a.dim == 96) return lt_for_bits<96>(a.k_bits, a.v_bits);
+  return nullptr;
+}
+
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream) {
   if (a.group < 1 || a.group > kDMaxG || a.dim % 32 || a.dim > kMaxDim) return hipErrorInvalidValue;
   hipError_t err;
   const bool wide = a.dim > 128;
-  if (a.group == 1)  // exact group sizes: the head loops fold away
+  if (const DenseLaunch lt = find_dense_lt(a))
+    err = lt(a, batch, stream);
+  else if (a.group == 1)  // exact group sizes: the head loops fold away
     err = wide ? launch_dense_split<1, 4, true>(a, batch, stream)
                : launch_dense_split<1, 2, true>(a, batch, stream);
   else if (a.group == 4)
@@ -470,7 +767,8 @@ hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t 
     err = wide ? launch_dense_split<16, 4, false>(a, batch, stream)
                : launch_dense_split<16, 2, false>(a, batch, stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dense_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(dense_combine_kernel, dim3(a.n_q_heads, batch), dim3(kDCombineThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

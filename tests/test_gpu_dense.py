@@ -135,6 +135,49 @@ def test_dense_attend_matches_oracle(d, kb, vb, G, Hkv, lengths, T):
             assert np.all(out[b] == 0.0)
 
 
+@pytest.mark.parametrize("kb", [2, 3, 4, 8])
+@pytest.mark.parametrize("vb", [2, 3, 4])
+def test_dense_attend_one_head_per_kv_head(kb, vb):
+    """Head dim 96 with one query head per KV head runs the register-held
+    kernel (two lanes per token, per-lane softmax state): every K/V bit pair it
+    has, with ragged tails, a range shorter than one wavefront step, a lone
+    token and an empty sequence."""
+    d, G, Hkv = 96, 1, 2
+    lengths, T = [700, 33, 1, 0], 700
+    announce(f"dense attend one head per KV head d={d} K{kb}/V{vb} lengths={lengths}")
+    out, ref = _attend_case(d, kb, vb, G, Hkv, lengths, T, seed=400 + 10 * kb + vb)
+    assert np.isfinite(out).all()
+    err = np.abs(out - ref).max()
+    assert err <= ATOL, err
+    assert np.all(out[3] == 0.0)
+
+
+@pytest.mark.parametrize("qmul", [1.0, 24.0])
+def test_dense_attend_one_head_per_kv_head_long(qmul):
+    """Several splits per sequence, tails that end inside a step, and (qmul 24)
+    scores spread over a range of hundreds in base 2, so the lanes' running
+    maxima move many times."""
+    d, kb, vb, G, Hkv = 96, 4, 3, 1, 3
+    lengths, T = [4100, 2049, 95], 4100
+    announce(f"dense attend one head per KV head d={d} K{kb}/V{vb} q x {qmul} lengths={lengths}")
+    kc, ko = dense_codecs(d, kb, 51)
+    vc, vo = dense_codecs(d, vb, 52)
+    rng = np.random.default_rng(53)
+    B = len(lengths)
+    k = _inputs(rng, (B, Hkv, T, d), d)
+    v = _inputs(rng, (B, Hkv, T, d), d)
+    q = (rng.standard_normal((B, G * Hkv, d)) * qmul).astype(np.float16)
+    kcodes, knorms = gpu_encode_cache(kc, k)
+    vcodes, vnorms = gpu_encode_cache(vc, v)
+    out = gpu_attend(kc, vc, q, kcodes, knorms, vcodes, vnorms, lengths)
+    okc, okn, _ = oracle.encode_dense(ko, k)
+    ovc, ovn, _ = oracle.encode_dense(vo, v)
+    ref = oracle.attend_dense(ko, vo, q, okc, okn, ovc, ovn, np.asarray(lengths))
+    assert np.isfinite(out).all()
+    err = np.abs(out - ref).max()
+    assert err <= ATOL, err
+
+
 def test_dense_attend_phi3_mini_shape_sampled():
     """A Phi-3-mini-shaped layer (32 query and 32 KV heads, head dim 96) at 4096
     tokens, K4/V2, in the launch configuration of a full call; sampled KV heads
@@ -159,13 +202,15 @@ def test_dense_attend_phi3_mini_shape_sampled():
         assert np.abs(out[:, g * G:(g + 1) * G] - ref).max() <= ATOL
 
 
-def test_dense_attend_rows_beyond_length_never_read():
+@pytest.mark.parametrize("G", [3, 1])
+def test_dense_attend_rows_beyond_length_never_read(G):
     """Rows past each sequence's length hold 0xFF codes and NaN norms; a device
     length above max_len is clamped to it. The cache is allocated well past
     what the launch covers (max_ctx 1000 against 5 splits of 64 tokens), so
-    every read stays in bounds even where a length exceeds max_len."""
-    d, kb, vb, G, Hkv, T, max_len = 96, 4, 2, 3, 2, 1000, 300
-    announce(f"dense attend poisoned rows d={d} max_ctx={T} max_len={max_len}")
+    every read stays in bounds even where a length exceeds max_len. G = 1 runs
+    the register-held kernel, whose steps past a range's end read its last row."""
+    d, kb, vb, Hkv, T, max_len = 96, 4, 2, 2, 1000, 300
+    announce(f"dense attend poisoned rows d={d} G={G} max_ctx={T} max_len={max_len}")
     kc, _ = dense_codecs(d, kb, 31)
     vc, _ = dense_codecs(d, vb, 32)
     rng = np.random.default_rng(33)
@@ -210,10 +255,11 @@ def test_dense_codecs_rejected_where_unsupported():
     assert e.value.status == tq.TQ_ERR_UNSUPPORTED
 
 
-def test_dense_graph_replay_matches_eager():
+@pytest.mark.parametrize("G", [3, 1])
+def test_dense_graph_replay_matches_eager(G):
     """The dense attend captured in a HIP graph: three replays, with eager work
     between them, bitwise equal to the eager call."""
-    d, G, Hkv, T = 96, 3, 2, 700
+    d, Hkv, T = 96, 2, 700
     announce(f"dense attend graph replay d={d} G={G} T={T}")
     kc, _ = dense_codecs(d, 4, 21)
     vc, _ = dense_codecs(d, 3, 22)
