@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "codec.hpp"
 #include "kernels.hpp"
@@ -388,6 +389,16 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
 // states are merged once, at the end of the range: per wavefront by two
 // transposing lane swaps and LDS, then across wavefronts.
 
+template <int... Is, class F>
+__device__ __forceinline__ void sfor_d_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+template <int N, class F>
+__device__ __forceinline__ void sfor_d(F&& f) {
+  sfor_d_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
 constexpr int kLtWaves = 12;     // wavefronts per workgroup (3 per SIMD at <= 168 VGPRs)
 constexpr int kLtStep = 32;      // tokens per wavefront step (two lanes per token)
 constexpr float kLtSlack = 8.f;  // the running maximum moves only when a score exceeds it by more
@@ -401,6 +412,9 @@ struct LtShape {
   // once its half is shifted down to bit 0
   static constexpr int KL = (HK % 32 + HK + 31) / 32, VL = (HV % 32 + HV + 31) / 32;
   static constexpr int KS = (HK + 31) / 32, VS = (HV + 31) / 32;
+  // V codes of up to 3 bits are looked up two coordinates at a time
+  static constexpr bool VP = VB <= 3;
+  static constexpr int VPN = VP ? (1 << (2 * VB)) * 32 : 1;  // pair-table entries
   static constexpr int R = H / 4;   // accumulators per lane after the two swaps
   static constexpr int RP = R | 1;  // their LDS stride (odd: no bank conflicts)
   static_assert(D % 32 == 0 && H % 16 == 0, "head dim");
@@ -430,6 +444,44 @@ __device__ __forceinline__ float swap_sum(const P& p) {
   return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
 }
 
+// (x & m) | o in one VALU operation (written out: the compiler turns the OR
+// of the disjoint terms into an add after a separate AND).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
+  return r;
+}
+// Byte offset of code j (width B, at bit j * B of the stream) in a table of
+// 256-byte rows, plus the lane's slot o within its row.
+template <int B, int S>
+__device__ __forceinline__ uint32_t lt_row_off(const uint32_t (&w)[S], int j, uint32_t m, uint32_t o) {
+  const int p = j * B, wi = p >> 5, sh = p & 31;
+  if (sh + B > 32) return and_or(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) << 8, m, o);
+  if (sh == 8) return and_or(w[wi], m, o);
+  return and_or(sh > 8 ? w[wi] >> (sh - 8) : w[wi] << (8 - sh), m, o);
+}
+// Byte BY of x, ANDed with m, in one VALU operation (a source byte select;
+// written out because the compiler folds the shifts that would lead to it
+// into shift-and pairs).
+template <int BY>
+__device__ __forceinline__ uint32_t byte_and(uint32_t x, uint32_t m) {
+  uint32_t r;
+  if constexpr (BY == 0) {
+    r = x & m;
+  } else if constexpr (BY == 1) {
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+        : "=v"(r) : "v"(x), "v"(m));
+  } else if constexpr (BY == 2) {
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
+        : "=v"(r) : "v"(x), "v"(m));
+  } else {
+    static_assert(BY == 3, "byte");
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+        : "=v"(r) : "v"(x), "v"(m));
+  }
+  return r;
+}
+
 template <int D, int KB, int VB>
 struct LtRows {
   uint32_t k[LtShape<D, KB, VB>::KL];
@@ -445,9 +497,17 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
   constexpr int H = S::H, NT = 64 * kLtWaves;
   __shared__ float s_q[D];
   __shared__ float s_ck[1 << KB], s_cv[1 << VB];
+  // V pair table: entry (code, slot) = (cV[code & m], cV[code >> VB]) for
+  // codes of two coordinates, copied into all 32 eight-byte bank slots so
+  // that lane l reading slot l % 32 never conflicts, whatever the codes
+  __shared__ float2 s_cvp[S::VPN];
   constexpr int QP = NT / D;  // threads per rotated query coordinate
-  __shared__ double s_qp[QP][D];
-  __shared__ float s_red[kLtWaves][64][S::RP];
+  // the query rotation's partial sums and the merge's accumulators share LDS
+  // (barriers separate their uses)
+  constexpr int QP_BYTES = QP * D * 8, RED_BYTES = kLtWaves * 64 * S::RP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_u[QP_BYTES > RED_BYTES ? QP_BYTES : RED_BYTES];
+  double (*s_qp)[D] = reinterpret_cast<double (*)[D]>(s_u);
+  float (*s_red)[64][S::RP] = reinterpret_cast<float (*)[64][S::RP]>(s_u);
   __shared__ float s_ml[kLtWaves][2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -483,6 +543,12 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
 
   for (int k = tid; k < (1 << KB); k += NT) s_ck[k] = a.k_centroids[k];
   for (int k = tid; k < (1 << VB); k += NT) s_cv[k] = a.v_centroids[k];
+  if constexpr (S::VP) {
+    for (int e = tid; e < S::VPN; e += NT) {
+      const int c = e >> 5;
+      s_cvp[e] = make_float2(a.v_centroids[c & ((1 << VB) - 1)], a.v_centroids[c >> VB]);
+    }
+  }
   // rotated query of this KV head's one query head, q_hat_i = sum_j m_ij q_j:
   // QP threads per coordinate sum consecutive stretches of j, then one adds
   // the partial sums in order (fp64 throughout)
@@ -514,22 +580,43 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
   if (t_end > t_begin) {  // uniform over the workgroup
     const int koff = half * (S::HK % 32), voff = half * (S::HV % 32);
     const int steps = (t_end - t_begin + kLtStep - 1) / kLtStep;
-    for (int st = wave; st < steps; st += kLtWaves) {
-      load(st + kLtWaves, nxt);  // unconditional: the prefetch has no branch
+    const uint32_t lane8 = (lane & 31) * 8;  // this lane's 8-byte slot in a pair-table row
+    const uint32_t m3c = 0x3cu, mpair = ((1u << (2 * VB)) - 1u) << 8;
+    // one step over the rows r of step st
+    auto step = [&](LtRows<D, KB, VB>& r, int st) {
       const bool valid = me + st * kLtStep < t_end;
       uint32_t kw[S::KS];
       if constexpr (S::HK % 32 != 0) {
-        lt_shift(cur.k, koff, kw);
+        lt_shift(r.k, koff, kw);
       } else {
 #pragma unroll
-        for (int k = 0; k < S::KS; ++k) kw[k] = cur.k[k];
+        for (int k = 0; k < S::KS; ++k) kw[k] = r.k[k];
       }
       float p4[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (KB == 4) {
+        // code n of a dword as a table byte offset in one AND with a byte
+        // select: even codes from w << 2, odd codes from w >> 2
 #pragma unroll
-      for (int j = 0; j < H; ++j) p4[j & 3] = fmaf(qv[j], s_ck[lt_field<KB>(kw, j)], p4[j & 3]);
+        for (int k = 0; k < S::KS; ++k) {
+          const uint32_t ea = kw[k] << 2, eb = kw[k] >> 2;
+          uint32_t off[8];
+          sfor_d<4>([&](auto by) {
+            off[2 * by] = byte_and<by>(ea, m3c);
+            off[2 * by + 1] = byte_and<by>(eb, m3c);
+          });
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            const float c = *(const float*)((const char*)s_ck + off[n]);
+            p4[n & 3] = fmaf(qv[8 * k + n], c, p4[n & 3]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < H; ++j) p4[j & 3] = fmaf(qv[j], s_ck[lt_field<KB>(kw, j)], p4[j & 3]);
+      }
       float sk = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       sk += xor_lane_f32<1>(sk);  // the token's other half; the same sum on both lanes
-      const float sc = valid ? sk * cur.nk : -INFINITY;
+      const float sc = valid ? sk * r.nk : -INFINITY;
       if (sc > m + kLtSlack) {
         const float al = exp2f(m - sc);
         l *= al;
@@ -539,17 +626,34 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
       }
       const float p = exp2f(sc - m);  // at most 2^kLtSlack
       l += p;
-      const float w = p * cur.nv;
+      const float w = p * r.nv;
       uint32_t vw[S::VS];
       if constexpr (S::HV % 32 != 0) {
-        lt_shift(cur.v, voff, vw);
+        lt_shift(r.v, voff, vw);
       } else {
 #pragma unroll
-        for (int k = 0; k < S::VS; ++k) vw[k] = cur.v[k];
+        for (int k = 0; k < S::VS; ++k) vw[k] = r.v[k];
       }
+      if constexpr (S::VP) {
 #pragma unroll
-      for (int j = 0; j < H; ++j) acc[j] = fmaf(w, s_cv[lt_field<VB>(vw, j)], acc[j]);
-      cur = nxt;
+        for (int i = 0; i < H / 2; ++i) {
+          const uint32_t off = lt_row_off<2 * VB>(vw, i, mpair, lane8);
+          const float2 e = *(const float2*)((const char*)s_cvp + off);
+          acc[2 * i] = fmaf(w, e.x, acc[2 * i]);
+          acc[2 * i + 1] = fmaf(w, e.y, acc[2 * i + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < H; ++j) acc[j] = fmaf(w, s_cv[lt_field<VB>(vw, j)], acc[j]);
+      }
+    };
+    // two row buffers in turn: the prefetch needs no register copies
+    for (int st = wave; st < steps; st += 2 * kLtWaves) {
+      load(st + kLtWaves, nxt);  // unconditional: the prefetch has no branch
+      step(cur, st);
+      if (st + kLtWaves >= steps) break;
+      load(st + 2 * kLtWaves, cur);
+      step(nxt, st + kLtWaves);
     }
   }
 
@@ -623,33 +727,61 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
 // Grid (n_q_heads, batch), kDCombineThreads threads: merge the splits by
 // log-sum-exp, then out_i = sum_j m_V[j][i] a_j / d (fp64 sums; several
 // threads per output coordinate sum consecutive stretches of j, and one adds
-// their partial sums in order).
+// their partial sums in order). Every global read that does not depend on
+// another (the thread's stretch of m_V, a group of splits' partials) is
+// issued before the first is used.
 constexpr int kDCombineThreads = 512;
+constexpr int kDMReg = 32;  // rotation entries a thread holds in registers
+constexpr int kDSplitGroup = 8;  // splits whose partials are read at once
 __global__ __launch_bounds__(kDCombineThreads) void dense_combine_kernel(DenseAttendArgs a) {
   constexpr int kParts = kDCombineThreads / 32;  // at most, for d = 32
   __shared__ float s_a[kMaxDim];
   __shared__ double s_part[kParts * 32];
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y, d = a.dim;
-  const size_t slot0 = ((size_t)b * a.n_q_heads + h) * a.splits;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.pml[(slot0 + s) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < a.splits; ++s)
-    L += a.pml[(slot0 + s) * 2 + 1] * exp2f(a.pml[(slot0 + s) * 2] - mx);
-  for (int j = tid; j < d; j += kDCombineThreads) {
-    float A = 0.f;
-    for (int s = 0; s < a.splits; ++s)
-      A += a.pacc[(slot0 + s) * d + j] * exp2f(a.pml[(slot0 + s) * 2] - mx);
-    s_a[j] = L > 0.f ? A / L : 0.f;  // no visible row: a zero output
+  const int parts = kDCombineThreads / d;  // d <= 256: at least 2
+  const bool rot = tid < parts * d;
+  const int i = tid % d, part = tid / d;
+  const int j0 = part * d / parts, j1 = (part + 1) * d / parts;
+  double mreg[kDMReg];
+#pragma unroll
+  for (int k = 0; k < kDMReg; ++k) mreg[k] = rot && j0 + k < j1 ? rot_v(a, j0 + k, i) : 0.0;
+
+  if (tid < d) {
+    const size_t slot0 = ((size_t)b * a.n_q_heads + h) * a.splits;
+    float mx = -INFINITY, L = 0.f, A = 0.f;
+    for (int s0 = 0; s0 < a.splits; s0 += kDSplitGroup) {
+      float pm[kDSplitGroup], pl[kDSplitGroup], pa[kDSplitGroup];
+#pragma unroll
+      for (int k = 0; k < kDSplitGroup; ++k) {
+        const bool in = s0 + k < a.splits;
+        const size_t sl = slot0 + (in ? s0 + k : 0);
+        pm[k] = in ? a.pml[sl * 2] : -INFINITY;
+        pl[k] = in ? a.pml[sl * 2 + 1] : 0.f;
+        pa[k] = in ? a.pacc[sl * d + tid] : 0.f;
+      }
+      float nm = mx;
+#pragma unroll
+      for (int k = 0; k < kDSplitGroup; ++k) nm = fmaxf(nm, pm[k]);
+      const float al = exp2f(mx - nm);  // 0 on the first group (split maxima are finite)
+      L *= al;
+      A *= al;
+#pragma unroll
+      for (int k = 0; k < kDSplitGroup; ++k) {
+        const float f = exp2f(pm[k] - nm);
+        L += pl[k] * f;
+        A += pa[k] * f;
+      }
+      mx = nm;
+    }
+    s_a[tid] = L > 0.f ? A / L : 0.f;  // no visible row: a zero output
   }
   __syncthreads();
-  const int parts = kDCombineThreads / d;  // d <= 256: at least 2
-  if (tid < parts * d) {
-    const int i = tid % d, part = tid / d;
-    const int j0 = part * d / parts, j1 = (part + 1) * d / parts;
+  if (rot) {
     double o = 0.0;
-#pragma unroll 4
-    for (int j = j0; j < j1; ++j) o += rot_v(a, j, i) * (double)s_a[j];
+#pragma unroll
+    for (int k = 0; k < kDMReg; ++k)
+      if (j0 + k < j1) o += mreg[k] * (double)s_a[j0 + k];
+    for (int j = j0 + kDMReg; j < j1; ++j) o += rot_v(a, j, i) * (double)s_a[j];
     s_part[part * d + i] = o;
   }
   __syncthreads();
