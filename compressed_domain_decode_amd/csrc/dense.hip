@@ -199,6 +199,172 @@ __global__ __launch_bounds__(256) void dense_encode_kernel(DenseEncodeArgs a) {
   }
 }
 
+// Encode with the rotation staged in LDS, for head dims up to 96. The kernel
+// above reads the whole transposed rotation from L2 for every four vectors;
+// here a workgroup copies it into LDS once and takes passes of kEV vectors.
+// Per pass: the vectors go to LDS as fp64; one thread per vector sums its
+// squares over the same pairwise tree (written as a compile-time recursion
+// over index ranges); each thread computes a tile of 4 vectors x 4
+// coordinates of w = m x, every output's products and sums in index order
+// (no fused multiply-add); then it bucketizes its 16 outputs and ORs each
+// vector's four codes into that vector's LDS row, which is stored as dwords.
+constexpr int kEV = 64;  // vectors per pass
+
+template <int D>
+struct EncLds {
+  static constexpr int THREADS = (kEV / 4) * (D / 4);
+  static constexpr int XS = D + 1;             // LDS row stride of a staged vector (doubles)
+  static constexpr int WORDS = D * 8 / 32;     // dwords of a row at 8 bits (the most)
+  static constexpr int PER = kEV * D / THREADS;  // staged elements per thread (16)
+  static constexpr int NS = D / 32;              // 32-leaf subtrees of a norm's tree
+  static constexpr size_t BYTES = sizeof(double) * ((size_t)D * D + (size_t)kEV * XS + kEV +
+                                                    (size_t)kEV * NS) +
+                                  sizeof(long long) * 3 * kEV +
+                                  sizeof(uint32_t) * ((size_t)kEV * WORDS + 256);
+};
+
+// Sum of x_j^2 over leaves [LO, LO + SIZE) of an N-leaf pairwise tree in
+// index order: a node adds its two halves, and a half that starts past the
+// last leaf is absent (the level-by-level tree's odd last element carried up).
+template <int N, int LO, int SIZE>
+__device__ __forceinline__ double enc_tree(const double* x) {
+#pragma clang fp contract(off)
+  if constexpr (SIZE == 1) {
+    return x[LO] * x[LO];
+  } else if constexpr (LO + SIZE / 2 >= N) {
+    return enc_tree<N, LO, SIZE / 2>(x);
+  } else {
+    return enc_tree<N, LO, SIZE / 2>(x) + enc_tree<N, LO + SIZE / 2, SIZE / 2>(x);
+  }
+}
+constexpr int enc_pow2(int n) { return n <= 1 ? 1 : 2 * enc_pow2((n + 1) / 2); }
+// The same tree above its 32-leaf subtrees, whose sums are sub[0], sub[1], ...
+// (D a multiple of 32: every subtree is whole).
+template <int N, int LO, int SIZE>
+__device__ __forceinline__ double enc_tree_top(const double* sub) {
+#pragma clang fp contract(off)
+  if constexpr (SIZE == 32) {
+    return sub[LO / 32];
+  } else if constexpr (LO + SIZE / 2 >= N) {
+    return enc_tree_top<N, LO, SIZE / 2>(sub);
+  } else {
+    return enc_tree_top<N, LO, SIZE / 2>(sub) + enc_tree_top<N, LO + SIZE / 2, SIZE / 2>(sub);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(EncLds<D>::THREADS) void dense_encode_lds_kernel(DenseEncodeArgs a) {
+#pragma clang fp contract(off)
+  using E = EncLds<D>;
+  extern __shared__ __attribute__((aligned(16))) double elds[];
+  double* s_m = elds;                              // [j][i] = m[i][j]
+  double* s_x = s_m + D * D;                       // [u][XS]
+  double* s_n = s_x + kEV * E::XS;                 // [kEV] norms
+  double* s_sub = s_n + kEV;                       // [kEV][NS] subtree sums of squares
+  long long* s_off = (long long*)(s_sub + kEV * E::NS);  // [3][kEV] offsets of x, codes, norms
+  uint32_t* s_row = (uint32_t*)(s_off + 3 * kEV);  // [kEV][WORDS]
+  float* s_bnd = (float*)(s_row + kEV * E::WORDS);  // [256]
+  const int tid = threadIdx.x;
+  const int b = a.bits, nb = (1 << b) - 1, words = D * b / 32;
+  for (int k = tid; k < D * D; k += E::THREADS) s_m[k] = a.mt[k];
+  for (int k = tid; k < 256; k += E::THREADS) s_bnd[k] = k < nb ? a.boundaries[k] : 0.f;
+  const long long nvec = (long long)a.n_tok * a.n_head;
+  const long long npass = (nvec + kEV - 1) / kEV;
+  const int uq = tid / (D / 4), iq = tid - uq * (D / 4);  // tile: vectors 4 uq.., coordinates 4 iq..
+  for (long long pass = blockIdx.x; pass < npass; pass += gridDim.x) {
+    const long long v0 = pass * kEV;
+    const int nv = nvec - v0 < kEV ? (int)(nvec - v0) : kEV;
+    // each vector's offsets, once (one thread per vector)
+    if (tid < nv) {
+      const long long v = v0 + tid, t = v / a.n_head, h = v - t * a.n_head;
+      s_off[tid] = t * a.xs_tok + h * a.xs_head;
+      s_off[kEV + tid] = t * a.cs_tok + h * a.cs_head;
+      s_off[2 * kEV + tid] = t * a.ns_tok + h * a.ns_head;
+    }
+    for (int k = tid; k < kEV * words; k += E::THREADS) s_row[(k / words) * E::WORDS + k % words] = 0u;
+    __syncthreads();
+    // stage the pass's vectors (zeros past the last): all loads before any store
+    {
+      float xf[E::PER];
+#pragma unroll
+      for (int r = 0; r < E::PER; ++r) {
+        const int k = tid + r * E::THREADS, u = k / D, j = k - u * D;
+        xf[r] = u < nv ? __half2float(((const __half*)a.x)[s_off[u] + j]) : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < E::PER; ++r) {
+        const int k = tid + r * E::THREADS, u = k / D, j = k - u * D;
+        s_x[u * E::XS + j] = (double)xf[r];
+      }
+    }
+    __syncthreads();
+    if (tid < kEV * E::NS) {  // one 32-leaf subtree per thread
+      const int u = tid / E::NS, q = tid - u * E::NS;
+      s_sub[tid] = enc_tree<32, 0, 32>(s_x + u * E::XS + 32 * q);
+    }
+    double w[4][4];
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) w[uu][ii] = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < D; ++j) {
+      double mv[4], xv[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) mv[ii] = s_m[j * D + 4 * iq + ii];
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) xv[uu] = s_x[(4 * uq + uu) * E::XS + j];
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) w[uu][ii] = w[uu][ii] + mv[ii] * xv[uu];
+    }
+    __syncthreads();  // subtree sums written
+    // norms (the tree above the subtrees), z = w / N, and the codes: the 16
+    // binary searches advance together, one boundary level at a time
+    double z[4][4];
+    int c[4][4];
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int u = 4 * uq + uu;
+      const double nrm = __builtin_sqrt(enc_tree_top<D, 0, enc_pow2(D)>(s_sub + u * E::NS));
+      if (iq == 0) s_n[u] = nrm;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        z[uu][ii] = nrm == 0.0 ? 0.0 : w[uu][ii] / nrm;
+        c[uu][ii] = 0;
+      }
+    }
+    for (int st = (nb + 1) >> 1; st >= 1; st >>= 1) {
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if ((double)s_bnd[c[uu][ii] + st - 1] < z[uu][ii]) c[uu][ii] += st;
+    }
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int u = 4 * uq + uu;
+      if (u < nv) {
+        uint32_t pk = 0u;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) pk |= (uint32_t)c[uu][ii] << (ii * b);
+        // the four codes occupy stream bits 4 iq b .. 4 iq b + 4 b - 1, LSB first
+        const int p = 4 * iq * b, wi = p >> 5, sh = p & 31;
+        atomicOr(&s_row[u * E::WORDS + wi], pk << sh);
+        if (sh + 4 * b > 32) atomicOr(&s_row[u * E::WORDS + wi + 1], pk >> (32 - sh));
+      }
+    }
+    __syncthreads();
+    for (int k = tid; k < nv * words; k += E::THREADS) {
+      const int u = k / words, kw = k - u * words;
+      ((uint32_t*)(a.codes + s_off[kEV + u]))[kw] = s_row[u * E::WORDS + kw];
+    }
+    for (int u = tid; u < nv; u += E::THREADS) a.norms[s_off[2 * kEV + u]] = (float)s_n[u];
+    __syncthreads();  // rows and vectors read before the next pass
+  }
+}
+
 // ---------------------------------------------------------------- attend
 
 // Rotation entries: m_K[i][j] and m_V[j][i]. For Walsh-Hadamard codecs
@@ -794,9 +960,23 @@ __global__ __launch_bounds__(kDCombineThreads) void dense_combine_kernel(DenseAt
 
 }  // namespace
 
+template <int D>
+hipError_t launch_encode_lds(const DenseEncodeArgs& a, long long nvec, hipStream_t stream) {
+  const long long npass = (nvec + kEV - 1) / kEV;
+  // as many workgroups as fit at once: 256 CUs, each with 160 KB of LDS
+  const long long fit = 256LL * (long long)(kDenseLdsFull / EncLds<D>::BYTES);
+  const int blocks = (int)(npass < fit ? npass : fit);
+  hipLaunchKernelGGL(dense_encode_lds_kernel<D>, dim3(blocks), dim3(EncLds<D>::THREADS),
+                     EncLds<D>::BYTES, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode_dense(const DenseEncodeArgs& a, hipStream_t stream) {
   const long long nvec = (long long)a.n_tok * a.n_head;
   if (nvec <= 0) return hipSuccess;
+  if (a.dim == 96) return launch_encode_lds<96>(a, nvec, stream);
+  if (a.dim == 64) return launch_encode_lds<64>(a, nvec, stream);
+  if (a.dim == 32) return launch_encode_lds<32>(a, nvec, stream);
   const long long per_block = (long long)kDW * kVPW;
   const long long blocks = (nvec + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -836,8 +1016,15 @@ hipError_t launch_dense_split(DenseAttendArgs a, int batch, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t allow_encode_lds() {
+  static_assert(EncLds<D>::BYTES <= kDenseLdsFull, "encode LDS");
+  return hipFuncSetAttribute((const void*)&dense_encode_lds_kernel<D>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)EncLds<D>::BYTES);
+}
+
 hipError_t prepare_attend_dense() {
-  const hipError_t e[] = {allow_dense_lds<1, 2, true>(),   allow_dense_lds<1, 4, true>(),
+  const hipError_t e[] = {allow_encode_lds<96>(), allow_encode_lds<64>(), allow_encode_lds<32>(),allow_dense_lds<1, 2, true>(),   allow_dense_lds<1, 4, true>(),
                           allow_dense_lds<4, 2, true>(),   allow_dense_lds<4, 4, true>(),
                           allow_dense_lds<4, 2, false>(),  allow_dense_lds<4, 4, false>(),
                           allow_dense_lds<16, 2, false>(), allow_dense_lds<16, 4, false>()};
