@@ -71,7 +71,10 @@ def gpu_attend(kc, vc, q_np, kcodes, knorms, vcodes, vnorms, lengths_np, max_len
 
 
 @pytest.mark.parametrize("d,bits", [(96, 2), (96, 3), (96, 4), (96, 8), (160, 3), (192, 4),
-                                    (32, 1), (224, 5), (256, 6), (128, 7)])
+                                    (32, 1), (224, 5), (256, 6), (128, 7),
+                                    # the LDS-staged kernel (d <= 96): every width
+                                    (96, 1), (96, 5), (96, 6), (96, 7), (64, 2), (64, 5),
+                                    (64, 8), (32, 4), (32, 8)])
 def test_dense_encode_matches_oracle(d, bits):
     announce(f"dense encode d={d} bits={bits}")
     g, o = dense_codecs(d, bits, 7)
