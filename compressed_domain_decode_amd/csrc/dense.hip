@@ -6,20 +6,25 @@
 // The caller supplies m (d x d, m / sqrt(d) orthogonal, d a multiple of 32 up
 // to 256). With m = H diag(sigma) this is exactly the Walsh-Hadamard codec.
 //
-// Encode, per fp16 vector x (four vectors per wavefront):
+// Encode, per fp16 vector x:
 //   N = sqrt(sum_j x_j^2)  fp64; pairwise tree in index order, an odd last
 //                          element carried up to the next level
 //   w = m x                fp64; products and sums in index order, no fused
-//                          multiply-add (m is read transposed, so a lane's
-//                          coordinate i walks a coalesced column)
+//                          multiply-add
 //   z = w / N (0 when N = 0), index = #{boundaries < z}, packed LSB-first.
+// dense_encode_lds_kernel (d <= 96) holds m in LDS and takes passes of 64
+// vectors, 4 x 4 output tiles per thread; dense_encode_kernel (larger d)
+// reads m transposed from global memory, four vectors per wavefront.
 //
 // Attend (the same split / combine shape as the Walsh-Hadamard path, without
 // its matrix-core scoring): q_hat = scale log2(e) / d * m_K q per query head;
-// per 64-token tile a lane scores one token, s = n_t q_hat . c_K[idx_t];
-// online softmax in base 2; a lane then owns coordinates and accumulates
-// p_t n^V_t c_V[idx^V_t] over the tile's tokens; the combine merges the
-// splits and applies the inverse rotation out = m_V^T a / d.
+// scores s = n_t q_hat . c_K[idx_t]; online softmax in base 2; the values
+// accumulate p_t n^V_t c_V[idx^V_t] in the rotated basis; the combine merges
+// the splits and applies the inverse rotation out = m_V^T a / d.
+// dense_lt_kernel (one query head per KV head, d = 96) keeps a token's work
+// in registers, two lanes per token; dense_split_kernel (other shapes)
+// stages 64-token tiles in LDS, a lane scoring one token and then owning
+// coordinates for the values.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
