@@ -462,7 +462,12 @@ tq_status decode_attend(const char* fn, const tq_codec* kc, const tq_codec* vc,
   // result as the dense codec with that matrix): every bit width pair is served
   const bool fast = !dense && tq::attend_supported(dim, k_bits, vc->tabs.bits, group * n_qtok);
   const bool wht_fallback = !dense && !fast && n_qtok == 1 && !raw.lengths && !prodk && !raw_k;
-  if (dense || wht_fallback) {
+  // one query head per KV head at the register-held kernel's shapes: that
+  // kernel also serves Walsh-Hadamard codec pairs (the matrix-core one would
+  // carry one head in each 4-head block)
+  const bool wht_lt = !dense && n_qtok == 1 && !raw.lengths && !prodk && !raw_k &&
+                      tq::dense_lt_supported(dim, k_bits, vc->tabs.bits, group);
+  if (dense || wht_fallback || wht_lt) {
     const tq::AttendPlan dplan = tq::plan_attend(batch, n_q_heads, n_kv_heads, dim, max_len);
     const tq_status ws = take_workspace(dplan.total_bytes);
     if (ws != TQ_OK) return ws;

@@ -372,15 +372,12 @@ __global__ __launch_bounds__(EncLds<D>::THREADS) void dense_encode_lds_kernel(De
 
 // ---------------------------------------------------------------- attend
 
-// Rotation entries: m_K[i][j] and m_V[j][i]. For Walsh-Hadamard codecs
-// m = H diag(sigma) with H_ij = (-1)^popcount(i & j), so an entry is a sign.
+// Key rotation entry m_K[i][j]. For Walsh-Hadamard codecs m = H diag(sigma)
+// with H_ij = (-1)^popcount(i & j), so an entry is a sign (the combine applies
+// the value rotation of such codecs by butterflies instead).
 __device__ __forceinline__ double rot_k(const DenseAttendArgs& a, int i, int j) {
   if (a.wht) return ((__popc(i & j) + (a.wht_k.bits[j >> 5] >> (j & 31))) & 1) ? -1.0 : 1.0;
   return a.mt_k[(size_t)j * a.dim + i];
-}
-__device__ __forceinline__ double rot_v(const DenseAttendArgs& a, int j, int i) {
-  if (a.wht) return ((__popc(i & j) + (a.wht_v.bits[i >> 5] >> (i & 31))) & 1) ? -1.0 : 1.0;
-  return a.m_v[(size_t)j * a.dim + i];
 }
 
 // Grid (splits, n_kv_heads, batch); nw = blockDim.x / 64 wavefronts take the
@@ -570,7 +567,10 @@ __device__ __forceinline__ void sfor_d(F&& f) {
   sfor_d_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
-constexpr int kLtWaves = 12;     // wavefronts per workgroup (3 per SIMD at <= 168 VGPRs)
+// wavefronts per workgroup: 3 per SIMD where a lane's state fits 168 VGPRs
+// (d = 96), else 2
+template <int D>
+constexpr int lt_waves() { return D <= 96 ? 12 : 8; }
 constexpr int kLtStep = 32;      // tokens per wavefront step (two lanes per token)
 constexpr float kLtSlack = 8.f;  // the running maximum moves only when a score exceeds it by more
 
@@ -660,12 +660,12 @@ struct LtRows {
   float nk, nv;
 };
 
-// Grid (splits, n_kv_heads, batch), kLtWaves wavefronts; the partials have
+// Grid (splits, n_kv_heads, batch), W wavefronts; the partials have
 // the layout of dense_split_kernel's, so dense_combine_kernel finishes both.
-template <int D, int KB, int VB>
-__global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs a) {
+template <int D, int KB, int VB, int W>
+__global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
   using S = LtShape<D, KB, VB>;
-  constexpr int H = S::H, NT = 64 * kLtWaves;
+  constexpr int H = S::H, NT = 64 * W;
   __shared__ float s_q[D];
   __shared__ float s_ck[1 << KB], s_cv[1 << VB];
   // V pair table: entry (code, slot) = (cV[code & m], cV[code >> VB]) for
@@ -675,11 +675,11 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
   constexpr int QP = NT / D;  // threads per rotated query coordinate
   // the query rotation's partial sums and the merge's accumulators share LDS
   // (barriers separate their uses)
-  constexpr int QP_BYTES = QP * D * 8, RED_BYTES = kLtWaves * 64 * S::RP * 4;
+  constexpr int QP_BYTES = QP * D * 8, RED_BYTES = W * 64 * S::RP * 4;
   __shared__ __attribute__((aligned(16))) unsigned char s_u[QP_BYTES > RED_BYTES ? QP_BYTES : RED_BYTES];
   double (*s_qp)[D] = reinterpret_cast<double (*)[D]>(s_u);
   float (*s_red)[64][S::RP] = reinterpret_cast<float (*)[64][S::RP]>(s_u);
-  __shared__ float s_ml[kLtWaves][2];
+  __shared__ float s_ml[W][2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -819,12 +819,12 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
       }
     };
     // two row buffers in turn: the prefetch needs no register copies
-    for (int st = wave; st < steps; st += 2 * kLtWaves) {
-      load(st + kLtWaves, nxt);  // unconditional: the prefetch has no branch
+    for (int st = wave; st < steps; st += 2 * W) {
+      load(st + W, nxt);  // unconditional: the prefetch has no branch
       step(cur, st);
-      if (st + kLtWaves >= steps) break;
-      load(st + 2 * kLtWaves, cur);
-      step(nxt, st + kLtWaves);
+      if (st + W >= steps) break;
+      load(st + 2 * W, cur);
+      step(nxt, st + W);
     }
   }
 
@@ -875,10 +875,10 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
     const int l0 = 32 * b5 + 16 * b4 + hh;
     float mx = s_ml[0][0];
 #pragma unroll
-    for (int w = 1; w < kLtWaves; ++w) mx = fmaxf(mx, s_ml[w][0]);
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_ml[w][0]);
     float A = 0.f, L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kLtWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       float sum = 0.f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) sum += s_red[w][l0 + 2 * u][k];
@@ -898,7 +898,8 @@ __global__ __launch_bounds__(64 * kLtWaves) void dense_lt_kernel(DenseAttendArgs
 // Grid (n_q_heads, batch), kDCombineThreads threads: merge the splits by
 // log-sum-exp, then out_i = sum_j m_V[j][i] a_j / d (fp64 sums; several
 // threads per output coordinate sum consecutive stretches of j, and one adds
-// their partial sums in order). Every global read that does not depend on
+// their partial sums in order), or for Walsh-Hadamard codecs
+// out = sigma_V (.) H a / d by butterflies. Every global read that does not depend on
 // another (the thread's stretch of m_V, a group of splits' partials) is
 // issued before the first is used.
 constexpr int kDCombineThreads = 512;
@@ -915,7 +916,8 @@ __global__ __launch_bounds__(kDCombineThreads) void dense_combine_kernel(DenseAt
   const int j0 = part * d / parts, j1 = (part + 1) * d / parts;
   double mreg[kDMReg];
 #pragma unroll
-  for (int k = 0; k < kDMReg; ++k) mreg[k] = rot && j0 + k < j1 ? rot_v(a, j0 + k, i) : 0.0;
+  for (int k = 0; k < kDMReg; ++k)
+    mreg[k] = !a.wht && rot && j0 + k < j1 ? a.m_v[(size_t)(j0 + k) * d + i] : 0.0;
 
   if (tid < d) {
     const size_t slot0 = ((size_t)b * a.n_q_heads + h) * a.splits;
@@ -947,12 +949,31 @@ __global__ __launch_bounds__(kDCombineThreads) void dense_combine_kernel(DenseAt
     s_a[tid] = L > 0.f ? A / L : 0.f;  // no visible row: a zero output
   }
   __syncthreads();
+  if (a.wht) {
+    // m = H diag(sigma): out_i = sigma_i (H a)_i / d, H a by in-place
+    // butterflies (d a power of 2; H_ij = (-1)^popcount(i & j))
+    for (int hs = 1; hs < d; hs <<= 1) {
+      for (int t = tid; t < d / 2; t += kDCombineThreads) {
+        const int lo = (t / hs) * 2 * hs + t % hs, hi = lo + hs;
+        const float x0 = s_a[lo], x1 = s_a[hi];
+        s_a[lo] = x0 + x1;
+        s_a[hi] = x0 - x1;
+      }
+      __syncthreads();
+    }
+    for (int i2 = tid; i2 < d; i2 += kDCombineThreads) {
+      const float v = s_a[i2] / (float)d;
+      a.out[((size_t)b * a.n_q_heads + h) * d + i2] =
+          ((a.wht_v.bits[i2 >> 5] >> (i2 & 31)) & 1u) ? -v : v;
+    }
+    return;
+  }
   if (rot) {
     double o = 0.0;
 #pragma unroll
     for (int k = 0; k < kDMReg; ++k)
       if (j0 + k < j1) o += mreg[k] * (double)s_a[j0 + k];
-    for (int j = j0 + kDMReg; j < j1; ++j) o += rot_v(a, j, i) * (double)s_a[j];
+    for (int j = j0 + kDMReg; j < j1; ++j) o += a.m_v[(size_t)j * d + i] * (double)s_a[j];
     s_part[part * d + i] = o;
   }
   __syncthreads();
@@ -1040,8 +1061,9 @@ hipError_t prepare_attend_dense() {
 
 template <int D, int KB, int VB>
 hipError_t launch_dense_lt(const DenseAttendArgs& a, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((dense_lt_kernel<D, KB, VB>), dim3(a.splits, a.n_kv_heads, batch),
-                     dim3(64 * kLtWaves), 0, stream, a);
+  constexpr int W = lt_waves<D>();
+  hipLaunchKernelGGL((dense_lt_kernel<D, KB, VB, W>), dim3(a.splits, a.n_kv_heads, batch),
+                     dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 using DenseLaunch = hipError_t (*)(const DenseAttendArgs&, int, hipStream_t);
@@ -1064,12 +1086,17 @@ DenseLaunch lt_for_bits(int kb, int vb) {
     default: return nullptr;
   }
 }
-// The register-held kernel's instances: one query head per KV head, dense
-// rotations, head dim 96, K 2/3/4/8 and V 2/3/4 bits.
-DenseLaunch find_dense_lt(const DenseAttendArgs& a) {
-  if (a.group != 1 || a.wht) return nullptr;
-  if (a.dim == 96) return lt_for_bits<96>(a.k_bits, a.v_bits);
+// The register-held kernel's instances: one query head per KV head, head dim
+// 96 or 128, K 2/3/4/8 and V 2/3/4 bits; the rotation dense or, at 128, the
+// Walsh-Hadamard codecs' H diag(sigma).
+DenseLaunch find_lt(int dim, int k_bits, int v_bits, int group) {
+  if (group != 1) return nullptr;
+  if (dim == 96) return lt_for_bits<96>(k_bits, v_bits);
+  if (dim == 128) return lt_for_bits<128>(k_bits, v_bits);
   return nullptr;
+}
+DenseLaunch find_dense_lt(const DenseAttendArgs& a) {
+  return find_lt(a.dim, a.k_bits, a.v_bits, a.group);
 }
 
 hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t stream) {
@@ -1097,5 +1124,9 @@ hipError_t launch_attend_dense(const DenseAttendArgs& a, int batch, hipStream_t 
 }
 
 float dense_qscale(float scale, int dim) { return scale * kDLog2e / (float)dim; }
+
+bool dense_lt_supported(int dim, int k_bits, int v_bits, int group) {
+  return find_lt(dim, k_bits, v_bits, group) != nullptr;
+}
 
 }  // namespace tq

@@ -158,6 +158,10 @@ hipError_t prepare_attend_dense();
 constexpr int kDenseLdsFull = 160 * 1024;
 constexpr int kDenseLdsDefault = 64 * 1024;
 float dense_qscale(float scale, int dim);
+// True where the register-held kernel (one query head per KV head) has an
+// instance for these shapes; Walsh-Hadamard codec pairs it covers are served
+// by it, with m = H diag(sigma), rather than by the matrix-core kernel.
+bool dense_lt_supported(int dim, int k_bits, int v_bits, int group);
 
 // Device address of this GPU's fixed scratch array (TQ_NOALLOC_SCRATCH_BYTES
 // bytes, 256-byte aligned), looked up on the first call per device.
