@@ -742,6 +742,52 @@ def main():
             del d_copies, dk, dv
         except tq.TQError as e:
             dense_line = {"unsupported": str(e)}
+    # ---- one query head per KV head with Walsh-Hadamard codecs: a
+    # Llama-2-7B-shaped layer (32 query and 32 KV heads, head dim 128) at 32K
+    # context, K4/V3 (the register-held kernel, two lanes per token)
+    mha_line = None
+    try:
+        md, mH, mT = 128, 32, 32768
+        mkc = tq.tq_codec_init(md, 4, wl.codec_seed)
+        mvc = tq.tq_codec_init(md, 3, wl.codec_seed)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(128)
+        mk = torch.randn((1, mH, mT, md), generator=gen, device=dev).half()
+        mv = torch.randn((1, mH, mT, md), generator=gen, device=dev).half()
+        mq = torch.randn((1, mH, md), generator=gen, device=dev).half()
+        mrow = mkc.row_bytes + 4 + mvc.row_bytes + 4
+        mcopies = cold_copies(args.cold_bytes, (mH * mT * mrow))
+        mmaj = lambda a, *row: a.view(mH, mT, *row).permute(1, 0, *range(2, 2 + len(row)))
+        m_copies = []
+        for i in range(mcopies):
+            t = (torch.empty((1, mH, mT, mkc.row_bytes), dtype=torch.uint8, device=dev),
+                 torch.empty((1, mH, mT), dtype=torch.float32, device=dev),
+                 torch.empty((1, mH, mT, mvc.row_bytes), dtype=torch.uint8, device=dev),
+                 torch.empty((1, mH, mT), dtype=torch.float32, device=dev))
+            tq.tq_encode(mkc, mmaj(mk, md), mmaj(t[0], mkc.row_bytes), mmaj(t[1]))
+            tq.tq_encode(mvc, mmaj(mv, md), mmaj(t[2], mvc.row_bytes), mmaj(t[3]))
+            m_copies.append(t)
+        del mk, mv
+        mlen = torch.full((1,), mT, dtype=torch.int32, device=dev)
+        mout = torch.empty((1, mH, md), dtype=torch.float32, device=dev)
+        mws = torch.empty(tq.tq_attend_workspace_bytes(1, mH, mH, md, mT), dtype=torch.uint8,
+                          device=dev)
+        torch.cuda.synchronize()
+
+        def mha_only(i):
+            c = m_copies[i % mcopies]
+            tq.tq_decode_attend(mkc, mvc, mq, c[0], c[1], c[2], c[3], mlen, mT,
+                                1.0 / math.sqrt(md), mout, mws)
+
+        us = per_call(mha_only, mcopies, max(2, args.steps // (4 * mcopies)))
+        mbytes = mH * mT * mrow
+        mha_line = {"shape": "1 x 32/32 heads, head dim 128, 32768 tokens, K4/V3",
+                    "timing": "graph replay" if graph is not None else "eager",
+                    "cold_copies": mcopies, "attend_us": round(us, 3),
+                    "GBps": round(mbytes / (us * 1e-6) / 1e9, 2)}
+        del m_copies
+    except tq.TQError as e:
+        mha_line = {"unsupported": str(e)}
     # ---- TurboQuant-Prod keys (3-bit codes + 1-bit sketch) with 4-bit values
     prod_line = None
     if graph is not None:
@@ -905,6 +951,7 @@ def main():
         "raw_k_decode": raw_k_line,
         "prod_decode": prod_line,
         "dense_rotation_decode": dense_line,
+        "one_head_per_kv_head_decode": mha_line,
         "two_phase_cache_decode": cache_line,
         "bulk_encode_kv": bulk,
     }
