@@ -567,10 +567,10 @@ __device__ __forceinline__ void sfor_d(F&& f) {
   sfor_d_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
-// wavefronts per workgroup: 3 per SIMD where a lane's state fits 168 VGPRs
-// (d = 96), else 2
+// wavefronts per workgroup: 4 per SIMD where a lane's state fits 128 VGPRs
+// (d = 64), 3 where it fits 168 (d = 96), else 2
 template <int D>
-constexpr int lt_waves() { return D <= 96 ? 12 : 8; }
+constexpr int lt_waves() { return D <= 64 ? 16 : D <= 96 ? 12 : 8; }
 constexpr int kLtStep = 32;      // tokens per wavefront step (two lanes per token)
 constexpr float kLtSlack = 8.f;  // the running maximum moves only when a score exceeds it by more
 
@@ -1087,10 +1087,11 @@ DenseLaunch lt_for_bits(int kb, int vb) {
   }
 }
 // The register-held kernel's instances: one query head per KV head, head dim
-// 96 or 128, K 2/3/4/8 and V 2/3/4 bits; the rotation dense or, at 128, the
-// Walsh-Hadamard codecs' H diag(sigma).
+// 64, 96 or 128, K 2/3/4/8 and V 2/3/4 bits; the rotation dense or, at 64
+// and 128, the Walsh-Hadamard codecs' H diag(sigma).
 DenseLaunch find_lt(int dim, int k_bits, int v_bits, int group) {
   if (group != 1) return nullptr;
+  if (dim == 64) return lt_for_bits<64>(k_bits, v_bits);
   if (dim == 96) return lt_for_bits<96>(k_bits, v_bits);
   if (dim == 128) return lt_for_bits<128>(k_bits, v_bits);
   return nullptr;
