@@ -549,13 +549,14 @@ __global__ __launch_bounds__(GM * EM > 8 ? 512 : 1024) void dense_split_kernel(D
 // KV row) the kernel above spends its time in dependent LDS round trips
 // (staged row, then centroid, per token and coordinate) with a quarter of
 // its lanes idle at head dim 96. Here everything a token needs stays in
-// registers: two lanes share a token, each holding half of the rotated query
-// and half of the value accumulator, and each lane keeps its own online
-// softmax state (running maximum, sum) over the tokens it visits, so a step
-// needs no cross-lane work beyond adding the two half scores. A lane loads
-// its half row straight from global memory, one step ahead. The lanes'
-// states are merged once, at the end of the range: per wavefront by two
-// transposing lane swaps and LDS, then across wavefronts.
+// registers: two lanes share a token (four at head dim 256), each holding
+// its part of the rotated query and of the value accumulator, and each lane
+// keeps its own online softmax state (running maximum, sum) over the tokens
+// it visits, so a step needs no cross-lane work beyond adding the parts'
+// scores. A lane loads its part of a row straight from global memory, one
+// step ahead. The lanes' states are merged once, at the end of the range:
+// per wavefront by two transposing lane swaps and LDS, then across
+// wavefronts.
 
 template <int... Is, class F>
 __device__ __forceinline__ void sfor_d_impl(std::integer_sequence<int, Is...>, F&& f) {
@@ -567,20 +568,25 @@ __device__ __forceinline__ void sfor_d(F&& f) {
   sfor_d_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
+// lanes per token: two, or four at d = 256 (a lane then holds 64 coordinates,
+// as at d = 128)
+template <int D>
+constexpr int lt_lanes() { return D <= 128 ? 2 : 4; }
 // wavefronts per workgroup: 4 per SIMD where a lane's state fits 128 VGPRs
 // (d = 64), 3 where it fits 168 (d = 96), else 2
 template <int D>
 constexpr int lt_waves() { return D <= 64 ? 16 : D <= 96 ? 12 : 8; }
-constexpr int kLtStep = 32;      // tokens per wavefront step (two lanes per token)
 constexpr float kLtSlack = 8.f;  // the running maximum moves only when a score exceeds it by more
 
 template <int D, int KB, int VB>
 struct LtShape {
-  static constexpr int H = D / 2;                           // coordinates per lane
-  static constexpr int HK = H * KB, HV = H * VB;            // bits of a half row
+  static constexpr int P = lt_lanes<D>();                   // lanes per token
+  static constexpr int STEP = 64 / P;                       // tokens per wavefront step
+  static constexpr int H = D / P;                           // coordinates per lane
+  static constexpr int HK = H * KB, HV = H * VB;            // bits of a lane's part of a row
   static constexpr int KW = D * KB / 32, VW = D * VB / 32;  // dwords per row
-  // dwords a lane loads (the second half may start inside a dword) and keeps
-  // once its half is shifted down to bit 0
+  // dwords a lane loads (with two parts the second may start inside a dword)
+  // and keeps once its part is shifted down to bit 0
   static constexpr int KL = (HK % 32 + HK + 31) / 32, VL = (HV % 32 + HV + 31) / 32;
   static constexpr int KS = (HK + 31) / 32, VS = (HV + 31) / 32;
   // V codes of up to 3 bits are looked up two coordinates at a time
@@ -589,6 +595,8 @@ struct LtShape {
   static constexpr int R = H / 4;   // accumulators per lane after the two swaps
   static constexpr int RP = R | 1;  // their LDS stride (odd: no bank conflicts)
   static_assert(D % 32 == 0 && H % 16 == 0, "head dim");
+  // with more than two parts every part starts at a dword (no bit offset)
+  static_assert(P == 2 || (HK % 32 == 0 && HV % 32 == 0), "part alignment");
 };
 
 // Bits [off, off + 32 S) of the window w (0 <= off < 32) as S dwords.
@@ -683,7 +691,8 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int half = lane & 1;
+  constexpr int P = S::P, STEP = S::STEP;
+  const int part = lane & (P - 1);  // which 1/P of the coordinates this lane holds
 
   // the range, and its first rows (in flight during the query rotation)
   const int len = min(a.lengths[b], a.max_len);  // never read past the host bound
@@ -692,14 +701,14 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
   const int t_end = (int)(t_stop < len ? t_stop : (len > 0 ? len : 0));
   const int last = t_end > 0 ? t_end - 1 : 0;  // a row that exists even for an empty range
   const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_ctx;
-  const uint32_t* kbase = (const uint32_t*)a.k_codes + row0 * S::KW + half * (S::HK / 32);
-  const uint32_t* vbase = (const uint32_t*)a.v_codes + row0 * S::VW + half * (S::HV / 32);
+  const uint32_t* kbase = (const uint32_t*)a.k_codes + row0 * S::KW + part * (S::HK / 32);
+  const uint32_t* vbase = (const uint32_t*)a.v_codes + row0 * S::VW + part * (S::HV / 32);
   const float* kn = a.k_norms + row0;
   const float* vn = a.v_norms + row0;
-  const int me = t_begin + (lane >> 1);
+  const int me = t_begin + lane / P;
   // rows of step st; tokens past the range read its last row (in bounds)
   auto load = [&](int st, LtRows<D, KB, VB>& r) {
-    const int t = me + st * kLtStep, rr = t < t_end ? t : last;
+    const int t = me + st * STEP, rr = t < t_end ? t : last;
     const uint32_t* kp = kbase + (size_t)rr * S::KW;
     const uint32_t* vp = vbase + (size_t)rr * S::VW;
 #pragma unroll
@@ -744,18 +753,18 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
   float qv[H], acc[H];
 #pragma unroll
   for (int i = 0; i < H; ++i) {
-    qv[i] = s_q[half * H + i];
+    qv[i] = s_q[part * H + i];
     acc[i] = 0.f;
   }
   float m = kDNoRow, l = 0.f;
   if (t_end > t_begin) {  // uniform over the workgroup
-    const int koff = half * (S::HK % 32), voff = half * (S::HV % 32);
-    const int steps = (t_end - t_begin + kLtStep - 1) / kLtStep;
+    const int koff = part * (S::HK % 32), voff = part * (S::HV % 32);
+    const int steps = (t_end - t_begin + STEP - 1) / STEP;
     const uint32_t lane8 = (lane & 31) * 8;  // this lane's 8-byte slot in a pair-table row
     const uint32_t m3c = 0x3cu, mpair = ((1u << (2 * VB)) - 1u) << 8;
     // one step over the rows r of step st
     auto step = [&](LtRows<D, KB, VB>& r, int st) {
-      const bool valid = me + st * kLtStep < t_end;
+      const bool valid = me + st * STEP < t_end;
       uint32_t kw[S::KS];
       if constexpr (S::HK % 32 != 0) {
         lt_shift(r.k, koff, kw);
@@ -786,7 +795,9 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
         for (int j = 0; j < H; ++j) p4[j & 3] = fmaf(qv[j], s_ck[lt_field<KB>(kw, j)], p4[j & 3]);
       }
       float sk = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      sk += xor_lane_f32<1>(sk);  // the token's other half; the same sum on both lanes
+      // the token's other parts; commutative adds leave the same sum on all
+      sk += xor_lane_f32<1>(sk);
+      if constexpr (P == 4) sk += xor_lane_f32<2>(sk);
       const float sc = valid ? sk * r.nk : -INFINITY;
       if (sc > m + kLtSlack) {
         const float al = exp2f(m - sc);
@@ -838,7 +849,7 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
   mw = fmaxf(mw, xor_lane_f32<16>(mw));
   mw = fmaxf(mw, xor_lane_f32<32>(mw));
   const float f = exp2f(m - mw);  // 1 where no lane saw a token (then l and acc are 0)
-  float lw = half ? 0.f : l * f;  // a token's sum is held by both of its lanes
+  float lw = part ? 0.f : l * f;  // a token's sum is held by all of its lanes
   lw += xor_lane_f32<1>(lw);
   lw += xor_lane_f32<2>(lw);
   lw += xor_lane_f32<4>(lw);
@@ -867,12 +878,12 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
     s_ml[wave][1] = lw;
   }
   __syncthreads();
-  // coordinate c: half c / H, index i within it, held by the 8 lanes of parity
-  // half in row (i / (H/2), i % (H/2) / R) at slot i % R
+  // coordinate c: part c / H, index i within it, held by the 16 / P lanes of
+  // that part in row (i / (H/2), i % (H/2) / R) at slot i % R
   for (int c = tid; c < D; c += NT) {
-    const int hh = c / H, i = c - hh * H;
+    const int pc = c / H, i = c - pc * H;
     const int b5 = i / (H / 2), i2 = i - b5 * (H / 2), b4 = i2 / S::R, k = i2 - b4 * S::R;
-    const int l0 = 32 * b5 + 16 * b4 + hh;
+    const int l0 = 32 * b5 + 16 * b4 + pc;
     float mx = s_ml[0][0];
 #pragma unroll
     for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_ml[w][0]);
@@ -881,7 +892,7 @@ __global__ __launch_bounds__(64 * W) void dense_lt_kernel(DenseAttendArgs a) {
     for (int w = 0; w < W; ++w) {
       float sum = 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += s_red[w][l0 + 2 * u][k];
+      for (int u = 0; u < 16 / P; ++u) sum += s_red[w][l0 + P * u][k];
       const float fw = exp2f(s_ml[w][0] - mx);
       A += sum * fw;
       L += s_ml[w][1] * fw;
@@ -950,21 +961,46 @@ __global__ __launch_bounds__(kDCombineThreads) void dense_combine_kernel(DenseAt
   }
   __syncthreads();
   if (a.wht) {
-    // m = H diag(sigma): out_i = sigma_i (H a)_i / d, H a by in-place
-    // butterflies (d a power of 2; H_ij = (-1)^popcount(i & j))
-    for (int hs = 1; hs < d; hs <<= 1) {
-      for (int t = tid; t < d / 2; t += kDCombineThreads) {
-        const int lo = (t / hs) * 2 * hs + t % hs, hi = lo + hs;
-        const float x0 = s_a[lo], x1 = s_a[hi];
-        s_a[lo] = x0 + x1;
-        s_a[hi] = x0 - x1;
+    // m = H diag(sigma): out_j = sigma_j (H a)_j / d (d = 64 E, E in {1, 2, 4};
+    // H_ij = (-1)^popcount(i & j)). Wavefront 0 holds coordinates E lane + e
+    // in registers: butterflies over the bits of e within a lane, then over
+    // the bits of the lane by lane exchanges.
+    if (tid < 64) {
+      const int E = d / 64, lane = tid;
+      float u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = e < E ? s_a[E * lane + e] : 0.f;
+      auto bfly = [](float& x, float& y) {
+        const float t = x;
+        x = t + y;
+        y = t - y;
+      };
+      if (E >= 2) {
+        bfly(u[0], u[1]);
+        bfly(u[2], u[3]);
       }
-      __syncthreads();
-    }
-    for (int i2 = tid; i2 < d; i2 += kDCombineThreads) {
-      const float v = s_a[i2] / (float)d;
-      a.out[((size_t)b * a.n_q_heads + h) * d + i2] =
-          ((a.wht_v.bits[i2 >> 5] >> (i2 & 31)) & 1u) ? -v : v;
+      if (E == 4) {
+        bfly(u[0], u[2]);
+        bfly(u[1], u[3]);
+      }
+      sfor_d<6>([&](auto MI) {
+        constexpr int m = 1 << MI;
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = xor_lane_f32<m>(u[e]);
+          u[e] = upper ? (p - u[e]) : (u[e] + p);
+        }
+      });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e < E) {
+          const int jj = E * lane + e;
+          const float v = u[e] / (float)d;
+          a.out[((size_t)b * a.n_q_heads + h) * d + jj] =
+              ((a.wht_v.bits[jj >> 5] >> (jj & 31)) & 1u) ? -v : v;
+        }
+      }
     }
     return;
   }
@@ -1087,13 +1123,14 @@ DenseLaunch lt_for_bits(int kb, int vb) {
   }
 }
 // The register-held kernel's instances: one query head per KV head, head dim
-// 64, 96 or 128, K 2/3/4/8 and V 2/3/4 bits; the rotation dense or, at 64
-// and 128, the Walsh-Hadamard codecs' H diag(sigma).
+// 64, 96, 128 or 256, K 2/3/4/8 and V 2/3/4 bits; the rotation dense or, at
+// powers of 2, the Walsh-Hadamard codecs' H diag(sigma).
 DenseLaunch find_lt(int dim, int k_bits, int v_bits, int group) {
   if (group != 1) return nullptr;
   if (dim == 64) return lt_for_bits<64>(k_bits, v_bits);
   if (dim == 96) return lt_for_bits<96>(k_bits, v_bits);
   if (dim == 128) return lt_for_bits<128>(k_bits, v_bits);
+  if (dim == 256) return lt_for_bits<256>(k_bits, v_bits);
   return nullptr;
 }
 DenseLaunch find_dense_lt(const DenseAttendArgs& a) {

@@ -290,15 +290,15 @@ def test_attend_every_bit_width_pair(d):
     print(f"  d={d}: worst max abs err {worst:.3e} over 64 pairs", flush=True)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("kb", [2, 3, 4, 8])
 @pytest.mark.parametrize("vb", [2, 3, 4])
 def test_attend_one_head_per_kv_head(d, kb, vb):
-    """One query head per KV head at head dims 64 and 128 runs the
+    """One query head per KV head at head dims 64, 128 and 256 runs the
     register-held kernel with m = H diag(sigma) formed from the codecs' signs
-    (two lanes per token, per-lane softmax state) instead of the matrix-core
-    kernel: every (K, V) bit pair it has, with several splits, a tail inside
-    a wavefront step, a lone token and an empty sequence."""
+    (two lanes per token, four at 256; per-lane softmax state) instead of the
+    matrix-core kernel: every (K, V) bit pair it has, with several splits, a
+    tail inside a wavefront step, a lone token and an empty sequence."""
     lengths = [3000, 65, 1, 0]
     announce(f"attend one head per KV head d={d} K{kb} V{vb} lengths={lengths}")
     got, want = _attend_case(d, kb, vb, 1, lengths=lengths, seed=900 + d + 10 * kb + vb)
