@@ -21,10 +21,11 @@
 // scores s = n_t q_hat . c_K[idx_t]; online softmax in base 2; the values
 // accumulate p_t n^V_t c_V[idx^V_t] in the rotated basis; the combine merges
 // the splits and applies the inverse rotation out = m_V^T a / d.
-// dense_lt_kernel (one query head per KV head, d = 96) keeps a token's work
-// in registers, two lanes per token; dense_split_kernel (other shapes)
-// stages 64-token tiles in LDS, a lane scoring one token and then owning
-// coordinates for the values.
+// dense_lt_kernel (one query head per KV head, d = 64, 96, 128 or 256; also
+// for Walsh-Hadamard codec pairs of that shape, m = H diag(sigma)) keeps a
+// token's work in registers, two lanes per token (four at 256);
+// dense_split_kernel (other shapes) stages 64-token tiles in LDS, a lane
+// scoring one token and then owning coordinates for the values.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 

@@ -34,6 +34,10 @@
  *       dim 128: 8/3 (16), 3/3 (16), 4/4 (8), 4/2 (8), 7/5 (8), 4/3, 2/2, 8/4,
  *                1/1 (4)
  *       dim 256: 2/2 (8), 4/4, 8/3, 3/3, 8/4, 4/2, 4/3 (4)
+ *     With one query head per KV head (G = 1) at dim 64, 128 or 256 and K
+ *     2/3/4/8, V 2/3/4 bits, tq_decode_attend runs a register-held kernel
+ *     instead (two lanes per token, four at dim 256; the rotation formed from
+ *     the signs), which is faster there than the matrix-core one.
  *     tq_decode_attend_multi (G x query tokens heads) and tq_decode_attend_mixed
  *     use these instances only; tq_decode_attend_raw_k and
  *     tq_decode_attend_prod list theirs. A request outside them returns
@@ -241,7 +245,9 @@ size_t tq_attend_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int d
  * Two kernels are enqueued: split attend (the query rotation runs in its
  * prologue) and combine + inverse rotation. Every (K bits, V bits) pair of
  * one dim is served (the coverage list at the top of this header names the
- * matrix-core pairs; the others take the slower sign-formed rotation kernels).
+ * matrix-core pairs and the one-query-head-per-KV-head shapes of the
+ * register-held kernel; the others take the slower sign-formed rotation
+ * kernels).
  * Results agree with softmax attention over the dequantised cache (computed
  * in fp64) to about 1e-5 absolute for unit-scale inputs, and within 2e-3 for
  * the tested workloads; sums in a different order make the low bits differ
